@@ -1,0 +1,316 @@
+"""Plain, slow, obviously-correct CPU oracle of the quantized session KV cache.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
+execute this module; only the tests, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` do.  It shares no code with the HIP
+library (no kernels, headers, helpers, tables or constants).
+
+What it computes, and where the pages say so
+--------------------------------------------
+* Different bit widths for keys and values (FP16, K8V8, K8V4, K4V8, K4V4):
+  "KVSplit -- contexto 2 a 3 vezes mais longo em Apple Silicon"
+  (pt.news.hada.io, topic 20969), sections "Principais resultados de
+  benchmark" and "Assimetria entre key e value"; the int8/int4 split also in
+  "KVBoost acelera inferencia de LLMs em 4,49x com cache reutilizavel",
+  section "Impacto".
+* The block format (32 elements + one fp16 scale, i.e. 8.5 and 4.5 bits per
+  element) is not stated on the pages; it is the reading that reproduces every
+  footprint the KVSplit page prints (section "Uso de memoria conforme o
+  comprimento da sequencia").  The 256-token capacity granule is the reading of
+  the same page's remark on 256-byte page alignment (section "Otimizacao para
+  Apple Silicon e limitacoes"), which is what makes its 128-token row come out.
+* Quantize on append, independent of the model weights: KVSplit page,
+  section "Opinioes no Hacker News" (the cache is quantized at run time as
+  tokens are processed).
+* Keep the cache between turns and process only the new tokens:
+  "Reutilizacao de Cache KV para Conversas Longas no Apple Silicon Oferece
+  Aceleracao de 200x" (openclawradar.com), section "Principais Descobertas e
+  Benchmarks".
+* Attention itself is the plain definition softmax(sigma * q.K^T) V, in fp64,
+  over the dequantized cache.
+
+Conventions fixed here (readings where the pages are silent; each is listed
+in the design notes of the repository):
+  per (token, KV head, 32 consecutive elements along head_dim):
+    amax = max |x_i|                       (x widened exactly to fp32)
+    d    = fp16_RNE(min(fp32(amax / qmax), 65504)),  qmax = 127 or 7
+    q_i  = 0 if d == 0 else clamp(RHAZ(fp32(x_i / d)), -qmax, qmax)
+  8-bit codes are stored as two's-complement int8; 4-bit codes as the nibble
+  u = q + 8, byte j of a block holding u[2j] in the low and u[2j+1] in the
+  high nibble; d is stored as little-endian fp16 bits.  The FP16 layout stores
+  fp16_RNE(x) and has no scale plane.
+  Planes are kept per (layer, KV head): Kc[cap][code bytes], Ks[cap][scale
+  bytes], Vc, Vs, token-major.  cap = round_up(max_tokens, 256).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "LAYOUTS", "LAYOUT_IDS", "BLOCK", "GRANULE", "layout_bits", "code_row_bytes",
+    "scale_row_bytes", "capacity", "layout_footprint_bytes", "f32_to_f16",
+    "block_scale", "rhaz", "quantize_rows", "pack_codes", "unpack_codes",
+    "pack_scales", "unpack_scales", "encode_rows", "dequant_rows", "OracleCache",
+    "attend_decode", "attend_chunk", "attention_exact", "to_f32",
+]
+
+#: layout id -> (name, key bits, value bits).  16 means the fp16 control.
+LAYOUTS = {0: ("FP16", 16, 16), 1: ("K8V8", 8, 8), 2: ("K8V4", 8, 4),
+           3: ("K4V8", 4, 8), 4: ("K4V4", 4, 4)}
+LAYOUT_IDS = {v[0]: k for k, v in LAYOUTS.items()}
+BLOCK = 32          # elements per quantization block (reading; see module doc)
+GRANULE = 256       # capacity granule in tokens (reading; see module doc)
+FP16_MAX = 65504.0
+
+
+def layout_bits(layout: int) -> tuple[int, int]:
+    """(key bits, value bits) of a layout id."""
+    _, kb, vb = LAYOUTS[int(layout)]
+    return kb, vb
+
+
+def code_row_bytes(bits: int, head_dim: int) -> int:
+    """Bytes of codes per (token, KV head): 2D for fp16, D for 8-bit, D/2 for 4-bit."""
+    return {16: 2 * head_dim, 8: head_dim, 4: head_dim // 2}[bits]
+
+
+def scale_row_bytes(bits: int, head_dim: int) -> int:
+    """Bytes of fp16 scales per (token, KV head): one per 32-element block; none for fp16."""
+    return 0 if bits == 16 else 2 * (head_dim // BLOCK)
+
+
+def capacity(max_tokens: int) -> int:
+    """Tokens allocated per (layer, KV head): max_tokens rounded up to 256."""
+    return -(-int(max_tokens) // GRANULE) * GRANULE
+
+
+def layout_footprint_bytes(layout: int, n_layers: int, n_kv_heads: int,
+                           head_dim: int, max_tokens: int) -> int:
+    """Bytes of all planes: L * Hkv * cap * (K row + V row), rows including scales."""
+    kb, vb = layout_bits(layout)
+    per_token = (code_row_bytes(kb, head_dim) + scale_row_bytes(kb, head_dim)
+                 + code_row_bytes(vb, head_dim) + scale_row_bytes(vb, head_dim))
+    return n_layers * n_kv_heads * capacity(max_tokens) * per_token
+
+
+# --------------------------------------------------------------------------
+# scalar conventions
+# --------------------------------------------------------------------------
+def to_f32(x) -> np.ndarray:
+    """Widen inputs to fp32.  bf16 and fp16 values widen exactly; callers hand
+    bf16 data in as fp32 arrays that hold bf16-representable values."""
+    return np.asarray(x, dtype=np.float32)
+
+
+def f32_to_f16(x32: np.ndarray) -> np.ndarray:
+    """IEEE round-to-nearest-even fp32 -> fp16 (numpy's cast)."""
+    return np.asarray(x32, dtype=np.float32).astype(np.float16)
+
+
+def block_scale(amax32: np.ndarray, qmax: int) -> np.ndarray:
+    """d = fp16_RNE(fp32(amax / qmax)), saturated at the largest finite fp16."""
+    d32 = np.asarray(amax32, dtype=np.float32) / np.float32(qmax)   # IEEE fp32 division
+    d32 = np.minimum(d32, np.float32(FP16_MAX))
+    return f32_to_f16(d32)
+
+
+def rhaz(y32: np.ndarray) -> np.ndarray:
+    """Round half away from zero, evaluated in fp64 (exact for fp32 inputs)."""
+    y = np.asarray(y32, dtype=np.float64)
+    return np.sign(y) * np.floor(np.abs(y) + 0.5)
+
+
+# --------------------------------------------------------------------------
+# codec
+# --------------------------------------------------------------------------
+def quantize_rows(x, bits: int):
+    """Quantize rows [n, D] block by block.
+
+    Returns (codes int16 [n, D], scales float16 [n, D/32]) for 8/4 bits, or
+    (fp16 values [n, D], None) for the fp16 control.
+    """
+    x32 = to_f32(x)
+    n, dim = x32.shape
+    if bits == 16:
+        return f32_to_f16(x32), None
+    qmax = {8: 127, 4: 7}[bits]
+    xb = x32.reshape(n, dim // BLOCK, BLOCK)
+    amax = np.max(np.abs(xb), axis=2)
+    d16 = block_scale(amax, qmax)
+    d32 = d16.astype(np.float32)[:, :, None]
+    y = np.zeros_like(xb)
+    np.divide(xb, d32, out=y, where=(d32 != 0))                      # fp32 division
+    q = np.clip(rhaz(y), -qmax, qmax)
+    q = np.where(d32 != 0, q, 0.0)
+    return q.astype(np.int16).reshape(n, dim), d16
+
+
+def pack_codes(codes, bits: int) -> np.ndarray:
+    """Codes [n, D] -> bytes [n, code_row_bytes]."""
+    if bits == 16:
+        c = np.ascontiguousarray(np.asarray(codes, dtype=np.float16))
+        return c.view(np.uint8).reshape(c.shape[0], -1)
+    c = np.asarray(codes, dtype=np.int16)
+    if bits == 8:
+        return c.astype(np.int8).view(np.uint8)
+    u = (c + 8).astype(np.uint8)                                     # nibble in [1, 15]
+    return (u[:, 0::2] | (u[:, 1::2] << 4)).astype(np.uint8)
+
+
+def unpack_codes(packed, bits: int, head_dim: int) -> np.ndarray:
+    """Inverse of pack_codes.  Returns int16 codes, or float16 for the control."""
+    p = np.asarray(packed, dtype=np.uint8)
+    if bits == 16:
+        return np.ascontiguousarray(p).view(np.float16).reshape(p.shape[0], head_dim)
+    if bits == 8:
+        return p.view(np.int8).astype(np.int16)
+    out = np.empty((p.shape[0], head_dim), dtype=np.int16)
+    out[:, 0::2] = (p & 0x0F).astype(np.int16) - 8
+    out[:, 1::2] = (p >> 4).astype(np.int16) - 8
+    return out
+
+
+def pack_scales(d16) -> np.ndarray:
+    """fp16 scales [n, nb] -> little-endian bytes [n, 2 nb]."""
+    d = np.ascontiguousarray(np.asarray(d16, dtype="<f2"))
+    return d.view(np.uint8).reshape(d.shape[0], -1)
+
+
+def unpack_scales(packed) -> np.ndarray:
+    p = np.ascontiguousarray(np.asarray(packed, dtype=np.uint8))
+    return p.view("<f2").reshape(p.shape[0], -1)
+
+
+def encode_rows(x, bits: int):
+    """Rows [n, D] -> (code bytes [n, cb], scale bytes [n, sb] or None)."""
+    codes, d16 = quantize_rows(x, bits)
+    return pack_codes(codes, bits), (None if d16 is None else pack_scales(d16))
+
+
+def dequant_rows(code_bytes, scale_bytes, bits: int, head_dim: int) -> np.ndarray:
+    """x_hat = q * d per element (exact in fp64), or the fp16 value for the control."""
+    c = unpack_codes(code_bytes, bits, head_dim)
+    if bits == 16:
+        return c.astype(np.float64)
+    d = unpack_scales(scale_bytes).astype(np.float64)
+    return c.astype(np.float64) * np.repeat(d, BLOCK, axis=1)
+
+
+# --------------------------------------------------------------------------
+# the session cache
+# --------------------------------------------------------------------------
+class OracleCache:
+    """Planes per (layer, KV head), appended token by token in order."""
+
+    def __init__(self, layout: int, n_layers: int, n_kv_heads: int, head_dim: int,
+                 max_tokens: int):
+        if head_dim % BLOCK:
+            raise ValueError("head_dim must be a multiple of 32")
+        self.layout, self.L, self.Hkv, self.D = int(layout), n_layers, n_kv_heads, head_dim
+        self.max_tokens = int(max_tokens)
+        self.cap = capacity(max_tokens)
+        self.kbits, self.vbits = layout_bits(layout)
+        self.len = [0] * n_layers
+        shp = (n_layers, n_kv_heads, self.cap)
+        self.Kc = np.zeros(shp + (code_row_bytes(self.kbits, head_dim),), np.uint8)
+        self.Ks = np.zeros(shp + (scale_row_bytes(self.kbits, head_dim),), np.uint8)
+        self.Vc = np.zeros(shp + (code_row_bytes(self.vbits, head_dim),), np.uint8)
+        self.Vs = np.zeros(shp + (scale_row_bytes(self.vbits, head_dim),), np.uint8)
+
+    def footprint_bytes(self) -> int:
+        return self.Kc.nbytes + self.Ks.nbytes + self.Vc.nbytes + self.Vs.nbytes
+
+    def append(self, layer: int, k, v) -> None:
+        """Quantize and store new tokens K, V [n, Hkv, D] at rows [len, len + n)."""
+        k32, v32 = to_f32(k), to_f32(v)
+        n = k32.shape[0]
+        t0 = self.len[layer]
+        if t0 + n > self.max_tokens:
+            raise ValueError("append past max_tokens")
+        for h in range(self.Hkv):
+            kc, ks = encode_rows(k32[:, h, :], self.kbits)
+            vc, vs = encode_rows(v32[:, h, :], self.vbits)
+            self.Kc[layer, h, t0:t0 + n] = kc
+            self.Vc[layer, h, t0:t0 + n] = vc
+            if ks is not None:
+                self.Ks[layer, h, t0:t0 + n] = ks
+            if vs is not None:
+                self.Vs[layer, h, t0:t0 + n] = vs
+        self.len[layer] = t0 + n
+
+    def reset(self) -> None:
+        self.len = [0] * self.L
+
+    def keys(self, layer: int, kv_head: int, t1: int | None = None) -> np.ndarray:
+        """Dequantized keys [t1, D] in fp64 (t1 defaults to the cached length)."""
+        t1 = self.len[layer] if t1 is None else t1
+        return dequant_rows(self.Kc[layer, kv_head, :t1], self.Ks[layer, kv_head, :t1],
+                            self.kbits, self.D)
+
+    def values(self, layer: int, kv_head: int, t1: int | None = None) -> np.ndarray:
+        t1 = self.len[layer] if t1 is None else t1
+        return dequant_rows(self.Vc[layer, kv_head, :t1], self.Vs[layer, kv_head, :t1],
+                            self.vbits, self.D)
+
+
+# --------------------------------------------------------------------------
+# attention over the dequantized cache (fp64)
+# --------------------------------------------------------------------------
+def attention_exact(q, keys, values, sm_scale: float) -> np.ndarray:
+    """softmax(sm_scale * q K^T) V for query rows q [r, D] against keys/values [T, D], fp64."""
+    q64 = np.asarray(q, dtype=np.float64)
+    s = sm_scale * (q64 @ np.asarray(keys, dtype=np.float64).T)
+    s -= s.max(axis=1, keepdims=True)
+    w = np.exp(s)
+    return (w @ np.asarray(values, dtype=np.float64)) / w.sum(axis=1, keepdims=True)
+
+
+def attend_decode(caches, layer: int, q, sm_scale: float) -> np.ndarray:
+    """One query per session: q [S, Hq, D] against each session's whole cached length.
+
+    q head h reads KV head h // (Hq / Hkv) (contiguous GQA groups).
+    """
+    q = to_f32(q)
+    n_s, hq, dim = q.shape
+    out = np.zeros((n_s, hq, dim), np.float64)
+    for s, c in enumerate(caches):
+        if c.len[layer] == 0:
+            raise ValueError("decode on an empty cache")
+        g = hq // c.Hkv
+        for h in range(c.Hkv):
+            out[s, h * g:(h + 1) * g] = attention_exact(
+                q[s, h * g:(h + 1) * g], c.keys(layer, h), c.values(layer, h), sm_scale)
+    return out
+
+
+def attend_chunk(cache: OracleCache, layer: int, q, n_new: int, sm_scale: float,
+                 rows=None, row_block: int = 64) -> np.ndarray:
+    """Causal attention of the last n_new cached positions.
+
+    q [n_new, Hq, D]; query j sits at absolute position len - n_new + j and sees
+    keys [0, that position] (inclusive), its own chunk read back from the
+    quantized cache.  ``rows`` restricts the computation to those query indices
+    (output [len(rows), Hq, D]); ``row_block`` only bounds memory.
+    """
+    q = to_f32(q)
+    total = cache.len[layer]
+    if not 0 < n_new <= total:
+        raise ValueError("chunk must already be appended")
+    rows = np.arange(n_new) if rows is None else np.asarray(rows)
+    hq, dim = q.shape[1], q.shape[2]
+    g = hq // cache.Hkv
+    out = np.zeros((len(rows), hq, dim), np.float64)
+    for h in range(cache.Hkv):
+        kh, vh = cache.keys(layer, h, total), cache.values(layer, h, total)
+        for b0 in range(0, len(rows), row_block):
+            rb = rows[b0:b0 + row_block]
+            pos = total - n_new + rb                                   # absolute positions
+            qb = q[rb, h * g:(h + 1) * g, :].astype(np.float64).reshape(-1, dim)
+            s = sm_scale * (qb @ kh.T)                                  # [r*g, total]
+            visible = np.arange(total)[None, :] <= np.repeat(pos, g)[:, None]
+            s[~visible] = -np.inf
+            s -= s.max(axis=1, keepdims=True)
+            w = np.exp(s)
+            o = (w @ vh) / w.sum(axis=1, keepdims=True)
+            out[b0:b0 + len(rb), h * g:(h + 1) * g] = o.reshape(len(rb), g, dim)
+    return out

@@ -1,0 +1,413 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+None of these checks re-types the oracle's own formula: footprints come from the
+page's printed table, scales and codes from exact rational arithmetic and Python's
+``struct`` half-precision packing, attention from pure-Python loops, closed forms and
+invariants.  A dropped term, a wrong sign, index or rounding mode in the oracle fails
+at least one of them.
+"""
+from __future__ import annotations
+
+import math
+import struct
+from fractions import Fraction
+from pathlib import Path
+
+import numpy as np
+import pytest
+
+import oracle as O
+from asymmetric_quantized_kv_amd import inputs as I
+
+GOLD = Path(__file__).parent / "golden"
+
+
+# ---------------------------------------------------------------------------
+# independent references
+# ---------------------------------------------------------------------------
+def f32_nearest(fr: Fraction) -> float:
+    """Exact round-to-nearest-even of a non-negative rational to fp32 (normal or subnormal)."""
+    if fr == 0:
+        return 0.0
+    assert fr > 0
+    e = fr.numerator.bit_length() - fr.denominator.bit_length()
+    if Fraction(2) ** e > fr:
+        e -= 1
+    e = max(e, -126)                       # subnormals share the 2^-126 binade spacing
+    ulp = Fraction(2) ** (e - 23)
+    q, r = divmod(fr, ulp)
+    q = int(q)
+    if r > ulp / 2 or (r == ulp / 2 and q % 2 == 1):
+        q += 1
+    return float(q * ulp)
+
+
+def f16_bits_struct(x: float) -> int:
+    return struct.unpack("<H", struct.pack("<e", x))[0]
+
+
+def rhaz_exact(fr: Fraction) -> int:
+    a = abs(fr)
+    n = math.floor(a + Fraction(1, 2))
+    return n if fr >= 0 else -n
+
+
+def ref_block(xs, bits):
+    """(d fp16 bits, codes) from exact arithmetic: d = fp16(RN32(amax / qmax)) saturated."""
+    qmax = 127 if bits == 8 else 7
+    xs32 = [float(np.float32(x)) for x in xs]
+    amax = max(abs(x) for x in xs32)
+    d32 = min(f32_nearest(Fraction(amax) / qmax), 65504.0)
+    dbits = f16_bits_struct(d32)
+    d = struct.unpack("<e", struct.pack("<H", dbits))[0]
+    if d == 0:
+        return dbits, [0] * len(xs32)
+    codes = [max(-qmax, min(qmax, rhaz_exact(Fraction(x) / Fraction(d)))) for x in xs32]
+    return dbits, codes
+
+
+def oracle_block(xs, bits):
+    x = np.zeros((1, 32), np.float32)
+    x[0, :len(xs)] = xs
+    q, d = O.quantize_rows(x, bits)
+    return int(d.view(np.uint16)[0, 0]), [int(v) for v in q[0]]
+
+
+# ---------------------------------------------------------------------------
+# footprint: the page's printed table
+# ---------------------------------------------------------------------------
+def _footprint_rows():
+    rows, savings = [], []
+    for ln in (GOLD / "footprint_kvsplit.txt").read_text().splitlines():
+        ln = ln.split("#")[0].strip()
+        if not ln:
+            continue
+        a, b, c = ln.split()
+        (savings if a == "saving" else rows).append((a, b, c))
+    return rows, savings
+
+
+@pytest.mark.parametrize("tokens,layout,printed", _footprint_rows()[0])
+def test_footprint_matches_printed_table(tokens, layout, printed):
+    got = O.layout_footprint_bytes(O.LAYOUT_IDS[layout], 22, 4, 64, int(tokens))
+    assert f"{got / 2**20:.2f}" == printed
+
+
+def test_footprint_savings_percent():
+    fp16 = O.layout_footprint_bytes(0, 22, 4, 64, 8192)
+    for _, layout, pct in _footprint_rows()[1]:
+        got = O.layout_footprint_bytes(O.LAYOUT_IDS[layout], 22, 4, 64, 8192)
+        assert round(100 * (1 - got / fp16)) == int(pct)
+
+
+def test_footprint_context_ratio():
+    # "K8V4 saves 59% ... about 2.4 times the context" (KVSplit page, Hacker News section)
+    r = O.layout_footprint_bytes(0, 22, 4, 64, 8192) / O.layout_footprint_bytes(2, 22, 4, 64, 8192)
+    assert 2.4 <= r < 2.5
+
+
+def test_cache_object_footprint_and_capacity_granule():
+    for layout in range(5):
+        c = O.OracleCache(layout, 2, 3, 64, 300)
+        assert c.cap == 512
+        assert c.footprint_bytes() == O.layout_footprint_bytes(layout, 2, 3, 64, 300)
+
+
+# ---------------------------------------------------------------------------
+# scale and codes: exact arithmetic and Python's half packing
+# ---------------------------------------------------------------------------
+def test_fp16_cast_matches_struct():
+    rng = np.random.default_rng(7)
+    x = np.concatenate([rng.standard_normal(20000).astype(np.float32) * 100,
+                        rng.standard_normal(2000).astype(np.float32) * 1e-5])
+    # exact fp16 midpoints and their fp32 neighbours
+    h = rng.integers(0x0400, 0x7BFF, 2000).astype(np.uint16).view(np.float16).astype(np.float64)
+    mid = (h + np.nextafter(h.astype(np.float16), np.float16(np.inf)).astype(np.float64)) / 2
+    m32 = mid.astype(np.float32)
+    x = np.concatenate([x, m32, np.nextafter(m32, np.float32(np.inf)), np.nextafter(m32, np.float32(0))])
+    got = O.f32_to_f16(x).view(np.uint16)
+    want = np.array([f16_bits_struct(float(v)) for v in x], np.uint16)
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_block_scale_exact(bits):
+    qmax = 127 if bits == 8 else 7
+    rng = np.random.default_rng(bits)
+    amax = list(np.abs(rng.standard_normal(3000).astype(np.float32)) * np.float32(3.0))
+    # amax values whose quotient by qmax lands next to an fp16 rounding midpoint
+    h = rng.integers(0x0400, 0x7BFE, 1500).astype(np.uint16).view(np.float16).astype(np.float64)
+    nxt = np.nextafter(h.astype(np.float16), np.float16(np.inf)).astype(np.float64)
+    for m in (h + nxt) / 2:
+        base = np.float32(m * qmax)
+        amax += [base, np.nextafter(base, np.float32(0)), np.nextafter(base, np.float32(np.inf))]
+    amax += [np.float32(1e7), np.float32(65504 * qmax), np.float32(1e-30), np.float32(0)]
+    a = np.array(amax, np.float32)
+    got = O.block_scale(a, qmax).view(np.uint16)
+    want = [f16_bits_struct(min(f32_nearest(Fraction(float(v)) / qmax), 65504.0)) for v in a]
+    assert got.tolist() == want
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_codes_exact_rational(bits):
+    rng = np.random.default_rng(100 + bits)
+    blocks = [rng.standard_normal(32).astype(np.float32) * s for s in (1, 8, 1e-3, 300)]
+    # engineered near-ties: x = (k + 1/2) d and its fp32 neighbours
+    for _ in range(40):
+        x = rng.standard_normal(32).astype(np.float32)
+        dbits, _ = ref_block(x, bits)
+        d = np.float32(struct.unpack("<e", struct.pack("<H", dbits))[0])
+        qmax = 127 if bits == 8 else 7
+        k = rng.integers(0, qmax, 31)
+        t = ((k + 0.5) * np.float64(d)).astype(np.float32)
+        t = np.where(rng.random(31) < 0.5, t, np.nextafter(t, np.float32(0)))
+        y = np.concatenate([[x[np.argmax(np.abs(x))]], t * np.sign(rng.standard_normal(31))]).astype(np.float32)
+        blocks.append(y)
+    for blk in blocks:
+        assert oracle_block(blk, bits) == ref_block(blk, bits)
+
+
+def _codec_cases():
+    out = []
+    for ln in (GOLD / "codec_cases.txt").read_text().splitlines():
+        if not ln.strip() or ln.startswith("#"):
+            continue
+        head, xs, codes = ln.split("|")
+        name, bits, dhex = head.split()
+        out.append((name, int(bits), int(dhex, 16), [float(v) for v in xs.split()], [int(v) for v in codes.split()]))
+    return out
+
+
+@pytest.mark.parametrize("case", _codec_cases(), ids=lambda c: c[0])
+def test_codec_golden_cases(case):
+    _, bits, dbits, xs, codes = case
+    gd, gc = oracle_block(xs, bits)
+    assert gd == dbits
+    assert gc[:len(codes)] == codes
+    assert all(c == 0 for c in gc[len(xs):])
+
+
+def test_nibble_packing_golden():
+    q = np.zeros((1, 32), np.int16)
+    q[0, 0], q[0, 1] = 7, -7
+    packed = O.pack_codes(q, 4)
+    assert packed.shape == (1, 16)
+    assert packed[0, 0] == 0x1F and packed[0, 1] == 0x88
+    q8 = np.array([[-1, 127, -127, 0] + [0] * 28], np.int16)
+    assert O.pack_codes(q8, 8)[0, :4].tolist() == [0xFF, 0x7F, 0x81, 0x00]
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_codec_invariants(bits):
+    qmax = 127 if bits == 8 else 7
+    k, _, _ = I.workload_small(11, 512, 2, 128, 2, 1, n_outliers=8)
+    x = k.reshape(-1, 128)
+    q, d = O.quantize_rows(x, bits)
+    dd = np.repeat(d.astype(np.float64), 32, axis=1)
+    assert np.all(np.abs(q) <= qmax)
+    normal = dd >= 2.0 ** -14
+    assert np.all(np.abs(x - q * dd)[normal] <= dd[normal] / 2)
+    packed = O.pack_codes(q, bits)
+    if bits == 4:
+        assert np.all((packed & 0xF) >= 1) and np.all((packed >> 4) >= 1)
+        assert np.all((packed & 0xF) <= 15)
+    else:
+        assert not np.any(packed.view(np.int8) == -128)
+    assert np.array_equal(O.unpack_codes(packed, bits, 128), q)
+    z, dz = O.quantize_rows(np.zeros((3, 64), np.float32), bits)
+    assert not z.any() and not dz.astype(np.float32).any()
+
+
+def test_fp16_layout_roundtrip():
+    x = I.normal((16, 64), 5)
+    c, s = O.encode_rows(x, 16)
+    assert s is None
+    assert np.array_equal(O.dequant_rows(c, s, 16, 64), x.astype(np.float16).astype(np.float64))
+
+
+def test_append_is_chunk_invariant():
+    k, v, _ = I.workload_small(12, 700, 2, 64, 4, 1)
+    for layout in range(5):
+        one = O.OracleCache(layout, 1, 2, 64, 700)
+        one.append(0, k, v)
+        parts = O.OracleCache(layout, 1, 2, 64, 700)
+        for a, b in ((0, 1), (1, 300), (300, 333), (333, 700)):
+            parts.append(0, k[a:b], v[a:b])
+        for name in ("Kc", "Ks", "Vc", "Vs"):
+            assert np.array_equal(getattr(one, name), getattr(parts, name))
+
+
+# ---------------------------------------------------------------------------
+# attention
+# ---------------------------------------------------------------------------
+def brute_attention(q, keys, values, scale):
+    """Pure-Python softmax attention of one query vector (math.fsum / math.exp)."""
+    s = [scale * math.fsum(qi * ki for qi, ki in zip(q, kr)) for kr in keys]
+    m = max(s)
+    w = [math.exp(x - m) for x in s]
+    tot = math.fsum(w)
+    return [math.fsum(wi * vr[j] for wi, vr in zip(w, values)) / tot for j in range(len(values[0]))]
+
+
+@pytest.mark.parametrize("layout", [0, 2, 3])
+def test_decode_matches_bruteforce(layout):
+    k, v, q = I.workload_small(21, 5, 2, 32 * 2, 4, 1)
+    c = O.OracleCache(layout, 1, 2, 64, 5)
+    c.append(0, k, v)
+    got = O.attend_decode([c], 0, q, 0.125)
+    for h in range(4):
+        kv = h // 2
+        want = brute_attention(q[0, h].astype(float).tolist(), c.keys(0, kv).tolist(), c.values(0, kv).tolist(), 0.125)
+        assert np.max(np.abs(got[0, h] - want)) <= 1e-12
+
+
+def test_chunk_matches_bruteforce():
+    k, v, q = I.workload_small(22, 7, 1, 32, 3, 3)
+    c = O.OracleCache(2, 1, 1, 32, 7)
+    c.append(0, k, v)
+    got = O.attend_chunk(c, 0, q, 3, 0.3)
+    kh, vh = c.keys(0, 0).tolist(), c.values(0, 0).tolist()
+    for j in range(3):
+        pos = 7 - 3 + j
+        for h in range(3):
+            want = brute_attention(q[j, h].astype(float).tolist(), kh[:pos + 1], vh[:pos + 1], 0.3)
+            assert np.max(np.abs(got[j, h] - want)) <= 1e-12
+
+
+def test_one_token_returns_its_value():
+    k, v, q = I.workload_small(23, 1, 2, 64, 4, 1)
+    c = O.OracleCache(2, 1, 2, 64, 1)
+    c.append(0, k, v)
+    out = O.attend_decode([c], 0, q, 0.125)
+    for h in range(4):
+        assert np.array_equal(out[0, h], c.values(0, h // 2)[0])
+
+
+def test_equal_keys_or_zero_query_average_values():
+    _, v, q = I.workload_small(24, 9, 1, 64, 2, 1)
+    k = np.repeat(I.normal((1, 1, 64), 25), 9, axis=0)
+    c = O.OracleCache(1, 1, 1, 64, 9)
+    c.append(0, k, v)
+    mean = c.values(0, 0).mean(axis=0)
+    assert np.max(np.abs(O.attend_decode([c], 0, q, 0.125)[0, 0] - mean)) < 1e-13
+    c2 = O.OracleCache(4, 1, 1, 64, 9)
+    c2.append(0, I.normal((9, 1, 64), 26), v)
+    out = O.attend_decode([c2], 0, np.zeros((1, 2, 64), np.float32), 0.125)
+    assert np.max(np.abs(out[0, 1] - c2.values(0, 0).mean(axis=0))) < 1e-13
+
+
+def test_two_token_closed_form():
+    # keys along e0 with lengths 2 and -1, query 3 e0, scale 0.5: scores 3 and -1.5
+    k = np.zeros((2, 1, 32), np.float32)
+    k[0, 0, 0], k[1, 0, 0] = 2.0, -1.0
+    v = np.zeros((2, 1, 32), np.float32)
+    v[0, 0, :], v[1, 0, :] = 1.0, -2.0
+    q = np.zeros((1, 1, 32), np.float32)
+    q[0, 0, 0] = 3.0
+    c = O.OracleCache(0, 1, 1, 32, 2)
+    c.append(0, k, v)
+    w1 = math.exp(-4.5)                      # e^(s1 - s0)
+    want = (1.0 + w1 * -2.0) / (1.0 + w1)
+    out = O.attend_decode([c], 0, q, 0.5)
+    assert np.max(np.abs(out[0, 0] - want)) < 1e-14
+
+
+def test_gqa_group_mapping():
+    hkv, g = 4, 3
+    k = I.normal((6, hkv, 64), 27)
+    v = np.zeros((6, hkv, 64), np.float32)
+    for h in range(hkv):
+        v[:, h, :] = h + 1
+    c = O.OracleCache(0, 1, hkv, 64, 6)
+    c.append(0, k, v)
+    out = O.attend_decode([c], 0, I.normal((1, hkv * g, 64), 28), 0.125)
+    for h in range(hkv * g):
+        assert np.allclose(out[0, h], h // g + 1, atol=1e-12)
+
+
+def test_causal_mask_inclusive():
+    # zero queries average the visible values; v_t = t makes that average pos / 2
+    n_tok, n_new = 40, 9
+    v = np.broadcast_to(np.arange(n_tok, dtype=np.float32)[:, None, None], (n_tok, 1, 32)).copy()
+    c = O.OracleCache(0, 1, 1, 32, n_tok)
+    c.append(0, I.normal((n_tok, 1, 32), 29), v)
+    out = O.attend_chunk(c, 0, np.zeros((n_new, 2, 32), np.float32), n_new, 0.2)
+    for j in range(n_new):
+        assert np.allclose(out[j], (n_tok - n_new + j) / 2, atol=1e-12)
+
+
+def test_fp16_layout_equals_unquantized_attention():
+    k, v, q = I.workload_small(30, 50, 2, 64, 4, 1)
+    k, v = k.astype(np.float16).astype(np.float32), v.astype(np.float16).astype(np.float32)
+    c = O.OracleCache(0, 1, 2, 64, 50)
+    c.append(0, k, v)
+    out = O.attend_decode([c], 0, q, 0.125)
+    for kv in range(2):
+        assert np.array_equal(c.keys(0, kv), k[:, kv].astype(np.float64))
+        assert np.array_equal(c.values(0, kv), v[:, kv].astype(np.float64))
+        want = O.attention_exact(q[0, 2 * kv:2 * kv + 2], k[:, kv].astype(np.float64),
+                                 v[:, kv].astype(np.float64), 0.125)
+        assert np.array_equal(out[0, 2 * kv:2 * kv + 2], want)
+
+
+@pytest.mark.parametrize("layout", [1, 2, 3, 4])
+def test_quantized_attention_within_perturbation_bound(layout):
+    k, v, q = I.workload_small(31, 200, 1, 64, 1, 1, n_outliers=4)
+    c = O.OracleCache(layout, 1, 1, 64, 200)
+    c.append(0, k, v)
+    scale = 0.125
+    kh, vh = c.keys(0, 0), c.values(0, 0)
+    qq = q[0, 0].astype(np.float64)
+    delta = scale * np.max(np.abs(kh - k[:, 0]) @ np.abs(qq))
+    bound = (math.exp(2 * delta) - 1) * np.max(np.abs(v)) + np.max(np.abs(vh - v[:, 0]))
+    exact = O.attention_exact(q[0, :1], k[:, 0].astype(np.float64), v[:, 0].astype(np.float64), scale)
+    got = O.attend_decode([c], 0, q, scale)[0, 0]
+    assert np.max(np.abs(got - exact[0])) <= bound
+
+
+def test_reuse_invariant_turn_equals_recompute():
+    # keep the cache and process only the new tokens == recompute the whole context
+    n_ctx, n_new = 300, 37
+    k, v, q = I.workload_small(32, n_ctx + n_new, 2, 64, 8, n_ctx + n_new, n_outliers=4)
+    turn = O.OracleCache(2, 1, 2, 64, n_ctx + n_new)
+    turn.append(0, k[:n_ctx], v[:n_ctx])
+    turn.append(0, k[n_ctx:], v[n_ctx:])
+    got = O.attend_chunk(turn, 0, q[n_ctx:], n_new, 0.125)
+    full = O.OracleCache(2, 1, 2, 64, n_ctx + n_new)
+    full.append(0, k, v)
+    want = O.attend_chunk(full, 0, q, n_ctx + n_new, 0.125)[n_ctx:]
+    assert np.max(np.abs(got - want)) <= 1e-12
+    # and the last row of a turn is the decode of that position
+    dec = O.attend_decode([turn], 0, q[-1:], 0.125)
+    assert np.max(np.abs(got[-1] - dec[0])) <= 1e-12
+
+
+def test_sampled_rows_match_full_chunk():
+    k, v, q = I.workload_small(33, 150, 2, 64, 4, 60)
+    c = O.OracleCache(2, 1, 2, 64, 150)
+    c.append(0, k, v)
+    full = O.attend_chunk(c, 0, q, 60, 0.125)
+    rows = np.array([0, 17, 59])
+    assert np.max(np.abs(O.attend_chunk(c, 0, q, 60, 0.125, rows=rows) - full[rows])) <= 1e-13
+
+
+def test_keys_more_sensitive_than_values():
+    # KVSplit page, "Assimetria entre key e value": K4V8 loses more than K8V4 at equal bits
+    errs = {}
+    n = 1024
+    z = I.normal((n, 1, 128), 34)
+    sc = np.exp(np.random.default_rng(35).standard_normal((1, 1, 128))).astype(np.float32)
+    k, v, q = z * sc, I.normal((n, 1, 128), 36), I.normal((1, 8, 128), 37)
+    exact = np.stack([O.attention_exact(q[0, h:h + 1], k[:, 0].astype(np.float64), v[:, 0].astype(np.float64),
+                                        128 ** -0.5)[0] for h in range(8)])
+    for name in ("K8V4", "K4V8"):
+        c = O.OracleCache(O.LAYOUT_IDS[name], 1, 1, 128, n)
+        c.append(0, k, v)
+        errs[name] = np.sqrt(np.mean((O.attend_decode([c], 0, q, 128 ** -0.5)[0] - exact) ** 2))
+    assert errs["K4V8"] > errs["K8V4"]
+
+
+def test_decode_rejects_empty_cache():
+    c = O.OracleCache(2, 1, 1, 64, 10)
+    with pytest.raises(ValueError):
+        O.attend_decode([c], 0, np.zeros((1, 1, 64), np.float32), 0.125)
