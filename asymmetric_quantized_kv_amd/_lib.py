@@ -1,0 +1,229 @@
+"""ctypes binding of ``libkvq.so`` (declared in ``include/kvq.h``).
+
+Argument marshalling only: every function here forwards to the C entry point of
+the same name; torch tensors supply device pointers and the current HIP stream.
+There is no fallback: if the library is missing the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes as C
+from pathlib import Path
+
+LIB_PATH = Path(__file__).resolve().with_name("libkvq.so")
+
+KV_OK, KV_EINVAL, KV_ECAPACITY, KV_ENOMEM, KV_EUNSUPPORTED, KV_EEMPTY, KV_EHIP = 0, -1, -2, -3, -4, -5, -6
+KV_FP16, KV_K8V8, KV_K8V4, KV_K4V8, KV_K4V4 = 0, 1, 2, 3, 4
+KV_F32, KV_BF16, KV_F16 = 0, 1, 2
+KV_PLANE_KC, KV_PLANE_KS, KV_PLANE_VC, KV_PLANE_VS = 0, 1, 2, 3
+LAYOUT_IDS = {"FP16": 0, "K8V8": 1, "K8V4": 2, "K4V8": 3, "K4V4": 4}
+STATUS_NAMES = {0: "KV_OK", -1: "KV_EINVAL", -2: "KV_ECAPACITY", -3: "KV_ENOMEM",
+                -4: "KV_EUNSUPPORTED", -5: "KV_EEMPTY", -6: "KV_EHIP"}
+
+_SIGS = {
+    "kv_cache_create": (C.c_void_p, [C.c_int, C.c_int, C.c_int, C.c_int, C.c_int64]),
+    "kv_cache_destroy": (None, [C.c_void_p]),
+    "kv_append_quant": (C.c_int, [C.c_void_p, C.c_int, C.c_void_p, C.c_void_p, C.c_int, C.c_int64, C.c_void_p]),
+    "kv_attend_decode": (C.c_int, [C.c_void_p, C.c_int, C.c_int, C.c_void_p, C.c_int, C.c_int, C.c_float,
+                                   C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
+    "kv_decode_workspace_bytes": (C.c_int64, [C.c_void_p, C.c_int, C.c_int, C.c_int]),
+    "kv_attend_chunk": (C.c_int, [C.c_void_p, C.c_int, C.c_void_p, C.c_int, C.c_int, C.c_int64, C.c_float,
+                                  C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
+    "kv_chunk_workspace_bytes": (C.c_int64, [C.c_void_p, C.c_int, C.c_int, C.c_int64]),
+    "kv_footprint_bytes": (C.c_int64, [C.c_void_p]),
+    "kv_layout_footprint_bytes": (C.c_int64, [C.c_int, C.c_int, C.c_int, C.c_int, C.c_int64]),
+    "kv_cache_len": (C.c_int64, [C.c_void_p, C.c_int]),
+    "kv_cache_reset": (C.c_int, [C.c_void_p]),
+    "kv_cache_truncate": (C.c_int, [C.c_void_p, C.c_int, C.c_int64]),
+    "kv_cache_plane": (C.c_int, [C.c_void_p, C.c_int, C.c_int, C.c_int, C.POINTER(C.c_void_p),
+                                 C.POINTER(C.c_int64)]),
+    "kv_cache_copy_plane": (C.c_int, [C.c_void_p, C.c_int, C.c_int, C.c_int, C.c_int64, C.c_int64,
+                                      C.c_void_p, C.c_void_p]),
+    "kv_last_error": (C.c_char_p, []),
+    "kv_last_status": (C.c_int, []),
+}
+
+_lib = None
+
+
+class KVError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{STATUS_NAMES.get(code, code)}: {msg}")
+        self.code = code
+
+
+def lib() -> C.CDLL:
+    """Load ``libkvq.so`` once.  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not LIB_PATH.exists():
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m asymmetric_quantized_kv_amd.build`")
+        h = C.CDLL(str(LIB_PATH))
+        for name, (res, args) in _SIGS.items():
+            f = getattr(h, name)
+            f.restype, f.argtypes = res, args
+        _lib = h
+    return _lib
+
+
+def kv_last_error() -> str:
+    return lib().kv_last_error().decode()
+
+
+def kv_last_status() -> int:
+    return lib().kv_last_status()
+
+
+def _check(rc: int) -> int:
+    if rc < 0:
+        raise KVError(rc, kv_last_error())
+    return rc
+
+
+# ---------------------------------------------------------------------------
+# torch plumbing
+# ---------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    codes = {torch.float32: KV_F32, torch.bfloat16: KV_BF16, torch.float16: KV_F16}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return codes[t.dtype]
+
+
+def _dev_ptr(t, name: str) -> int:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return _torch().cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+# ---------------------------------------------------------------------------
+# entry points
+# ---------------------------------------------------------------------------
+def kv_cache_create(layout, n_layers: int, n_kv_heads: int, head_dim: int, max_tokens: int) -> int:
+    if isinstance(layout, str):
+        layout = LAYOUT_IDS[layout]
+    h = lib().kv_cache_create(int(layout), n_layers, n_kv_heads, head_dim, max_tokens)
+    if not h:
+        raise KVError(lib().kv_last_status(), kv_last_error())
+    return h
+
+
+def kv_cache_destroy(cache: int) -> None:
+    lib().kv_cache_destroy(cache)
+
+
+def kv_append_quant(cache: int, layer: int, k, v, stream=None) -> None:
+    """k, v: device tensors [n_new, n_kv_heads, head_dim] (fp32 / bf16 / fp16)."""
+    if k.shape != v.shape or k.dtype != v.dtype or k.dim() != 3:
+        raise ValueError("k and v must be [n_new, n_kv_heads, head_dim] of one dtype")
+    _check(lib().kv_append_quant(cache, layer, _dev_ptr(k, "k"), _dev_ptr(v, "v"), _dtype_code(k),
+                                 k.shape[0], _stream(stream)))
+
+
+def _handles(sessions):
+    arr = (C.c_void_p * len(sessions))(*sessions)
+    return arr
+
+
+def kv_decode_workspace_bytes(sessions, layer: int, n_q_heads: int) -> int:
+    return _check(lib().kv_decode_workspace_bytes(_handles(sessions), len(sessions), layer, n_q_heads))
+
+
+def kv_attend_decode(sessions, layer: int, q, sm_scale: float, out=None, workspace=None, stream=None):
+    """q: device [n_sessions, n_q_heads, head_dim]; returns out (fp32, same shape)."""
+    torch = _torch()
+    n_s, hq, d = q.shape
+    if n_s != len(sessions):
+        raise ValueError("q's first dimension must equal the number of sessions")
+    if out is None:
+        out = torch.empty((n_s, hq, d), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        nb = kv_decode_workspace_bytes(sessions, layer, hq)
+        workspace = torch.empty(max(nb, 16), dtype=torch.uint8, device=q.device)
+    _check(lib().kv_attend_decode(_handles(sessions), len(sessions), layer, _dev_ptr(q, "q"), _dtype_code(q),
+                                  hq, float(sm_scale), _dev_ptr(out, "out"), _dev_ptr(workspace, "workspace"),
+                                  workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def kv_chunk_workspace_bytes(cache: int, layer: int, n_q_heads: int, n_new: int) -> int:
+    return _check(lib().kv_chunk_workspace_bytes(cache, layer, n_q_heads, n_new))
+
+
+def kv_attend_chunk(cache: int, layer: int, q, n_new: int, sm_scale: float, out=None, workspace=None,
+                    stream=None):
+    """q: device [n_new, n_q_heads, head_dim]; returns out (fp32, same shape)."""
+    torch = _torch()
+    n, hq, d = q.shape
+    if n != n_new:
+        raise ValueError("q's first dimension must equal n_new")
+    if out is None:
+        out = torch.empty((n, hq, d), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        nb = kv_chunk_workspace_bytes(cache, layer, hq, n_new)
+        workspace = torch.empty(max(nb, 16), dtype=torch.uint8, device=q.device)
+    _check(lib().kv_attend_chunk(cache, layer, _dev_ptr(q, "q"), _dtype_code(q), hq, n_new, float(sm_scale),
+                                 _dev_ptr(out, "out"), _dev_ptr(workspace, "workspace"),
+                                 workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def kv_footprint_bytes(cache: int) -> int:
+    return _check(lib().kv_footprint_bytes(cache))
+
+
+def kv_layout_footprint_bytes(layout, n_layers: int, n_kv_heads: int, head_dim: int, max_tokens: int) -> int:
+    if isinstance(layout, str):
+        layout = LAYOUT_IDS[layout]
+    return _check(lib().kv_layout_footprint_bytes(int(layout), n_layers, n_kv_heads, head_dim, max_tokens))
+
+
+def kv_cache_len(cache: int, layer: int) -> int:
+    return _check(lib().kv_cache_len(cache, layer))
+
+
+def kv_cache_reset(cache: int) -> None:
+    _check(lib().kv_cache_reset(cache))
+
+
+def kv_cache_truncate(cache: int, layer: int, new_len: int) -> None:
+    _check(lib().kv_cache_truncate(cache, layer, new_len))
+
+
+def kv_cache_plane(cache: int, layer: int, kv_head: int, plane: int):
+    """(device address, row bytes) of one plane."""
+    p, rb = C.c_void_p(), C.c_int64()
+    _check(lib().kv_cache_plane(cache, layer, kv_head, plane, C.byref(p), C.byref(rb)))
+    return (p.value or 0), rb.value
+
+
+def kv_cache_copy_plane(cache: int, layer: int, kv_head: int, plane: int, row0: int, n_rows: int, dst,
+                        stream=None):
+    """Copy plane rows into the device uint8 tensor ``dst`` (n_rows * row_bytes bytes)."""
+    _check(lib().kv_cache_copy_plane(cache, layer, kv_head, plane, row0, n_rows, _dev_ptr(dst, "dst"),
+                                     _stream(stream)))
+    return dst
+
+
+def read_plane(cache: int, layer: int, kv_head: int, plane: int, row0: int, n_rows: int):
+    """Host numpy copy [n_rows, row_bytes] of plane rows (synchronizes the stream)."""
+    torch = _torch()
+    _, rb = kv_cache_plane(cache, layer, kv_head, plane)
+    buf = torch.empty((n_rows, rb), dtype=torch.uint8, device="cuda")
+    if rb and n_rows:
+        kv_cache_copy_plane(cache, layer, kv_head, plane, row0, n_rows, buf)
+    return buf.cpu().numpy()

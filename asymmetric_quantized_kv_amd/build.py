@@ -1,0 +1,77 @@
+"""Build ``libkvq.so`` (the C-ABI library) for gfx950 with hipcc, in-tree.
+
+Usage: ``python -m asymmetric_quantized_kv_amd.build [--jobs N]``.  Every call
+recompiles all sources (each translation unit in parallel) and relinks.
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+from pathlib import Path
+
+PKG = Path(__file__).resolve().parent
+ROOT = PKG.parent
+CSRC = PKG / "csrc"
+BUILD = ROOT / "_build"
+LIB = PKG / "libkvq.so"
+SOURCES = ["kvq_host.cpp", "append.hip", "decode.hip", "merge.hip", "chunk.hip"]
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and Path(cand).exists():
+            return cand
+    raise RuntimeError("hipcc not found (set HIPCC or install ROCm)")
+
+
+def compile_flags() -> list[str]:
+    return [
+        f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+        "-I", str(ROOT / "include"), "-I", str(CSRC),
+        # IEEE fp32 division and denormals: the codec must be bit-exact.
+        "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-gpu-flush-denormals-to-zero",
+        # no packed fp32 instructions anywhere in device code
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
+    ]
+
+
+def _compile(src: str) -> Path:
+    BUILD.mkdir(exist_ok=True)
+    obj = BUILD / (src + ".o")
+    lang = ["-x", "hip"] if src.endswith(".hip") else []
+    cmd = [hipcc(), *compile_flags(), *lang, "-c", str(CSRC / src), "-o", str(obj)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    noisy = [ln for ln in (r.stdout + r.stderr).splitlines()
+             if ln.strip() and "packed-fp32-ops" not in ln]
+    if noisy:
+        sys.stderr.write("\n".join(noisy) + "\n")
+    return obj
+
+
+def build(jobs: int | None = None, verbose: bool = True) -> Path:
+    jobs = jobs or min(len(SOURCES), os.cpu_count() or 1)
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        objs = list(ex.map(_compile, SOURCES))
+    tmp = LIB.with_suffix(".so.tmp")
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *map(str, objs), "-o", str(tmp)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, LIB)
+    if verbose:
+        print(f"built {LIB}")
+    return LIB
+
+
+if __name__ == "__main__":
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--jobs", type=int, default=None)
+    build(ap.parse_args().jobs)

@@ -1,0 +1,145 @@
+// Quantize-on-append: new tokens' keys and values are encoded block by block and
+// written at the end of the session cache ("KVSplit -- contexto 2 a 3 vezes mais longo
+// em Apple Silicon", section "Opinioes no Hacker News": the cache is quantized at run
+// time as tokens are processed; bit widths per "Principais resultados de benchmark").
+//
+// Eight lanes own one 32-element block (4 elements each): loads and stores of a wave
+// are contiguous, the block's amax is reduced over the 8 lanes, and every lane encodes
+// its own 4 elements.  Rounding follows the format fixed in include/kvq.h: fp32 IEEE
+// division, fp16 round-to-nearest-even for the scale, round-half-away for the codes.
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+template <int DT>
+__device__ __forceinline__ void load4(const void* src, int64_t elem, float (&x)[4]) {
+  if constexpr (DT == 0) {  // fp32
+    float4 v = *reinterpret_cast<const float4*>(static_cast<const float*>(src) + elem);
+    x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+  } else {
+    uint2 v = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(src) + elem);
+    uint32_t w[4] = {v.x & 0xffffu, v.x >> 16, v.y & 0xffffu, v.y >> 16};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (DT == 1) {  // bf16: the upper half of an fp32
+        x[i] = __uint_as_float(w[i] << 16);
+      } else {                  // fp16
+        _Float16 h;
+        uint16_t b = (uint16_t)w[i];
+        __builtin_memcpy(&h, &b, 2);
+        x[i] = (float)h;
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ uint16_t f16_bits(float x) {
+  _Float16 h = (_Float16)x;  // round to nearest even
+  uint16_t b;
+  __builtin_memcpy(&b, &h, 2);
+  return b;
+}
+
+template <int BITS, int DT, int D>
+__device__ __forceinline__ void encode_one(const void* src, uint8_t* region, const Geom& g,
+                                           int64_t row, int64_t elem, int blk, int sub,
+                                           int64_t code_off, int64_t scale_off, int code_row,
+                                           int scale_row) {
+  float x[4];
+  load4<DT>(src, elem, x);
+  uint8_t* codes = region + code_off + row * code_row;
+  if constexpr (BITS == 16) {
+    uint32_t lo = f16_bits(x[0]) | ((uint32_t)f16_bits(x[1]) << 16);
+    uint32_t hi = f16_bits(x[2]) | ((uint32_t)f16_bits(x[3]) << 16);
+    *reinterpret_cast<uint2*>(codes + (blk * 32 + sub * 4) * 2) = make_uint2(lo, hi);
+  } else {
+    constexpr float qmax = BITS == 8 ? 127.f : 7.f;
+    float amax = fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
+    amax = fmaxf(amax, __shfl_xor(amax, 1, 8));
+    amax = fmaxf(amax, __shfl_xor(amax, 2, 8));
+    amax = fmaxf(amax, __shfl_xor(amax, 4, 8));
+    float d32 = fminf(amax / qmax, 65504.f);       // IEEE division, saturate
+    _Float16 d16 = (_Float16)d32;                   // round to nearest even
+    float d = (float)d16;
+    int q[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float y = d != 0.f ? x[i] / d : 0.f;          // IEEE division
+      float r = roundf(y);                          // half away from zero
+      r = fminf(fmaxf(r, -qmax), qmax);
+      q[i] = (int)r;
+    }
+    if constexpr (BITS == 8) {
+      uint32_t w = (q[0] & 0xff) | ((q[1] & 0xff) << 8) | ((q[2] & 0xff) << 16) | ((uint32_t)(q[3] & 0xff) << 24);
+      *reinterpret_cast<uint32_t*>(codes + blk * 32 + sub * 4) = w;
+    } else {
+      uint32_t u0 = q[0] + 8, u1 = q[1] + 8, u2 = q[2] + 8, u3 = q[3] + 8;
+      uint16_t w = (uint16_t)(u0 | (u1 << 4) | (u2 << 8) | (u3 << 12));
+      *reinterpret_cast<uint16_t*>(codes + blk * 16 + sub * 2) = w;
+    }
+    if (sub == 0) {
+      uint16_t b;
+      __builtin_memcpy(&b, &d16, 2);
+      *reinterpret_cast<uint16_t*>(region + scale_off + row * scale_row + blk * 2) = b;
+    }
+  }
+}
+
+template <int KB, int VB, int DT, int D>
+__global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
+  constexpr int kNb = D / kBlock;
+  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t total = a.n * a.hkv * kNb * 8;
+  if (tid >= total) return;       // whole 8-lane groups drop out together (total % 8 == 0)
+  const int sub = (int)(tid & 7);
+  const int64_t bidx = tid >> 3;  // (token, head, block)
+  const int blk = (int)(bidx % kNb);
+  const int64_t th = bidx / kNb;  // token * hkv + head
+  const int head = (int)(th % a.hkv);
+  const int64_t tok = th / a.hkv;
+  const int64_t elem = th * D + blk * kBlock + sub * 4;
+  const int64_t row = a.t0 + tok;
+  uint8_t* region = a.layer_base + (int64_t)head * a.g.region();
+  if (blockIdx.y == 0)
+    encode_one<KB, DT, D>(a.src[0], region, a.g, row, elem, blk, sub, a.g.off_kc(), a.g.off_ks(), a.g.kc, a.g.ks);
+  else
+    encode_one<VB, DT, D>(a.src[1], region, a.g, row, elem, blk, sub, a.g.off_vc(), a.g.off_vs(), a.g.vc, a.g.vs);
+}
+
+template <int KB, int VB, int DT, int D>
+hipError_t launch_t(const AppendArgs& a, hipStream_t s) {
+  const int64_t total = a.n * a.hkv * (D / kBlock) * 8;
+  const int64_t blocks = (total + 255) / 256;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((append_kernel<KB, VB, DT, D>), dim3((unsigned)blocks, 2), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int KB, int VB, int DT>
+hipError_t launch_d(const AppendArgs& a, int d, hipStream_t s) {
+  if (d == 64) return launch_t<KB, VB, DT, 64>(a, s);
+  if (d == 128) return launch_t<KB, VB, DT, 128>(a, s);
+  return hipErrorInvalidValue;
+}
+
+template <int KB, int VB>
+hipError_t launch_dt(const AppendArgs& a, int dtype, int d, hipStream_t s) {
+  if (dtype == 0) return launch_d<KB, VB, 0>(a, d, s);
+  if (dtype == 1) return launch_d<KB, VB, 1>(a, d, s);
+  if (dtype == 2) return launch_d<KB, VB, 2>(a, d, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_append(const AppendArgs& a, int kbits, int vbits, int dtype, int d, hipStream_t s) {
+  if (kbits == 16 && vbits == 16) return launch_dt<16, 16>(a, dtype, d, s);
+  if (kbits == 8 && vbits == 8) return launch_dt<8, 8>(a, dtype, d, s);
+  if (kbits == 8 && vbits == 4) return launch_dt<8, 4>(a, dtype, d, s);
+  if (kbits == 4 && vbits == 8) return launch_dt<4, 8>(a, dtype, d, s);
+  if (kbits == 4 && vbits == 4) return launch_dt<4, 4>(a, dtype, d, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace kvq

@@ -1,0 +1,97 @@
+// Internal declarations shared by the host side of the C ABI and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace kvq {
+
+constexpr int kBlock = 32;          // elements per quantization block
+constexpr int kGranule = 256;       // capacity granule (tokens)
+constexpr int kMaxSessions = 64;    // sessions per decode launch (kernel-argument table)
+constexpr int kDecodeChunk = 128;   // tokens one wave scores before its softmax update
+constexpr int kDecodeWaveTokens = 4 * kDecodeChunk;  // split granularity of decode
+constexpr int kChunkRows = 128;     // query rows per chunk-prefill workgroup
+constexpr int kChunkKeys = 64;      // keys per chunk-prefill tile
+
+__host__ __device__ constexpr int code_row_bytes(int bits, int d) {
+  return bits == 16 ? 2 * d : (bits == 8 ? d : d / 2);
+}
+__host__ __device__ constexpr int scale_row_bytes(int bits, int d) {
+  return bits == 16 ? 0 : 2 * (d / kBlock);
+}
+
+// Planes of one (layer, KV head) region, token-major, in this order: KC, KS, VC, VS.
+struct Geom {
+  int64_t cap;      // tokens per plane
+  int32_t kc, ks, vc, vs;  // row bytes
+  __host__ __device__ int64_t region() const { return cap * (int64_t)(kc + ks + vc + vs); }
+  __host__ __device__ int64_t off_kc() const { return 0; }
+  __host__ __device__ int64_t off_ks() const { return cap * (int64_t)kc; }
+  __host__ __device__ int64_t off_vc() const { return cap * (int64_t)(kc + ks); }
+  __host__ __device__ int64_t off_vs() const { return cap * (int64_t)(kc + ks + vc); }
+};
+
+struct AppendArgs {
+  const void* src[2];     // k, v: [n][Hkv][D]
+  uint8_t* layer_base;    // arena + layer * Hkv * region
+  Geom g;
+  int64_t t0;             // first row written
+  int64_t n;              // tokens
+  int hkv;
+};
+
+struct SessionRef {
+  const uint8_t* base;    // arena + layer * Hkv * region of this session
+  int64_t cap;
+  int64_t len;
+};
+
+struct DecodeArgs {
+  SessionRef sess[kMaxSessions];
+  int n_sess;             // sessions in this launch
+  int sess0;              // global index of sess[0] (rows of q / out / workspace)
+  int hkv, hq, group;
+  int n_splits;
+  int64_t tps;            // tokens per split, multiple of kDecodeWaveTokens
+  const void* q;
+  int q_dtype;
+  float qk_scale;         // sm_scale * log2(e)
+  float* ws;              // [S][Hq][n_splits][D + 2] partials when n_splits > 1
+  float* out;             // [S][Hq][D] when n_splits == 1
+  int32_t kc, ks, vc, vs; // row bytes (shared by all sessions)
+};
+
+struct ChunkArgs {
+  const uint8_t* base;    // arena + layer * Hkv * region
+  Geom g;
+  int64_t len;            // cached tokens (the chunk is the last n_new of them)
+  int64_t n_new;
+  int hkv, hq, group;
+  int n_splits;
+  int64_t tps;            // keys per split, multiple of kChunkKeys
+  const void* q;
+  int q_dtype;
+  float qk_scale;
+  float* ws;              // [n_new][Hq][n_splits][D + 2] partials when n_splits > 1
+  float* out;             // [n_new][Hq][D] when n_splits == 1
+};
+
+struct MergeArgs {
+  const float* ws;        // [rows][n_splits][D + 2]: o (unnormalized), m (log2 units), l
+  float* out;             // [rows][D]
+  int64_t rows;
+  int n_splits;
+  int d;
+};
+
+// Launchers (one per translation unit).  They return hipErrorInvalidValue for a
+// combination that is not instantiated.
+hipError_t launch_append(const AppendArgs& a, int kbits, int vbits, int dtype, int d,
+                         hipStream_t s);
+hipError_t launch_decode(const DecodeArgs& a, int kbits, int vbits, int d, int gp,
+                         hipStream_t s);
+hipError_t launch_chunk(const ChunkArgs& a, int kbits, int vbits, int d, hipStream_t s);
+hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
+
+}  // namespace kvq

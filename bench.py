@@ -1,0 +1,292 @@
+#!/usr/bin/env python3
+"""Benchmark of the quantized session KV cache on one MI355X.
+
+Metric: K8V4 decode KV-read GB/s (% of HBM peak) + chunk-append tokens/s at a
+100K-token context.  One step is one pass of the whole hot path on synthetic,
+seeded inputs already resident in HBM:
+  * decode:  one query per session over 64 sessions x 32,768 cached tokens,
+             Hq 32 / Hkv 8 / D 128, K8V4 (split-K partial kernel + merge);
+  * turn:    a 500-token turn against a 100,000-token session, Hq 64 / Hkv 8 /
+             D 128, K8V4: quantize-on-append of the 500 tokens + causal chunk
+             attention (+ merge of context splits).  The session is rolled back to
+             100,000 tokens (a host-side length update) before every turn.
+`value` is the decode's cache bytes per second; the turn's tokens/s is reported
+beside it.  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent
+if str(ROOT) not in sys.path:
+    sys.path.insert(0, str(ROOT))
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16/bf16 matrix peak, published
+
+DEC_S, DEC_T, DEC_HQ, DEC_HKV, D = 64, 32_768, 32, 8, 128
+TURN_CTX, TURN_NEW, TURN_HQ, TURN_HKV = 100_000, 500, 64, 8
+TRAFFIC_FILE = ROOT / "profiles" / "traffic.json"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing on host cores")
+    ap.add_argument("--no-k4v8", action="store_true", help="skip the K4V8 decode on the identical inputs")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 1 GiB device copy (for HBM counter calibration)")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for f in ("decode.hip", "chunk.hip", "append.hip", "merge.hip", "kvq_internal.h", "wave_ops.h"):
+        h.update((ROOT / "asymmetric_quantized_kv_amd" / "csrc" / f).read_bytes())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if taken on these sources."""
+    try:
+        t = json.loads(TRAFFIC_FILE.read_text())
+    except (OSError, ValueError):
+        return None
+    e = t.get(kernel)
+    if not e or e.get("kernel_src_sha") != kernel_source_sha():
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import asymmetric_quantized_kv_amd as kvq
+    from asymmetric_quantized_kv_amd import inputs as I
+
+    torch.cuda.set_device(0)
+    kvq.lib()
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream()
+
+    def to_dev(x):
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev).to(torch.bfloat16).contiguous()
+
+    # ---- decode workload ---------------------------------------------------------
+    layouts = ["K8V4"] + ([] if args.no_k4v8 else ["K4V8"])
+    t0 = time.time()
+    caches = {L: [kvq.kv_cache_create(L, 1, DEC_HKV, D, DEC_T) for _ in range(DEC_S)] for L in layouts}
+    keep = {}                                    # host copies of the sessions the CPU baseline uses
+    n_cpu_sessions = 0 if args.no_cpu_baseline else 8
+    for s in range(DEC_S):
+        k, v = I.config4_session(s)
+        kd, vd = to_dev(k), to_dev(v)
+        for L in layouts:
+            kvq.kv_append_quant(caches[L][s], 0, kd, vd)
+        if s < n_cpu_sessions:
+            keep[s] = (k, v)
+        del kd, vd
+    q_dec = to_dev(I.config4_queries())
+    torch.cuda.synchronize()
+    log(f"decode caches ready ({time.time() - t0:.1f} s)")
+    dec_bytes = sum(kvq.kv_footprint_bytes(h) for h in caches["K8V4"])   # every row is cached
+    sm = D ** -0.5
+    out_dec = torch.empty((DEC_S, DEC_HQ, D), dtype=torch.float32, device=dev)
+    ws_dec = torch.empty(max(16, kvq.kv_decode_workspace_bytes(caches["K8V4"], 0, DEC_HQ)), dtype=torch.uint8,
+                         device=dev)
+
+    # ---- turn workload -------------------------------------------------------------
+    c3 = I.config3()
+    h3 = kvq.kv_cache_create("K8V4", 1, TURN_HKV, D, TURN_CTX + TURN_NEW)
+    kvq.kv_append_quant(h3, 0, to_dev(c3["k"][:TURN_CTX]), to_dev(c3["v"][:TURN_CTX]))
+    k_new, v_new = to_dev(c3["k"][TURN_CTX:]), to_dev(c3["v"][TURN_CTX:])
+    q_new = to_dev(c3["q"])
+    out_turn = torch.empty((TURN_NEW, TURN_HQ, D), dtype=torch.float32, device=dev)
+    # the workspace is sized after the append, for the length the chunk call sees
+    kvq.kv_append_quant(h3, 0, k_new, v_new)
+    ws_turn = torch.empty(max(16, kvq.kv_chunk_workspace_bytes(h3, 0, TURN_HQ, TURN_NEW)), dtype=torch.uint8,
+                          device=dev)
+    torch.cuda.synchronize()
+    log(f"turn cache ready ({time.time() - t0:.1f} s)")
+
+    def decode(L="K8V4"):
+        kvq.kv_attend_decode(caches[L], 0, q_dec, sm, out=out_dec, workspace=ws_dec)
+
+    def turn_append():
+        kvq.kv_cache_truncate(h3, 0, TURN_CTX)
+        kvq.kv_append_quant(h3, 0, k_new, v_new)
+
+    def turn_attend():
+        kvq.kv_attend_chunk(h3, 0, q_new, TURN_NEW, sm, out=out_turn, workspace=ws_turn)
+
+    for _ in range(args.warmup):
+        decode()
+        turn_append()
+        turn_attend()
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        decode()
+        ev[i][1].record(stream)
+        turn_append()
+        ev[i][2].record(stream)
+        turn_attend()
+        ev[i][3].record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - w0) * 1e3
+    dec_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    app_ms = [e[1].elapsed_time(e[2]) for e in ev]
+    chk_ms = [e[2].elapsed_time(e[3]) for e in ev]
+    mean = lambda xs: sum(xs) / len(xs)
+    dec_t, app_t, chk_t = mean(dec_ms), mean(app_ms), mean(chk_ms)
+    dec_gbps = dec_bytes / (dec_t * 1e-3) / 1e9
+    turn_tok_s = TURN_NEW / ((app_t + chk_t) * 1e-3)
+    # causal pairs of the turn: query j (position TURN_CTX + j) sees TURN_CTX + j + 1 keys
+    pairs = TURN_HQ * sum(TURN_CTX + j + 1 for j in range(TURN_NEW))
+    chunk_flop = 4.0 * D * pairs
+    chunk_tflops = chunk_flop / (chk_t * 1e-3) / 1e12
+    log(f"decode {dec_t:.4f} ms ({dec_gbps:.1f} GB/s), append {app_t:.4f} ms, chunk {chk_t:.4f} ms "
+        f"({chunk_tflops:.1f} TFLOP/s), wall {wall_ms / args.steps:.3f} ms/step")
+
+    extra = {}
+    if "K4V8" in layouts:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for _ in range(args.warmup):
+            decode("K4V8")
+        e0.record(stream)
+        for _ in range(args.steps):
+            decode("K4V8")
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t48 = e0.elapsed_time(e1) / args.steps
+        extra["decode_k4v8_GBps"] = round(dec_bytes / (t48 * 1e-3) / 1e9, 1)
+        extra["decode_k4v8_ms"] = round(t48, 4)
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        log("copy calibration: 1 GiB device-to-device copy done")
+
+    cpu = None
+    if n_cpu_sessions:
+        cpu = cpu_baseline(keep, sm)
+        extra["cpu_baseline_chunk"] = cpu_baseline_chunk(c3, sm)
+
+    record = {
+        "metric": "K8V4 decode KV-read GB/s (% HBM peak) + chunk-append tokens/s at 100K ctx",
+        "value": round(dec_gbps, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dec_t + app_t + chk_t, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8 dot (QK), f16 dot2 (PV), f16 MFMA (chunk); f32 accumulate",
+        "data": "synthetic (seeded numpy; bf16 K/V/Q)",
+        "config": {
+            "workload": "decode: 64 sessions x 32,768 cached tokens, Hq 32 / Hkv 8 / D 128, K8V4, one bf16 query "
+                        "per session; turn: 500 new tokens appended to a 100,000-token session then causal chunk "
+                        "attention, Hq 64 / Hkv 8 / D 128, K8V4",
+            "decode_cache_bytes": dec_bytes,
+            "turn_causal_pairs": pairs,
+        },
+        "hbm_frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
+        "chunk_append_tokens_per_s": round(turn_tok_s, 1),
+        "decode_ms": round(dec_t, 4),
+        "append_ms": round(app_t, 4),
+        "chunk_ms": round(chk_t, 4),
+        "roofline": {
+            "bound": "hbm", "kernel": "decode (partial pass + split merge)",
+            "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": load_traffic("decode_k8v4"),
+        },
+        "roofline_chunk": {
+            "bound": "mfma", "kernel": "chunk prefill (+ split merge)",
+            "achieved": round(chunk_tflops, 1), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(chunk_tflops / MFMA_F16_PEAK_TFLOPS, 4), "traffic": load_traffic("chunk_k8v4"),
+        },
+        "cpu_baseline": cpu,
+        "kernel_src_sha": kernel_source_sha(),
+    }
+    record.update(extra)
+    print(json.dumps(record), flush=True)
+
+
+def cpu_baseline(keep, sm):
+    """The oracle's decode on 8 of the 64 sessions (full length, all heads), on host cores."""
+    import numpy as np
+
+    import oracle as O
+    from asymmetric_quantized_kv_amd import inputs as I
+
+    q = I.config4_queries()
+    ocs = []
+    for s in sorted(keep):
+        k, v = keep[s]
+        c = O.OracleCache(2, 1, DEC_HKV, D, DEC_T)
+        c.append(0, k, v)
+        ocs.append(c)
+    sample_bytes = sum(c.footprint_bytes() for c in ocs)
+    qs = q[:len(ocs)]
+    reps, spent, cpu0 = 0, 0.0, time.process_time()
+    while spent < 10.0 and reps < 20:
+        t = time.perf_counter()
+        O.attend_decode(ocs, 0, qs, sm)
+        spent += time.perf_counter() - t
+        reps += 1
+    cpu_used = time.process_time() - cpu0
+    gbps = sample_bytes * reps / spent / 1e9
+    return {"value": round(gbps, 4), "unit": "GB/s", "cores": max(1, round(cpu_used / spent)), "kind": "oracle",
+            "sample": f"decode of sessions 0-{len(ocs) - 1} of 64 (all 8 KV heads, 32,768 tokens each), "
+                      f"{reps} repetitions, {spent:.1f} s; quantization excluded",
+            "affinity_cpus": len(os.sched_getaffinity(0))}
+
+
+def cpu_baseline_chunk(c3, sm):
+    """The oracle's chunk attention for 16 of the 500 new tokens (all 64 heads), on host cores."""
+    import numpy as np
+
+    import oracle as O
+
+    c = O.OracleCache(2, 1, TURN_HKV, D, TURN_CTX + TURN_NEW)
+    c.append(0, c3["k"], c3["v"])
+    rows = np.linspace(0, TURN_NEW - 1, 16).astype(int)
+    t, cpu0 = time.perf_counter(), time.process_time()
+    O.attend_chunk(c, 0, c3["q"], TURN_NEW, sm, rows=rows)
+    spent = time.perf_counter() - t
+    cpu_used = time.process_time() - cpu0
+    return {"value": round(len(rows) / spent, 2), "unit": "tokens/s", "cores": max(1, round(cpu_used / spent)),
+            "kind": "oracle", "sample": f"{len(rows)} of the 500 new tokens x 64 heads at 100,000 cached tokens, "
+                                        f"{spent:.1f} s; quantization excluded"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,178 @@
+/*
+ * kvq.h -- C ABI of the asymmetric quantized session KV cache for gfx950 (MI355X).
+ *
+ * A session cache keeps every token's keys and values between turns so that a new
+ * turn only processes its new tokens ("Reutilizacao de Cache KV para Conversas Longas
+ * no Apple Silicon Oferece Aceleracao de 200x", openclawradar.com, section "Principais
+ * Descobertas e Benchmarks").  Keys and values are stored with different bit widths
+ * ("KVSplit -- contexto 2 a 3 vezes mais longo em Apple Silicon", pt.news.hada.io
+ * topic 20969, sections "Principais resultados de benchmark" and "Assimetria entre key
+ * e value"), quantized when the tokens are written, independently of the model weights
+ * (same page, section "Opinioes no Hacker News").
+ *
+ * Storage format (the pages print footprints, not a format; this one reproduces every
+ * footprint the KVSplit page prints, section "Uso de memoria conforme o comprimento da
+ * sequencia"):
+ *   - per (token, KV head), head_dim is cut into blocks of 32 consecutive elements;
+ *   - 8-bit and 4-bit blocks carry one fp16 scale d = fp16_rne(fp32(amax / qmax)),
+ *     qmax = 127 or 7, saturated at 65504; codes q = clamp(round_half_away(fp32(x / d)),
+ *     -qmax, qmax), all zero when d == 0;
+ *   - 8-bit codes are int8 (two's complement); 4-bit codes are nibbles u = q + 8, byte j
+ *     of a block = u[2j] | u[2j+1] << 4; the FP16 layout stores fp16_rne(x), no scale;
+ *   - planes per (layer, KV head), token-major: KC [cap][code bytes], KS [cap][2*D/32],
+ *     VC, VS; cap = max_tokens rounded up to 256 tokens (the KVSplit page's remark on
+ *     256-byte alignment, section "Otimizacao para Apple Silicon e limitacoes").
+ *
+ * Conventions for every entry point:
+ *   - status: 0 (KV_OK) or a negative KV_E* code; kv_last_error() then holds a message
+ *     (thread-local).  All argument checks happen on the host before any launch; on a
+ *     check failure the cache is unchanged.  After a HIP error the cache is poisoned and
+ *     every later call on it returns KV_EHIP until kv_cache_destroy.
+ *   - device pointers (k, v, q, out, workspace) belong to the caller, must be 16-byte
+ *     aligned, and must stay valid until the stream has passed the call.  The library
+ *     owns the cache arena.
+ *   - every call is asynchronous on `stream` (a hipStream_t; NULL = the null stream).
+ *     The cached length of a layer advances when kv_append_quant is enqueued.
+ *   - a handle must not be used from two threads at once; handles are independent.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define KV_OK            0
+#define KV_EINVAL       -1   /* bad argument (null, range, alignment, shape mismatch)   */
+#define KV_ECAPACITY    -2   /* append past max_tokens                                   */
+#define KV_ENOMEM       -3   /* device allocation failed                                 */
+#define KV_EUNSUPPORTED -4   /* valid but not built (head_dim other than 64/128, ...)    */
+#define KV_EEMPTY       -5   /* attention over a layer with no cached token              */
+#define KV_EHIP         -6   /* a HIP call failed; the cache is poisoned                 */
+
+/* layouts: key bits x value bits (the five configurations the KVSplit page compares) */
+#define KV_FP16 0
+#define KV_K8V8 1
+#define KV_K8V4 2
+#define KV_K4V8 3
+#define KV_K4V4 4
+
+/* element types of k, v, q */
+#define KV_F32  0
+#define KV_BF16 1
+#define KV_F16  2
+
+/* planes of one (layer, KV head) */
+#define KV_PLANE_KC 0   /* key codes    */
+#define KV_PLANE_KS 1   /* key scales   */
+#define KV_PLANE_VC 2   /* value codes  */
+#define KV_PLANE_VS 3   /* value scales */
+
+typedef struct kv_cache kv_cache;
+
+/* Create an empty session cache on the current HIP device.
+ * layout: KV_FP16..KV_K4V4.  n_layers >= 1, n_kv_heads >= 1, head_dim in {64, 128}
+ * (other multiples of 32 -> KV_EUNSUPPORTED), 1 <= max_tokens <= 2^31 - 256.
+ * Allocates n_layers * n_kv_heads * round_up(max_tokens, 256) token rows, zero-filled.
+ * Returns NULL on error (kv_last_error() says why; KV_ENOMEM if hipMalloc failed). */
+kv_cache* kv_cache_create(int layout, int n_layers, int n_kv_heads, int head_dim,
+                          int64_t max_tokens);
+
+/* Free the arena.  The caller ensures no queued work still uses the cache.  NULL is a no-op. */
+void kv_cache_destroy(kv_cache* cache);
+
+/* Quantize n_new tokens and write them at rows [len, len + n_new) of `layer`
+ * (quantize-on-append; the KVSplit page, section "Opinioes no Hacker News").
+ * k, v: device, [n_new][n_kv_heads][head_dim] contiguous, element type `dtype`.
+ * Errors: KV_EINVAL (null cache/pointer, layer out of range, n_new < 0, bad dtype,
+ * misaligned pointer), KV_ECAPACITY (len + n_new > max_tokens), KV_EHIP.
+ * n_new == 0 is a no-op. */
+int kv_append_quant(kv_cache* cache, int layer, const void* k, const void* v, int dtype,
+                    int64_t n_new, void* stream);
+
+/* Single-query attention for each of n_sessions caches over all of their cached tokens
+ * of `layer`: out[s][h] = softmax(sm_scale * q[s][h] . K_s^T) V_s, with q head h reading
+ * KV head h / (n_q_heads / n_kv_heads).  The dense definition of attention over the
+ * dequantized cache; the pages discuss where it is bound (KVSplit page, "Opinioes no
+ * Hacker News": the gain comes from memory traffic).
+ * sessions: host array of n_sessions handles sharing (layout, n_layers, n_kv_heads,
+ * head_dim); their lengths may differ.  q: device [n_sessions][n_q_heads][head_dim] of
+ * q_dtype.  out: device fp32, same shape.  workspace: device scratch of at least
+ * kv_decode_workspace_bytes(...) bytes (may be NULL when that is 0).
+ * Errors: KV_EINVAL (mismatched sessions, n_q_heads % n_kv_heads, group size > 16,
+ * small workspace, null/misaligned pointers), KV_EEMPTY (a session with len == 0),
+ * KV_EHIP. */
+int kv_attend_decode(kv_cache* const* sessions, int n_sessions, int layer, const void* q,
+                     int q_dtype, int n_q_heads, float sm_scale, float* out,
+                     void* workspace, size_t ws_bytes, void* stream);
+
+/* Workspace bytes kv_attend_decode needs for these sessions; < 0 on bad arguments. */
+int64_t kv_decode_workspace_bytes(kv_cache* const* sessions, int n_sessions, int layer,
+                                  int n_q_heads);
+
+/* Causal attention of the last n_new cached positions of `layer` (the turn just
+ * appended) against everything cached so far: only the new tokens are processed
+ * (openclawradar.com page, section "Principais Descobertas e Benchmarks").
+ * Query row j sits at absolute position len - n_new + j and sees keys [0, that position],
+ * its own chunk read back quantized from the cache.
+ * q: device [n_new][n_q_heads][head_dim] of q_dtype; out: device fp32, same shape.
+ * workspace: at least kv_chunk_workspace_bytes(...) bytes.
+ * Errors: KV_EINVAL (n_new < 1 or > len, n_q_heads % n_kv_heads, small workspace,
+ * null/misaligned pointers), KV_EEMPTY (len == 0), KV_EHIP. */
+int kv_attend_chunk(kv_cache* cache, int layer, const void* q, int q_dtype, int n_q_heads,
+                    int64_t n_new, float sm_scale, float* out, void* workspace,
+                    size_t ws_bytes, void* stream);
+
+/* Workspace bytes kv_attend_chunk needs; < 0 on bad arguments. */
+int64_t kv_chunk_workspace_bytes(const kv_cache* cache, int layer, int n_q_heads,
+                                 int64_t n_new);
+
+/* Device bytes of all planes: n_layers * n_kv_heads * cap * (K row + V row), the footprint
+ * the KVSplit page tabulates (section "Uso de memoria conforme o comprimento da sequencia").
+ * < 0 for a NULL cache. */
+int64_t kv_footprint_bytes(const kv_cache* cache);
+
+/* The same footprint for a shape, without allocating (pure host arithmetic). < 0 if invalid. */
+int64_t kv_layout_footprint_bytes(int layout, int n_layers, int n_kv_heads, int head_dim,
+                                  int64_t max_tokens);
+
+/* Cached tokens of `layer` (as enqueued); < 0 on bad arguments. */
+int64_t kv_cache_len(const kv_cache* cache, int layer);
+
+/* Forget every cached token (lengths to 0; bytes are left as they are), for a full
+ * rebuild after a cache miss (openclawradar.com page, "Principais Descobertas e
+ * Benchmarks": a miss re-processes the whole context). */
+int kv_cache_reset(kv_cache* cache);
+
+/* Forget the tokens of `layer` at positions >= new_len (lengths only; bytes are left as
+ * they are and are overwritten by the next append).  Rolls a session back to an earlier
+ * turn, e.g. to re-run or discard the last turn.  KV_EINVAL if new_len is negative or
+ * larger than the cached length. */
+int kv_cache_truncate(kv_cache* cache, int layer, int64_t new_len);
+
+/* Device address and row pitch of one plane of (layer, kv_head).  *ptr is NULL and
+ * *row_bytes 0 for the scale planes of the FP16 layout. */
+int kv_cache_plane(const kv_cache* cache, int layer, int kv_head, int plane,
+                   const void** ptr, int64_t* row_bytes);
+
+/* Copy rows [row0, row0 + n_rows) of a plane to dst (device or host memory, packed with
+ * row pitch = row_bytes) on `stream`; synchronous when dst is pageable host memory. */
+int kv_cache_copy_plane(const kv_cache* cache, int layer, int kv_head, int plane,
+                        int64_t row0, int64_t n_rows, void* dst, void* stream);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* kv_last_error(void);
+
+/* Status code of the last failed call on this thread (KV_OK if none); the way to get
+ * the reason a kv_cache_create returned NULL. */
+int kv_last_status(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

@@ -1,0 +1,99 @@
+"""The C ABI on the host: the library loads, exports every symbol include/kvq.h
+declares, and rejects bad arguments before any HIP call (no GPU needed)."""
+from __future__ import annotations
+
+import ctypes as C
+import re
+from pathlib import Path
+
+import pytest
+
+import oracle as O
+import asymmetric_quantized_kv_amd as kvq
+from asymmetric_quantized_kv_amd import _lib
+
+ROOT = Path(__file__).resolve().parent.parent
+HEADER = ROOT / "include" / "kvq.h"
+
+
+@pytest.fixture(scope="session", autouse=True)
+def built_library():
+    if not _lib.LIB_PATH.exists():
+        from asymmetric_quantized_kv_amd import build
+        build.build(verbose=False)
+    return kvq.lib()
+
+
+def header_functions():
+    text = re.sub(r"/\*.*?\*/", "", HEADER.read_text(), flags=re.S)
+    return sorted(set(re.findall(r"\b(kv_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_north_star_calls():
+    names = header_functions()
+    for n in ("kv_cache_create", "kv_append_quant", "kv_attend_decode", "kv_attend_chunk", "kv_footprint_bytes"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(built_library):
+    names = header_functions()
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(built_library, n), n
+    assert set(names) <= set(_lib._SIGS), "binding misses a declared entry point"
+
+
+@pytest.mark.parametrize("layout", range(5))
+def test_layout_footprint_matches_oracle(layout):
+    for L, hkv, d, t in [(22, 4, 64, 8192), (22, 4, 64, 128), (1, 8, 128, 100_500), (3, 5, 96, 1), (2, 1, 32, 257)]:
+        assert kvq.kv_layout_footprint_bytes(layout, L, hkv, d, t) == O.layout_footprint_bytes(layout, L, hkv, d, t)
+
+
+@pytest.mark.parametrize("args,code", [
+    ((7, 1, 4, 64, 100), kvq.KV_EINVAL),       # layout
+    ((2, 0, 4, 64, 100), kvq.KV_EINVAL),       # n_layers
+    ((2, 1, 0, 64, 100), kvq.KV_EINVAL),       # n_kv_heads
+    ((2, 1, 4, 48, 100), kvq.KV_EINVAL),       # head_dim % 32
+    ((2, 1, 4, 64, 0), kvq.KV_EINVAL),         # max_tokens
+    ((2, 1, 4, 64, 1 << 31), kvq.KV_EINVAL),
+    ((2, 1, 4, 96, 100), kvq.KV_EUNSUPPORTED), # valid but not built
+])
+def test_create_rejects_bad_shapes(args, code):
+    with pytest.raises(kvq.KVError) as e:
+        kvq.kv_cache_create(*args)
+    assert e.value.code == code
+    assert kvq.kv_last_status() == code and kvq.kv_last_error()
+
+
+def test_forced_allocation_failure(monkeypatch):
+    monkeypatch.setenv("KVQ_FAULT", "alloc")
+    with pytest.raises(kvq.KVError) as e:
+        kvq.kv_cache_create("K8V4", 1, 4, 64, 100)
+    assert e.value.code == kvq.KV_ENOMEM and "KVQ_FAULT" in str(e.value)
+
+
+def test_null_handles_are_rejected(built_library):
+    L = built_library
+    assert L.kv_append_quant(None, 0, None, None, 0, 1, None) == kvq.KV_EINVAL
+    assert L.kv_attend_decode(None, 1, 0, None, 0, 4, 0.1, None, None, 0, None) == kvq.KV_EINVAL
+    assert L.kv_attend_chunk(None, 0, None, 0, 4, 1, 0.1, None, None, 0, None) == kvq.KV_EINVAL
+    assert L.kv_footprint_bytes(None) == kvq.KV_EINVAL
+    assert L.kv_cache_len(None, 0) == kvq.KV_EINVAL
+    assert L.kv_cache_reset(None) == kvq.KV_EINVAL
+    assert L.kv_cache_truncate(None, 0, 0) == kvq.KV_EINVAL
+    assert L.kv_decode_workspace_bytes(None, 1, 0, 4) == kvq.KV_EINVAL
+    assert L.kv_chunk_workspace_bytes(None, 0, 4, 1) == kvq.KV_EINVAL
+    p, rb = C.c_void_p(), C.c_int64()
+    assert L.kv_cache_plane(None, 0, 0, 0, C.byref(p), C.byref(rb)) == kvq.KV_EINVAL
+    assert L.kv_cache_copy_plane(None, 0, 0, 0, 0, 1, None, None) == kvq.KV_EINVAL
+    arr = (C.c_void_p * 2)(None, None)
+    assert L.kv_attend_decode(arr, 2, 0, None, 0, 4, 0.1, None, None, 0, None) == kvq.KV_EINVAL
+    assert "NULL" in kvq.kv_last_error()
+    L.kv_cache_destroy(None)   # no-op
+
+
+def test_status_is_cleared_by_a_good_call():
+    with pytest.raises(kvq.KVError):
+        kvq.kv_cache_create(9, 1, 1, 64, 1)
+    assert kvq.kv_layout_footprint_bytes(2, 1, 1, 64, 1) > 0
+    assert kvq.kv_last_status() == kvq.KV_OK and kvq.kv_last_error() == ""

@@ -1,0 +1,266 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Cache planes must match bit for bit; attention outputs within 5e-3 max abs error.
+Sizes span several kernel tiles and ragged tails; the oracle finishes in seconds.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle as O
+import asymmetric_quantized_kv_amd as kvq
+from asymmetric_quantized_kv_amd import inputs as I
+
+from gpu_util import TOL, assert_planes_equal, dev, gpu_cache, host_inputs, log, max_err, torch_mod
+
+pytestmark = pytest.mark.gpu
+
+LAYOUTS = ["FP16", "K8V8", "K8V4", "K4V8", "K4V4"]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = torch_mod()
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    kvq.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------
+# quantize-on-append
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_append_planes_bit_exact(layout, dtype, d):
+    log(f"append {layout} {dtype} D={d}")
+    hkv, n = 3, 611
+    k, v, _ = I.workload_small(40 + d, n, hkv, d, hkv, 1, bf16=(dtype == "bf16"), n_outliers=4)
+    k = np.where(np.arange(n)[:, None, None] % 97 == 5, 0.0, k).astype(np.float32)     # zero blocks
+    k = np.where(np.arange(n)[:, None, None] % 89 == 7, k * 1e-30, k).astype(np.float32)  # scale underflow
+    oc = O.OracleCache(O.LAYOUT_IDS[layout], 2, hkv, d, n)
+    with gpu_cache(layout, 2, hkv, d, n) as h:
+        for a, b in ((0, 1), (1, 38), (38, 300), (300, n)):
+            kvq.kv_append_quant(h, 1, dev(k[a:b], dtype), dev(v[a:b], dtype))
+            oc.append(1, host_inputs(k[a:b], dtype), host_inputs(v[a:b], dtype))
+        assert kvq.kv_cache_len(h, 1) == n and kvq.kv_cache_len(h, 0) == 0
+        assert kvq.kv_footprint_bytes(h) == oc.footprint_bytes()
+        assert_planes_equal(h, oc, 1)
+
+
+def _golden_rows():
+    rows = []
+    from test_oracle import _codec_cases
+    for _, bits, _, xs, _ in _codec_cases():
+        r = np.zeros(64, np.float32)
+        r[:len(xs)] = xs
+        r[32:32 + len(xs)] = [-x for x in xs]
+        rows.append(r)
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("layout", ["K8V8", "K8V4", "K4V4"])
+def test_append_codec_edge_cases(layout):
+    rows = _golden_rows()
+    k = rows[:, None, :]
+    v = (rows[:, None, :] / np.float32(4.0)).astype(np.float32)
+    oc = O.OracleCache(O.LAYOUT_IDS[layout], 1, 1, 64, len(rows))
+    oc.append(0, k, v)
+    with gpu_cache(layout, 1, 1, 64, len(rows)) as h:
+        kvq.kv_append_quant(h, 0, dev(k, "f32"), dev(v, "f32"))
+        assert_planes_equal(h, oc, 0)
+
+
+# ---------------------------------------------------------------------------
+# decode
+# ---------------------------------------------------------------------------
+DECODE_CASES = [
+    # layout, D, group, dtype, session lengths
+    ("K8V4", 64, 8, "f32", [128]),
+    ("K8V4", 128, 4, "bf16", [1, 129, 700, 2500]),
+    ("K4V8", 128, 4, "bf16", [300, 1, 4097]),
+    ("K8V8", 64, 8, "f32", [513, 2048]),
+    ("K4V4", 64, 8, "f16", [77, 1000]),
+    ("FP16", 128, 4, "bf16", [640, 3]),
+    ("FP16", 64, 8, "f32", [1500]),
+    ("K8V4", 128, 1, "bf16", [900, 200]),
+    ("K8V4", 128, 2, "f32", [1025]),
+    ("K4V8", 64, 3, "f32", [333, 700]),
+    ("K8V8", 128, 5, "bf16", [1200]),
+    ("K4V4", 128, 8, "bf16", [2000, 31]),
+    ("K8V4", 64, 16, "f32", [600]),
+    ("K4V8", 128, 16, "bf16", [257]),
+    ("FP16", 64, 2, "f16", [64, 5000]),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=lambda c: f"{c[0]}-D{c[1]}-G{c[2]}-{c[3]}-{len(c[4])}s")
+def test_decode_matches_oracle(case):
+    layout, d, g, dtype, lens = case
+    log(f"decode {case}")
+    hkv = 2
+    hq = hkv * g
+    lid = O.LAYOUT_IDS[layout]
+    sessions, ocs = [], []
+    q = I.normal((len(lens), hq, d), 500 + d + g, 9)
+    if dtype == "bf16":
+        q = I.bf16_round(q)
+    try:
+        for i, n in enumerate(lens):
+            k, v, _ = I.workload_small(600 + 7 * i + g, n, hkv, d, hq, 1, bf16=(dtype == "bf16"), n_outliers=4)
+            h = kvq.kv_cache_create(layout, 2, hkv, d, n + 50)
+            sessions.append(h)
+            kvq.kv_append_quant(h, 1, dev(k, dtype), dev(v, dtype))
+            oc = O.OracleCache(lid, 2, hkv, d, n + 50)
+            oc.append(1, host_inputs(k, dtype), host_inputs(v, dtype))
+            ocs.append(oc)
+        scale = d ** -0.5
+        out = kvq.kv_attend_decode(sessions, 1, dev(q, dtype), scale)
+        want = O.attend_decode(ocs, 1, host_inputs(q, dtype), scale)
+        err = max_err(out, want)
+        log(f"  max err {err:.3e}")
+        assert err <= TOL
+    finally:
+        torch_mod().cuda.synchronize()
+        for h in sessions:
+            kvq.kv_cache_destroy(h)
+
+
+def test_decode_more_sessions_than_one_launch():
+    log("decode 70 sessions")
+    d, hkv, g, n_s = 64, 1, 4, 70
+    sessions, ocs = [], []
+    q = I.normal((n_s, hkv * g, d), 77)
+    try:
+        for i in range(n_s):
+            n = 1 + (i * 37) % 300
+            k, v, _ = I.workload_small(700 + i, n, hkv, d, hkv * g, 1)
+            h = kvq.kv_cache_create("K8V4", 1, hkv, d, 400)
+            kvq.kv_append_quant(h, 0, dev(k, "f32"), dev(v, "f32"))
+            oc = O.OracleCache(2, 1, hkv, d, 400)
+            oc.append(0, k, v)
+            sessions.append(h)
+            ocs.append(oc)
+        out = kvq.kv_attend_decode(sessions, 0, dev(q, "f32"), 0.125)
+        assert max_err(out, O.attend_decode(ocs, 0, q, 0.125)) <= TOL
+    finally:
+        torch_mod().cuda.synchronize()
+        for h in sessions:
+            kvq.kv_cache_destroy(h)
+
+
+def test_config1_exact_workload():
+    log("config 1")
+    c = I.config1()
+    oc = O.OracleCache(2, 1, 4, 64, 128)
+    oc.append(0, c["k"], c["v"])
+    with gpu_cache("K8V4", 1, 4, 64, 128) as h:
+        kvq.kv_append_quant(h, 0, dev(c["k"], "f32"), dev(c["v"], "f32"))
+        assert_planes_equal(h, oc, 0)
+        out = kvq.kv_attend_decode([h], 0, dev(c["q"], "f32"), 64 ** -0.5)
+        err = max_err(out, O.attend_decode([oc], 0, c["q"], 64 ** -0.5))
+        log(f"  config 1 max err {err:.3e}")
+        assert tuple(out.shape) == (1, 32, 64) and err <= TOL
+
+
+# ---------------------------------------------------------------------------
+# chunk prefill
+# ---------------------------------------------------------------------------
+CHUNK_CASES = [
+    # layout, D, group, dtype, cached before the turn, new tokens
+    ("K8V4", 128, 8, "bf16", 0, 1),
+    ("K8V4", 128, 8, "bf16", 700, 37),
+    ("K8V4", 128, 8, "bf16", 3000, 200),
+    ("K4V8", 128, 5, "bf16", 1500, 64),
+    ("K8V8", 64, 4, "f32", 100, 300),
+    ("K4V4", 64, 1, "f16", 2100, 129),
+    ("FP16", 128, 4, "bf16", 50, 50),
+    ("FP16", 64, 8, "f32", 4000, 16),
+    ("K8V4", 64, 2, "f32", 0, 700),
+    ("K4V8", 128, 16, "bf16", 333, 3),
+]
+
+
+@pytest.mark.parametrize("case", CHUNK_CASES, ids=lambda c: f"{c[0]}-D{c[1]}-G{c[2]}-{c[3]}-{c[4]}+{c[5]}")
+def test_chunk_matches_oracle(case):
+    layout, d, g, dtype, n_ctx, n_new = case
+    log(f"chunk {case}")
+    hkv = 2
+    hq = hkv * g
+    n = n_ctx + n_new
+    k, v, q = I.workload_small(900 + g + d, n, hkv, d, hq, n_new, bf16=(dtype == "bf16"), n_outliers=4)
+    oc = O.OracleCache(O.LAYOUT_IDS[layout], 1, hkv, d, n)
+    with gpu_cache(layout, 1, hkv, d, n) as h:
+        if n_ctx:
+            kvq.kv_append_quant(h, 0, dev(k[:n_ctx], dtype), dev(v[:n_ctx], dtype))
+            oc.append(0, host_inputs(k[:n_ctx], dtype), host_inputs(v[:n_ctx], dtype))
+        kvq.kv_append_quant(h, 0, dev(k[n_ctx:], dtype), dev(v[n_ctx:], dtype))
+        oc.append(0, host_inputs(k[n_ctx:], dtype), host_inputs(v[n_ctx:], dtype))
+        scale = d ** -0.5
+        out = kvq.kv_attend_chunk(h, 0, dev(q, dtype), n_new, scale)
+        want = O.attend_chunk(oc, 0, host_inputs(q, dtype), n_new, scale)
+        err = max_err(out, want)
+        log(f"  max err {err:.3e}")
+        assert err <= TOL
+
+
+# ---------------------------------------------------------------------------
+# determinism and device-side error paths
+# ---------------------------------------------------------------------------
+def test_outputs_are_run_to_run_deterministic():
+    torch = torch_mod()
+    k, v, q = I.workload_small(950, 3000, 2, 128, 8, 100, bf16=True, n_outliers=4)
+    with gpu_cache("K8V4", 1, 2, 128, 3000) as h:
+        kvq.kv_append_quant(h, 0, dev(k, "bf16"), dev(v, "bf16"))
+        qd = dev(q[-1:], "bf16")
+        a = kvq.kv_attend_decode([h], 0, qd, 0.088)
+        b = kvq.kv_attend_decode([h], 0, qd, 0.088)
+        assert torch.equal(a, b)
+        qc = dev(q, "bf16")
+        c1 = kvq.kv_attend_chunk(h, 0, qc, 100, 0.088)
+        c2 = kvq.kv_attend_chunk(h, 0, qc, 100, 0.088)
+        assert torch.equal(c1, c2)
+
+
+def test_device_error_paths():
+    torch = torch_mod()
+    with gpu_cache("K8V4", 1, 2, 64, 100) as h, gpu_cache("K4V8", 1, 2, 64, 100) as other:
+        q = torch.zeros((1, 4, 64), dtype=torch.float32, device="cuda")
+        with pytest.raises(kvq.KVError) as e:
+            kvq.kv_attend_decode([h], 0, q, 0.1)
+        assert e.value.code == kvq.KV_EEMPTY
+        with pytest.raises(kvq.KVError) as e:
+            kvq.kv_attend_chunk(h, 0, q, 1, 0.1)
+        assert e.value.code == kvq.KV_EEMPTY
+        x = torch.zeros((101, 2, 64), dtype=torch.float32, device="cuda")
+        with pytest.raises(kvq.KVError) as e:
+            kvq.kv_append_quant(h, 0, x, x)
+        assert e.value.code == kvq.KV_ECAPACITY and kvq.kv_cache_len(h, 0) == 0
+        kvq.kv_append_quant(h, 0, x[:10], x[:10])
+        kvq.kv_append_quant(other, 0, x[:10], x[:10])
+        with pytest.raises(kvq.KVError) as e:
+            kvq.kv_attend_decode([h, other], 0, torch.zeros((2, 4, 64), device="cuda"), 0.1)
+        assert e.value.code == kvq.KV_EINVAL
+        with pytest.raises(kvq.KVError) as e:
+            kvq.kv_attend_chunk(h, 0, torch.zeros((11, 4, 64), device="cuda"), 11, 0.1)
+        assert e.value.code == kvq.KV_EINVAL
+        with pytest.raises(kvq.KVError) as e:
+            kvq.kv_attend_decode([h], 0, torch.zeros((1, 3, 64), device="cuda"), 0.1)
+        assert e.value.code == kvq.KV_EINVAL
+        with pytest.raises(kvq.KVError) as e:
+            kvq.kv_append_quant(h, 1, x[:1], x[:1])
+        assert e.value.code == kvq.KV_EINVAL
+        raw = torch.zeros(4 * 64 + 1, dtype=torch.float32, device="cuda")[1:].view(1, 4, 64)
+        with pytest.raises(kvq.KVError) as e:
+            kvq.kv_attend_decode([h], 0, raw, 0.1)
+        assert e.value.code == kvq.KV_EINVAL and "aligned" in str(e.value)
+        with pytest.raises(kvq.KVError) as e:
+            kvq.kv_cache_truncate(h, 0, 11)
+        assert e.value.code == kvq.KV_EINVAL
+        kvq.kv_cache_truncate(h, 0, 4)
+        assert kvq.kv_cache_len(h, 0) == 4
+        kvq.kv_cache_reset(h)
+        assert kvq.kv_cache_len(h, 0) == 0
