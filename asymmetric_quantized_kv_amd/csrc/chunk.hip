@@ -6,26 +6,54 @@
 // token-major, so a tile of rows spans few positions and the causal edge stays narrow.
 //
 // Q.K^T and P.V are dense contractions and run on the matrix cores
-// (v_mfma_f32_32x32x16_f16).  Operands are fp16 rather than bf16: codes times an fp16
-// scale need more than bf16's 8 significant bits (a 1-key attention would return the
+// (v_mfma_f32_32x32x16_f16).  Operands are fp16 rather than bf16: a code times an fp16
+// scale needs more than bf16's 8 significant bits (a 1-key attention would return the
 // value with a 2^-9 relative error), while fp16 keeps 11 bits at the same MFMA rate.
+// Quantized keys are carried as fp16 hi + lo (code * scale = hi + lo exactly), so scores
+// are exact up to fp32 accumulation; fp32 queries are likewise carried as hi + lo.
 //
 // A workgroup (4 waves) owns 128 rows of one KV head and one split of the context.
-// Per 64-key tile: the workgroup dequantizes K into LDS as [key][d] and V as [d][key];
-// each wave computes S^T = K Q^T (lane = query row, 16 keys per 32-key block), keeps an
-// online softmax per row, and accumulates O^T += V^T P^T.  The P operand is taken in
-// the key order the S^T accumulator already has, and V^T is read in that same order,
-// so no register shuffle is needed between the two contractions.
+// Per 64-key tile: the workgroup dequantizes K into LDS as [key][d] and V as [d][key]
+// (packed fp16 arithmetic on magic-number conversions of the codes), while the raw
+// codes of the next tile are already in flight; each wave computes S^T = K Q^T (lane =
+// query row, 16 keys per 32-key block), keeps an online softmax per row, and accumulates
+// O^T += V^T P^T.  P is used in the key order the S^T accumulator already has and V^T is
+// read in that same order, so no register shuffle sits between the two contractions.
+// The running max only moves when a row's tile max exceeds it by more than 2^8
+// (probabilities up to 256 stay exact in fp16), which makes the rescale of the
+// accumulators rare.
 #include "kvq_internal.h"
+
+#ifndef KVQ_CHUNK_KSPLIT
+#define KVQ_CHUNK_KSPLIT 1
+#endif
 
 namespace kvq {
 namespace {
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float float16_t __attribute__((ext_vector_type(16)));
 
+constexpr float kLazyMax = 8.f;   // log2 headroom before the running max is moved
+
+__device__ __forceinline__ half2_t h2(uint32_t x) { return __builtin_bit_cast(half2_t, x); }
+__device__ __forceinline__ uint32_t u32(half2_t x) { return __builtin_bit_cast(uint32_t, x); }
 __device__ __forceinline__ float h2f(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
+__device__ __forceinline__ half2_t hconst(float a) {
+  half2_t r;
+  r.x = (_Float16)a;
+  r.y = (_Float16)a;
+  return r;
+}
+__device__ __forceinline__ half2_t splat(uint16_t b) {
+  const _Float16 h = __builtin_bit_cast(_Float16, b);
+  half2_t r;
+  r.x = h;
+  r.y = h;
+  return r;
+}
 
 __device__ __forceinline__ float q_at(const void* q, int dt, int64_t i) {
   if (dt == 0) return static_cast<const float*>(q)[i];
@@ -34,44 +62,59 @@ __device__ __forceinline__ float q_at(const void* q, int dt, int64_t i) {
   return h2f(b);
 }
 
-// Dequantize 8 consecutive elements whose codes start at byte `p` (fp16: values).
-template <int BITS>
-__device__ __forceinline__ void dequant8(const uint8_t* p, float d, _Float16 (&o)[8]) {
-  if constexpr (BITS == 16) {
-    const uint4 v = *reinterpret_cast<const uint4*>(p);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+template <int W>
+__device__ __forceinline__ void load_dw(const uint8_t* p, uint32_t* o) {
+  if constexpr (W % 4 == 0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      o[2 * i] = __builtin_bit_cast(_Float16, (uint16_t)(w[i] & 0xffffu));
-      o[2 * i + 1] = __builtin_bit_cast(_Float16, (uint16_t)(w[i] >> 16));
+    for (int i = 0; i < W / 4; ++i) {
+      const uint4 t = reinterpret_cast<const uint4*>(p)[i];
+      o[4 * i] = t.x; o[4 * i + 1] = t.y; o[4 * i + 2] = t.z; o[4 * i + 3] = t.w;
     }
-  } else if constexpr (BITS == 8) {
-    const uint2 v = *reinterpret_cast<const uint2*>(p);
-    const uint32_t w[2] = {v.x, v.y};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int c = (int)(int8_t)((w[i >> 2] >> (8 * (i & 3))) & 0xff);
-      o[i] = (_Float16)((float)c * d);   // exact product, one rounding to fp16
-    }
+  } else if constexpr (W == 2) {
+    const uint2 t = *reinterpret_cast<const uint2*>(p);
+    o[0] = t.x; o[1] = t.y;
   } else {
-    const uint32_t w = *reinterpret_cast<const uint32_t*>(p);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int c = (int)((w >> (4 * i)) & 0xf) - 8;
-      o[i] = (_Float16)((float)c * d);
-    }
+    o[0] = *reinterpret_cast<const uint32_t*>(p);
   }
 }
 
-template <int KB, int VB, int D, bool QSPLIT>
+// fp16 magic numbers: 0x64xx reads as 1024 + xx when xx < 4 bits of exponent room, so
+// a code placed in the low mantissa bits comes back exactly after one packed subtract.
+constexpr uint32_t kMagic = 0x64646464u;
+constexpr uint32_t kHalfBias1024 = 0x64006400u;
+
+// the 4 codes of one dword of 8-bit keys as fp16 pairs (e0, e1), (e2, e3)
+__device__ __forceinline__ void k8_pairs(uint32_t w, half2_t (&c)[2]) {
+  const uint32_t x = w ^ 0x80808080u;                                            // c + 128
+  c[0] = h2(__builtin_amdgcn_perm(kMagic, x, 0x04010400u)) - hconst(1152.f);
+  c[1] = h2(__builtin_amdgcn_perm(kMagic, x, 0x04030402u)) - hconst(1152.f);
+}
+
+// the 8 codes of one dword of 4-bit keys as fp16 pairs (e2j, e2j+1), j = 0..3
+__device__ __forceinline__ void k4_pairs(uint32_t w, half2_t (&c)[4]) {
+  const uint32_t w4 = w >> 4;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t sel = (uint32_t)j | ((uint32_t)(4 + j) << 16) | 0x0c000c00u;  // [w.bj, 0, w4.bj, 0]
+    const uint32_t p = __builtin_amdgcn_perm(w4, w, sel);
+    c[j] = h2((p & 0x000F000Fu) | kHalfBias1024) - hconst(1032.f);
+  }
+}
+
+template <int KB, int VB, int D, bool QSPLIT, bool KSPLIT_>
 __global__ __launch_bounds__(256, 2) void chunk_kernel(ChunkArgs a) {
+  constexpr bool KSPLIT = KSPLIT_ && KB != 16;   // fp16 keys are exact already
   constexpr int NK = kChunkKeys;   // keys per tile
   constexpr int KSTR = D + 8;      // halves per LDS key row
   constexpr int VSTR = NK + 8;     // halves per LDS transposed-value row
   constexpr int NDT = D / 32;      // 32-wide output blocks along d
   constexpr int NKS = D / 16;      // k-steps of Q.K^T
-  constexpr int KSEG = D / 8;      // 8-element segments per key row
+  constexpr int KE = D / 4;        // key elements one thread dequantizes (4 threads per key)
+  constexpr int KW = KE * KB / 32; // their dwords
+  constexpr int VW = VB / 4;       // dwords of 8 value elements of one key
+  constexpr int VITEMS = (NK / 4) * (D / 8);  // (4 keys x 8 d) value items per tile
   __shared__ __attribute__((aligned(16))) _Float16 s_k[NK * KSTR];
+  __shared__ __attribute__((aligned(16))) _Float16 s_kl[KSPLIT ? NK * KSTR : 8];
   __shared__ __attribute__((aligned(16))) _Float16 s_vt[D * VSTR];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -94,7 +137,6 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(ChunkArgs a) {
   const uint8_t* vs = kc + a.g.off_vs();
 
   // Q^T as the B operand: lane (col, hl) holds d = 16 k + 8 hl .. + 7 of its row.
-  // bf16 and fp16 queries are exact in fp16; fp32 queries are carried as hi + lo.
   half8_t qv[NKS];
   half8_t ql[QSPLIT ? NKS : 1];
   {
@@ -117,6 +159,29 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(ChunkArgs a) {
   const int64_t wave_min_pos = base_pos + r0 / a.group;
   const bool wave_active = r0 < rows;
 
+  // this thread's share of a tile: key row tid / 4 (a quarter of it) and one value item
+  // of 4 keys x 8 elements
+  const int k_key = tid >> 2, k_part = tid & 3;
+  const int v_kg = tid & 15, v_dg = tid >> 4;
+  const bool v_on = tid < VITEMS;
+  uint32_t kraw[KW];
+  uint16_t kscale = 0;
+  uint32_t vraw[4][VW];
+  uint16_t vscale[4] = {0, 0, 0, 0};
+  auto fetch = [&](int64_t kt0) {
+    const int64_t key = kt0 + k_key;
+    load_dw<KW>(kc + key * a.g.kc + k_part * (KW * 4), kraw);
+    if constexpr (KB != 16) kscale = *reinterpret_cast<const uint16_t*>(ks + key * a.g.ks + 2 * ((k_part * KE) / kBlock));
+    if (v_on) {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int64_t vk = kt0 + 4 * v_kg + kk;
+        load_dw<VW>(vc + vk * a.g.vc + v_dg * VB, vraw[kk]);
+        if constexpr (VB != 16) vscale[kk] = *reinterpret_cast<const uint16_t*>(vs + vk * a.g.vs + 2 * (v_dg >> 2));
+      }
+    }
+  };
+
   float m = -INFINITY, l = 0.f;
   float16_t o[NDT];
 #pragma unroll
@@ -124,39 +189,94 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(ChunkArgs a) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) o[t][v] = 0.f;
 
+  if (k_lo < k_end) fetch(k_lo);
   for (int64_t kt0 = k_lo; kt0 < k_end; kt0 += NK) {
-    // ---- K tile -> LDS [key][d] -------------------------------------------------
-    for (int it = tid; it < NK * KSEG; it += 256) {
-      const int t = it / KSEG, sg = it % KSEG;
-      const int64_t key = kt0 + t;
-      float d = 1.f;
-      if constexpr (KB != 16) d = h2f(*reinterpret_cast<const uint16_t*>(ks + key * a.g.ks + 2 * (sg >> 2)));
-      _Float16 v[8];
-      dequant8<KB>(kc + key * a.g.kc + sg * KB, d, v);
-      half8_t h;
+    // ---- dequantize the fetched tile into LDS -------------------------------------
+    {
+      half2_t hi[KE / 2], lo[KE / 2];
+      if constexpr (KB == 16) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) h[i] = v[i];
-      *reinterpret_cast<half8_t*>(&s_k[t * KSTR + 8 * sg]) = h;
+        for (int i = 0; i < KE / 2; ++i) hi[i] = h2(kraw[i]);
+      } else {
+        const half2_t d2 = splat(kscale);
+#pragma unroll
+        for (int w = 0; w < KW; ++w) {
+          if constexpr (KB == 8) {
+            half2_t c[2];
+            k8_pairs(kraw[w], c);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+              hi[2 * w + j] = c[j] * d2;
+              if constexpr (KSPLIT) lo[2 * w + j] = __builtin_elementwise_fma(c[j], d2, -hi[2 * w + j]);
+            }
+          } else {
+            half2_t c[4];
+            k4_pairs(kraw[w], c);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              hi[4 * w + j] = c[j] * d2;
+              if constexpr (KSPLIT) lo[4 * w + j] = __builtin_elementwise_fma(c[j], d2, -hi[4 * w + j]);
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < KE / 8; ++i) {
+        const int off = k_key * KSTR + k_part * KE + 8 * i;
+        *reinterpret_cast<uint4*>(&s_k[off]) =
+            make_uint4(u32(hi[4 * i]), u32(hi[4 * i + 1]), u32(hi[4 * i + 2]), u32(hi[4 * i + 3]));
+        if constexpr (KSPLIT)
+          *reinterpret_cast<uint4*>(&s_kl[off]) =
+              make_uint4(u32(lo[4 * i]), u32(lo[4 * i + 1]), u32(lo[4 * i + 2]), u32(lo[4 * i + 3]));
+      }
     }
-    // ---- V tile -> LDS [d][key] (4 keys x 8 d per item) ---------------------------
-    for (int it = tid; it < (NK / 4) * KSEG; it += 256) {
-      const int kg = it % (NK / 4), sg = it / (NK / 4);
-      _Float16 v[4][8];
+    if (v_on) {
+      // keys (0, 1) and (2, 3) side by side per element: pr[e][pair] = (v_2p, v_2p+1)
+      uint32_t pr[8][2];
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int64_t key = kt0 + 4 * kg + kk;
-        float d = 1.f;
-        if constexpr (VB != 16) d = h2f(*reinterpret_cast<const uint16_t*>(vs + key * a.g.vs + 2 * (sg >> 2)));
-        dequant8<VB>(vc + key * a.g.vc + sg * VB, d, v[kk]);
+      for (int p = 0; p < 2; ++p) {
+        const uint32_t* wa = vraw[2 * p];
+        const uint32_t* wb = vraw[2 * p + 1];
+        half2_t d2 = hconst(1.f);
+        if constexpr (VB != 16) {
+          d2.x = __builtin_bit_cast(_Float16, vscale[2 * p]);
+          d2.y = __builtin_bit_cast(_Float16, vscale[2 * p + 1]);
+        }
+        if constexpr (VB == 4) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const uint32_t sel = (uint32_t)j | ((uint32_t)(4 + j) << 16) | 0x0c000c00u;  // [a.bj, 0, b.bj, 0]
+            const uint32_t q = __builtin_amdgcn_perm(wb[0], wa[0], sel);
+            const half2_t ce = h2((q & 0x000F000Fu) | kHalfBias1024) - hconst(1032.f);
+            const half2_t co = h2(((q >> 4) & 0x000F000Fu) | kHalfBias1024) - hconst(1032.f);
+            pr[2 * j][p] = u32(ce * d2);
+            pr[2 * j + 1][p] = u32(co * d2);
+          }
+        } else if constexpr (VB == 8) {
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            const uint32_t xa = wa[i] ^ 0x80808080u, xb = wb[i] ^ 0x80808080u;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const uint32_t sel = (uint32_t)j | ((uint32_t)(4 + j) << 16) | 0x0c000c00u;
+              const uint32_t q = __builtin_amdgcn_perm(xb, xa, sel) | kHalfBias1024;
+              pr[4 * i + j][p] = u32((h2(q) - hconst(1152.f)) * d2);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            pr[2 * i][p] = __builtin_amdgcn_perm(wb[i], wa[i], 0x05040100u);
+            pr[2 * i + 1][p] = __builtin_amdgcn_perm(wb[i], wa[i], 0x07060302u);
+          }
+        }
       }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        half4_t h;
-        h[0] = v[0][e]; h[1] = v[1][e]; h[2] = v[2][e]; h[3] = v[3][e];
-        *reinterpret_cast<half4_t*>(&s_vt[(8 * sg + e) * VSTR + 4 * kg]) = h;
-      }
+      for (int e = 0; e < 8; ++e)
+        *reinterpret_cast<uint2*>(&s_vt[(8 * v_dg + e) * VSTR + 4 * v_kg]) = make_uint2(pr[e][0], pr[e][1]);
     }
     __syncthreads();
+    if (kt0 + NK < k_end) fetch(kt0 + NK);   // the next tile's codes fly during the math below
 
     if (wave_active) {
       // ---- S^T = K Q^T --------------------------------------------------------------
@@ -167,8 +287,13 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(ChunkArgs a) {
         for (int v = 0; v < 16; ++v) s[st][v] = 0.f;
 #pragma unroll
         for (int k = 0; k < NKS; ++k) {
-          const half8_t ak = *reinterpret_cast<const half8_t*>(&s_k[(32 * st + col) * KSTR + 16 * k + 8 * hl]);
+          const int off = (32 * st + col) * KSTR + 16 * k + 8 * hl;
+          const half8_t ak = *reinterpret_cast<const half8_t*>(&s_k[off]);
           s[st] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ak, qv[k], s[st], 0, 0, 0);
+          if constexpr (KSPLIT) {
+            const half8_t al = *reinterpret_cast<const half8_t*>(&s_kl[off]);
+            s[st] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, qv[k], s[st], 0, 0, 0);
+          }
           if constexpr (QSPLIT) s[st] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ak, ql[k], s[st], 0, 0, 0);
         }
       }
@@ -188,39 +313,42 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(ChunkArgs a) {
       for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[st][v]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mn = fmaxf(m, mx * a.qk_scale);
-      const float mu = mn == -INFINITY ? 0.f : mn;
-      const float alpha = __builtin_amdgcn_exp2f(m - mu);
-      float ps = 0.f;
-      half8_t pb[4];
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[st][v], a.qk_scale, -mu));
-          ps += p;
-          pb[2 * st + (v >> 3)][v & 7] = (_Float16)p;
-        }
-      l = l * alpha + ps;
-      m = mn;
-      if (__any(alpha != 1.f)) {
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.qk_scale;
+      const bool move = mx > m + kLazyMax;
+      if (__any(move)) {
+        const float mn = move ? mx : m;
+        const float alpha = __builtin_amdgcn_exp2f(m - (mn == -INFINITY ? 0.f : mn));
+        l *= alpha;
 #pragma unroll
         for (int t = 0; t < NDT; ++t)
 #pragma unroll
           for (int v = 0; v < 16; ++v) o[t][v] *= alpha;
+        m = mn;
       }
+      const float mu = m == -INFINITY ? 0.f : m;
+      half8_t pb[4];
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int v = 0; v < 16; v += 2) {
+          half2_t pp;
+          pp.x = (_Float16)__builtin_amdgcn_exp2f(fmaf(s[st][v], a.qk_scale, -mu));
+          pp.y = (_Float16)__builtin_amdgcn_exp2f(fmaf(s[st][v + 1], a.qk_scale, -mu));
+          l = __builtin_amdgcn_fdot2(pp, hconst(1.f), l, false);   // sum of the rounded weights
+          pb[2 * st + (v >> 3)][v & 7] = pp.x;
+          pb[2 * st + (v >> 3)][(v & 7) + 1] = pp.y;
+        }
       // ---- O^T += V^T P^T ---------------------------------------------------------------
 #pragma unroll
       for (int t = 0; t < NDT; ++t) {
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
           const _Float16* vp = &s_vt[(32 * t + col) * VSTR + 32 * (kk >> 1) + 16 * (kk & 1) + 4 * hl];
-          const half4_t lo = *reinterpret_cast<const half4_t*>(vp);
-          const half4_t hi = *reinterpret_cast<const half4_t*>(vp + 8);
+          const half4_t lo4 = *reinterpret_cast<const half4_t*>(vp);
+          const half4_t hi4 = *reinterpret_cast<const half4_t*>(vp + 8);
           half8_t av;
-          av[0] = lo[0]; av[1] = lo[1]; av[2] = lo[2]; av[3] = lo[3];
-          av[4] = hi[0]; av[5] = hi[1]; av[6] = hi[2]; av[7] = hi[3];
+          av[0] = lo4[0]; av[1] = lo4[1]; av[2] = lo4[2]; av[3] = lo4[3];
+          av[4] = hi4[0]; av[5] = hi4[1]; av[6] = hi4[2]; av[7] = hi4[3];
           o[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, pb[kk], o[t], 0, 0, 0);
         }
       }
@@ -259,15 +387,20 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(ChunkArgs a) {
   }
 }
 
+template <int KB, int VB, int D, bool QSPLIT>
+const void* kernel_ptr() {
+  return reinterpret_cast<const void*>(&chunk_kernel<KB, VB, D, QSPLIT, KVQ_CHUNK_KSPLIT != 0>);
+}
+
 template <int KB, int VB, int D>
 hipError_t launch_t(const ChunkArgs& a, hipStream_t s) {
   const int64_t rows = a.n_new * a.group;
   const int64_t mt = (rows + kChunkRows - 1) / kChunkRows;
   dim3 grid((unsigned)mt, a.hkv, a.n_splits);
   if (a.q_dtype == 0)
-    hipLaunchKernelGGL((chunk_kernel<KB, VB, D, true>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((chunk_kernel<KB, VB, D, true, KVQ_CHUNK_KSPLIT != 0>), grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((chunk_kernel<KB, VB, D, false>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((chunk_kernel<KB, VB, D, false, KVQ_CHUNK_KSPLIT != 0>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -276,6 +409,12 @@ hipError_t launch_d(const ChunkArgs& a, int d, hipStream_t s) {
   if (d == 64) return launch_t<KB, VB, 64>(a, s);
   if (d == 128) return launch_t<KB, VB, 128>(a, s);
   return hipErrorInvalidValue;
+}
+
+template <int KB, int VB>
+const void* ptr_d(int d, bool q_fp32) {
+  if (d == 64) return q_fp32 ? kernel_ptr<KB, VB, 64, true>() : kernel_ptr<KB, VB, 64, false>();
+  return q_fp32 ? kernel_ptr<KB, VB, 128, true>() : kernel_ptr<KB, VB, 128, false>();
 }
 
 }  // namespace
@@ -287,6 +426,14 @@ hipError_t launch_chunk(const ChunkArgs& a, int kbits, int vbits, int d, hipStre
   if (kbits == 4 && vbits == 8) return launch_d<4, 8>(a, d, s);
   if (kbits == 4 && vbits == 4) return launch_d<4, 4>(a, d, s);
   return hipErrorInvalidValue;
+}
+
+const void* chunk_kernel_for(int kbits, int vbits, int d, bool q_fp32) {
+  if (kbits == 16) return ptr_d<16, 16>(d, q_fp32);
+  if (kbits == 8 && vbits == 8) return ptr_d<8, 8>(d, q_fp32);
+  if (kbits == 8) return ptr_d<8, 4>(d, q_fp32);
+  if (vbits == 8) return ptr_d<4, 8>(d, q_fp32);
+  return ptr_d<4, 4>(d, q_fp32);
 }
 
 }  // namespace kvq

@@ -177,21 +177,42 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     for (int e = 0; e < E; ++e) acc[g][e] = 0.f;
   }
 
+  const uint32_t koff = grp * a.kc + sub * (KW * 4), ksoff = grp * a.ks + blk * 2;
+  const uint32_t voff = grp * a.vc + sub * (VW * 4), vsoff = grp * a.vs + blk * 2;
   const int64_t n_chunks = te > ts ? (te - ts + CT - 1) / CT : 0;
-  for (int64_t c = wave; c < n_chunks; c += 4) {
+  for (int64_t c = __builtin_amdgcn_readfirstlane(wave); c < n_chunks; c += 4) {
     const int64_t c0 = ts + c * CT;
-    // ---- phase A: scores ------------------------------------------------------
+    // wave-uniform chunk bases; per-lane offsets inside a chunk fit 32 bits
+    const uint8_t* kcc = kc + c0 * a.kc;
+    const uint8_t* ksc = ks + c0 * a.ks;
+    const uint8_t* vcc = vc + c0 * a.vc;
+    const uint8_t* vsc = vs + c0 * a.vs;
+    const bool tail = c0 + CT > te;
+    // ---- phase A: scores (codes of step s + 1 in flight while step s computes) ----
+    uint32_t kbuf[2][2][KW];
+    uint16_t kscl[2][2] = {{0, 0}, {0, 0}};
+    // address = uniform base (chunk, step, token half) + one loop-invariant lane offset
+    auto load_k = [&](int s, int slot) {
+      const uint8_t* c0p = kcc + (int64_t)(s * STEP) * a.kc;
+      load_dwords<KW>(c0p + koff, kbuf[slot][0]);
+      load_dwords<KW>(c0p + (int64_t)TPS * a.kc + koff, kbuf[slot][1]);
+      if constexpr (KB != 16) {
+        const uint8_t* s0p = ksc + (int64_t)(s * STEP) * a.ks;
+        kscl[slot][0] = *reinterpret_cast<const uint16_t*>(s0p + ksoff);
+        kscl[slot][1] = *reinterpret_cast<const uint16_t*>(s0p + (int64_t)TPS * a.ks + ksoff);
+      }
+    };
+    load_k(0, 0);
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       const int la = s * STEP + grp, lb = la + TPS;
-      const int64_t ta = c0 + la, tb = c0 + lb;
-      uint32_t ka[KW], kb[KW];
-      load_dwords<KW>(kc + ta * a.kc + sub * (KW * 4), ka);
-      load_dwords<KW>(kc + tb * a.kc + sub * (KW * 4), kb);
+      if (s + 1 < NS) load_k(s + 1, (s + 1) & 1);
+      const uint32_t* ka = kbuf[s & 1][0];
+      const uint32_t* kb = kbuf[s & 1][1];
       float da = 1.f, db = 1.f;
       if constexpr (KB != 16) {
-        da = h2f(*reinterpret_cast<const uint16_t*>(ks + ta * a.ks + blk * 2));
-        db = h2f(*reinterpret_cast<const uint16_t*>(ks + tb * a.ks + blk * 2));
+        da = h2f(kscl[s & 1][0]);
+        db = h2f(kscl[s & 1][1]);
       }
       float pa[GP], pb[GP];
 #pragma unroll
@@ -206,32 +227,47 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
           pa[g] = xa * qsc[g];
           pb[g] = xb * qsc[g];
         } else {
-          int ha = corr_a[g], la_ = corr_b[g], hb = corr_a[g], lb_ = corr_b[g];
+          // one chain per token: high digit, times 256, then the low digit
+          int ha = corr_a[g], hb = corr_a[g];
           if constexpr (KB == 8) {
 #pragma unroll
             for (int j = 0; j < KW; ++j) {
               ha = __builtin_amdgcn_sdot4((int)ka[j], (int)qa_r[g][j], ha, false);
-              la_ = __builtin_amdgcn_sdot4((int)ka[j], (int)qb_r[g][j], la_, false);
               hb = __builtin_amdgcn_sdot4((int)kb[j], (int)qa_r[g][j], hb, false);
-              lb_ = __builtin_amdgcn_sdot4((int)kb[j], (int)qb_r[g][j], lb_, false);
             }
-          } else {
+            ha = (ha << 8) + corr_b[g];
+            hb = (hb << 8) + corr_b[g];
 #pragma unroll
             for (int j = 0; j < KW; ++j) {
-              const uint32_t ae = ka[j] & 0x0F0F0F0Fu, ao = (ka[j] >> 4) & 0x0F0F0F0Fu;
-              const uint32_t be = kb[j] & 0x0F0F0F0Fu, bo = (kb[j] >> 4) & 0x0F0F0F0Fu;
-              ha = __builtin_amdgcn_sdot4((int)ae, (int)qa_r[g][2 * j], ha, false);
-              ha = __builtin_amdgcn_sdot4((int)ao, (int)qa_r[g][2 * j + 1], ha, false);
-              la_ = __builtin_amdgcn_sdot4((int)ae, (int)qb_r[g][2 * j], la_, false);
-              la_ = __builtin_amdgcn_sdot4((int)ao, (int)qb_r[g][2 * j + 1], la_, false);
-              hb = __builtin_amdgcn_sdot4((int)be, (int)qa_r[g][2 * j], hb, false);
-              hb = __builtin_amdgcn_sdot4((int)bo, (int)qa_r[g][2 * j + 1], hb, false);
-              lb_ = __builtin_amdgcn_sdot4((int)be, (int)qb_r[g][2 * j], lb_, false);
-              lb_ = __builtin_amdgcn_sdot4((int)bo, (int)qb_r[g][2 * j + 1], lb_, false);
+              ha = __builtin_amdgcn_sdot4((int)ka[j], (int)qb_r[g][j], ha, false);
+              hb = __builtin_amdgcn_sdot4((int)kb[j], (int)qb_r[g][j], hb, false);
+            }
+          } else {
+            uint32_t ae[KW], ao[KW], be[KW], bo[KW];
+#pragma unroll
+            for (int j = 0; j < KW; ++j) {
+              ae[j] = ka[j] & 0x0F0F0F0Fu; ao[j] = (ka[j] >> 4) & 0x0F0F0F0Fu;
+              be[j] = kb[j] & 0x0F0F0F0Fu; bo[j] = (kb[j] >> 4) & 0x0F0F0F0Fu;
+            }
+#pragma unroll
+            for (int j = 0; j < KW; ++j) {
+              ha = __builtin_amdgcn_sdot4((int)ae[j], (int)qa_r[g][2 * j], ha, false);
+              ha = __builtin_amdgcn_sdot4((int)ao[j], (int)qa_r[g][2 * j + 1], ha, false);
+              hb = __builtin_amdgcn_sdot4((int)be[j], (int)qa_r[g][2 * j], hb, false);
+              hb = __builtin_amdgcn_sdot4((int)bo[j], (int)qa_r[g][2 * j + 1], hb, false);
+            }
+            ha = (ha << 8) + corr_b[g];
+            hb = (hb << 8) + corr_b[g];
+#pragma unroll
+            for (int j = 0; j < KW; ++j) {
+              ha = __builtin_amdgcn_sdot4((int)ae[j], (int)qb_r[g][2 * j], ha, false);
+              ha = __builtin_amdgcn_sdot4((int)ao[j], (int)qb_r[g][2 * j + 1], ha, false);
+              hb = __builtin_amdgcn_sdot4((int)be[j], (int)qb_r[g][2 * j], hb, false);
+              hb = __builtin_amdgcn_sdot4((int)bo[j], (int)qb_r[g][2 * j + 1], hb, false);
             }
           }
-          pa[g] = (float)(ha * 256 + la_) * (da * qsc[g]);
-          pb[g] = (float)(hb * 256 + lb_) * (db * qsc[g]);
+          pa[g] = (float)ha * (da * qsc[g]);
+          pb[g] = (float)hb * (db * qsc[g]);
         }
         pa[g] = group_sum<LPT>(pa[g]);
         pb[g] = group_sum<LPT>(pb[g]);
@@ -239,16 +275,35 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       if (sub == 0) {
 #pragma unroll
         for (int g = 0; g < GP; ++g) {
-          s_sc[wave][la][g] = ta < te ? pa[g] : -INFINITY;
-          s_sc[wave][lb][g] = tb < te ? pb[g] : -INFINITY;
+          s_sc[wave][la][g] = pa[g];
+          s_sc[wave][lb][g] = pb[g];
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
+    // the first value codes of the chunk fly during the softmax statistics
+    uint32_t vbuf[2][2][VW];
+    uint16_t vscl[2][2] = {{0, 0}, {0, 0}};
+    auto load_v = [&](int s, int slot) {
+      const uint8_t* c0p = vcc + (int64_t)(s * STEP) * a.vc;
+      load_dwords<VW>(c0p + voff, vbuf[slot][0]);
+      load_dwords<VW>(c0p + (int64_t)TPS * a.vc + voff, vbuf[slot][1]);
+      if constexpr (VB != 16) {
+        const uint8_t* s0p = vsc + (int64_t)(s * STEP) * a.vs;
+        vscl[slot][0] = *reinterpret_cast<const uint16_t*>(s0p + vsoff);
+        vscl[slot][1] = *reinterpret_cast<const uint16_t*>(s0p + (int64_t)TPS * a.vs + vsoff);
+      }
+    };
+    load_v(0, 0);
     wave_lds_sync();
     // ---- phase B: softmax statistics, one lane per token ------------------------
 #pragma unroll
     for (int g = 0; g < GP; ++g) {
-      const float sa = s_sc[wave][lane][g], sb = s_sc[wave][lane + 64][g];
+      float sa = s_sc[wave][lane][g], sb = s_sc[wave][lane + 64][g];
+      if (tail) {  // tokens past the cached length score -inf
+        if (c0 + lane >= te) sa = -INFINITY;
+        if (c0 + lane + 64 >= te) sb = -INFINITY;
+      }
       const float cm = wave_max(fmaxf(sa, sb));
       const float mn = fmaxf(m[g], cm);
       const float mu = mn == -INFINITY ? 0.f : mn;
@@ -265,18 +320,17 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       m[g] = mn;
     }
     wave_lds_sync();
-    // ---- phase C: values ------------------------------------------------------
+    // ---- phase C: values (codes of step s + 1 in flight while step s computes) ---
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       const int la = s * STEP + grp, lb = la + TPS;
-      const int64_t ta = c0 + la, tb = c0 + lb;
-      uint32_t va[VW], vb[VW];
-      load_dwords<VW>(vc + ta * a.vc + sub * (VW * 4), va);
-      load_dwords<VW>(vc + tb * a.vc + sub * (VW * 4), vb);
+      if (s + 1 < NS) load_v(s + 1, (s + 1) & 1);
+      const uint32_t* va = vbuf[s & 1][0];
+      const uint32_t* vb = vbuf[s & 1][1];
       float da = 1.f, db = 1.f;
       if constexpr (VB != 16) {
-        da = h2f(*reinterpret_cast<const uint16_t*>(vs + ta * a.vs + blk * 2));
-        db = h2f(*reinterpret_cast<const uint16_t*>(vs + tb * a.vs + blk * 2));
+        da = h2f(vscl[s & 1][0]);
+        db = h2f(vscl[s & 1][1]);
       }
       half2_t w[GP];
 #pragma unroll
@@ -318,6 +372,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
           }
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
     wave_lds_sync();
   }
@@ -373,9 +428,12 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   }
 }
 
+template <int GP>
+constexpr int lane_elems() { return GP <= 2 ? 32 : (GP == 4 ? 16 : 8); }
+
 template <int KB, int VB, int D, int GP>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
-  constexpr int E = GP <= 2 ? 32 : (GP == 4 ? 16 : 8);
+  constexpr int E = lane_elems<GP>();
   dim3 grid(a.n_splits, a.hkv, a.n_sess);
   hipLaunchKernelGGL((decode_kernel<KB, VB, D, GP, E>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
@@ -400,7 +458,31 @@ hipError_t launch_d(const DecodeArgs& a, int d, int gp, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
+template <int KB, int VB, int D>
+const void* ptr_g(int gp) {
+  switch (gp) {
+    case 1: return reinterpret_cast<const void*>(&decode_kernel<KB, VB, D, 1, lane_elems<1>()>);
+    case 2: return reinterpret_cast<const void*>(&decode_kernel<KB, VB, D, 2, lane_elems<2>()>);
+    case 4: return reinterpret_cast<const void*>(&decode_kernel<KB, VB, D, 4, lane_elems<4>()>);
+    case 8: return reinterpret_cast<const void*>(&decode_kernel<KB, VB, D, 8, lane_elems<8>()>);
+    default: return reinterpret_cast<const void*>(&decode_kernel<KB, VB, D, 16, lane_elems<16>()>);
+  }
+}
+
+template <int KB, int VB>
+const void* ptr_d(int d, int gp) {
+  return d == 64 ? ptr_g<KB, VB, 64>(gp) : ptr_g<KB, VB, 128>(gp);
+}
+
 }  // namespace
+
+const void* decode_kernel_for(int kbits, int vbits, int d, int gp) {
+  if (kbits == 16) return ptr_d<16, 16>(d, gp);
+  if (kbits == 8 && vbits == 8) return ptr_d<8, 8>(d, gp);
+  if (kbits == 8) return ptr_d<8, 4>(d, gp);
+  if (vbits == 8) return ptr_d<4, 8>(d, gp);
+  return ptr_d<4, 4>(d, gp);
+}
 
 hipError_t launch_decode(const DecodeArgs& a, int kbits, int vbits, int d, int gp, hipStream_t s) {
   if (kbits == 16 && vbits == 16) return launch_d<16, 16>(a, d, gp, s);

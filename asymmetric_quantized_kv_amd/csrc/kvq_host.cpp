@@ -7,6 +7,8 @@
 
 #include <algorithm>
 #include <cstdarg>
+#include <mutex>
+#include <utility>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -103,30 +105,64 @@ int decode_group_pad(int g) {
   return -1;
 }
 
-// Split plan.  The workspace bound depends only on the shapes (not on lengths),
-// so a workspace sized once keeps fitting while the caches grow.
-constexpr int64_t kDecodeTargetWgs = 2048;
-constexpr int64_t kChunkTargetWgs = 1024;
+// Split plan.  A launch is cut along the context into n splits so that its
+// workgroups fill the device in as few rounds as possible: with `base` workgroups per
+// split and `slots` resident workgroups, the time is ~ ceil(base * n / slots) rounds
+// of (tokens per split).  The workspace bound depends only on shapes and the device,
+// not on lengths, so a workspace sized once keeps fitting while the caches grow.
 constexpr int64_t kChunkMinKeysPerSplit = 1024;
+constexpr int kMaxSplitsChunk = 64;
 
-int64_t decode_split_cap(int64_t n_pairs) {
-  return std::max<int64_t>(1, ceil_div(kDecodeTargetWgs, n_pairs));
-}
-void decode_plan(int64_t n_pairs, int64_t max_len, int* n_splits, int64_t* tps) {
-  int64_t cap = decode_split_cap(n_pairs);
-  int64_t t = std::max<int64_t>(kDecodeWaveTokens, round_up(ceil_div(max_len, cap), kDecodeWaveTokens));
-  *tps = t;
-  *n_splits = (int)ceil_div(max_len, t);
+std::mutex g_plan_mu;
+
+// resident workgroups of `kernel` (256 threads) on `device`; 0 if the runtime cannot say
+int64_t resident_slots(int device, const void* kernel) {
+  static int cus[64];
+  static std::vector<std::pair<const void*, int>> per_cu;
+  std::lock_guard<std::mutex> lk(g_plan_mu);
+  if (device < 0 || device >= 64) return 0;
+  if (cus[device] == 0 && hipDeviceGetAttribute(&cus[device], hipDeviceAttributeMultiprocessorCount, device) != hipSuccess) {
+    (void)hipGetLastError();
+    cus[device] = -1;
+  }
+  if (cus[device] <= 0) return 0;
+  int n = -1;
+  for (auto& e : per_cu)
+    if (e.first == kernel) n = e.second;
+  if (n < 0) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, 256, 0) != hipSuccess) {
+      (void)hipGetLastError();
+      n = 1;
+    }
+    per_cu.emplace_back(kernel, std::max(n, 1));
+    n = std::max(n, 1);
+  }
+  return (int64_t)cus[device] * n;
 }
 
-int64_t chunk_split_cap(int64_t wgs) {
-  return std::min<int64_t>(64, std::max<int64_t>(1, ceil_div(kChunkTargetWgs, wgs)));
+int64_t split_cap(int64_t base, int64_t slots, int64_t hard_cap) {
+  if (slots <= 0) slots = 1024;
+  return std::max<int64_t>(1, std::min<int64_t>(hard_cap, ceil_div(2 * slots, base)));
 }
-void chunk_plan(int64_t wgs, int64_t len, int* n_splits, int64_t* tps) {
-  int64_t cap = chunk_split_cap(wgs);
-  int64_t t = std::max<int64_t>(kChunkMinKeysPerSplit, round_up(ceil_div(len, cap), kChunkKeys));
-  *tps = t;
-  *n_splits = (int)ceil_div(len, t);
+
+// Pick the split count; `gran` is the split granularity in tokens.
+void plan_splits(int64_t base, int64_t slots, int64_t cap, int64_t len, int64_t gran, int64_t min_tokens,
+                 int* n_splits, int64_t* tps) {
+  if (slots <= 0) slots = 1024;
+  double best = 0;
+  *n_splits = 1;
+  *tps = round_up(std::max<int64_t>(len, 1), gran);
+  for (int64_t s = 1; s <= cap; ++s) {
+    const int64_t t = std::max(round_up(min_tokens, gran), round_up(ceil_div(len, s), gran));
+    const int64_t n = ceil_div(len, t);
+    if (n != s && s > 1) continue;
+    const double cost = (double)ceil_div(base * n, slots) * (double)t;
+    if (s == 1 || cost < best * 0.98) {
+      best = cost;
+      *n_splits = (int)n;
+      *tps = t;
+    }
+  }
 }
 
 int check_sessions(kv_cache* const* sessions, int n_sessions, int layer) {
@@ -327,7 +363,11 @@ int64_t kv_decode_workspace_bytes(kv_cache* const* sessions, int n_sessions, int
   const kv_cache* s0 = sessions[0];
   if (n_q_heads < 1 || n_q_heads % s0->hkv)
     return fail(KV_EINVAL, "n_q_heads %d is not a positive multiple of n_kv_heads %d", n_q_heads, s0->hkv);
-  int64_t cap = decode_split_cap((int64_t)n_sessions * s0->hkv);
+  const int gp = decode_group_pad(n_q_heads / s0->hkv);
+  if (gp < 0) return fail(KV_EUNSUPPORTED, "decode group size %d > 16 is not built", n_q_heads / s0->hkv);
+  const int64_t base = (int64_t)n_sessions * s0->hkv;
+  const int64_t slots = resident_slots(s0->device, decode_kernel_for(s0->kbits, s0->vbits, s0->d, gp));
+  const int64_t cap = split_cap(base, slots, 1 << 20);
   if (cap <= 1) return 0;
   return (int64_t)n_sessions * n_q_heads * cap * (s0->d + 2) * (int64_t)sizeof(float);
 }
@@ -353,9 +393,12 @@ int kv_attend_decode(kv_cache* const* sessions, int n_sessions, int layer, const
     if (sessions[i]->len[layer] == 0) return fail(KV_EEMPTY, "session %d has no cached token in layer %d", i, layer);
     max_len = std::max(max_len, sessions[i]->len[layer]);
   }
+  const int64_t base = (int64_t)n_sessions * hkv;
+  const int64_t slots = resident_slots(s0->device, decode_kernel_for(s0->kbits, s0->vbits, d, gp));
   int n_splits;
   int64_t tps;
-  decode_plan((int64_t)n_sessions * hkv, max_len, &n_splits, &tps);
+  plan_splits(base, slots, split_cap(base, slots, 1 << 20), max_len, kDecodeWaveTokens, kDecodeWaveTokens,
+              &n_splits, &tps);
   int64_t need = n_splits > 1 ? (int64_t)n_sessions * n_q_heads * n_splits * (d + 2) * (int64_t)sizeof(float) : 0;
   if ((int64_t)ws_bytes < need) return fail(KV_EINVAL, "workspace of %zu bytes is smaller than the %lld needed", ws_bytes, (long long)need);
   if (need && (!workspace || !aligned16(workspace))) return fail(KV_EINVAL, "workspace must be a 16-byte aligned device pointer");
@@ -418,8 +461,9 @@ int64_t kv_chunk_workspace_bytes(const kv_cache* cache, int layer, int n_q_heads
     return fail(KV_EINVAL, "n_q_heads %d is not a positive multiple of n_kv_heads %d", n_q_heads, cache->hkv);
   if (n_new < 1) return fail(KV_EINVAL, "n_new must be >= 1");
   int64_t rows = n_new * (n_q_heads / cache->hkv);
-  int64_t wgs = ceil_div(rows, kChunkRows) * cache->hkv;
-  int64_t cap = chunk_split_cap(wgs);
+  int64_t base = ceil_div(rows, kChunkRows) * cache->hkv;
+  const int64_t slots = resident_slots(cache->device, chunk_kernel_for(cache->kbits, cache->vbits, cache->d, false));
+  int64_t cap = split_cap(base, slots, kMaxSplitsChunk);
   if (cap <= 1) return 0;
   return n_new * n_q_heads * cap * (cache->d + 2) * (int64_t)sizeof(float);
 }
@@ -444,9 +488,12 @@ int kv_attend_chunk(kv_cache* cache, int layer, const void* q, int q_dtype, int 
   const int64_t rows = n_new * group;
   const int64_t mtiles = ceil_div(rows, kChunkRows);
   if (mtiles > 0x7fffffff) return fail(KV_EUNSUPPORTED, "chunk of %lld rows is too large", (long long)rows);
+  const int64_t base = mtiles * cache->hkv;
+  const int64_t slots = resident_slots(cache->device, chunk_kernel_for(cache->kbits, cache->vbits, cache->d, false));
   int n_splits;
   int64_t tps;
-  chunk_plan(mtiles * cache->hkv, len, &n_splits, &tps);
+  plan_splits(base, slots, split_cap(base, slots, kMaxSplitsChunk), len, kChunkKeys, kChunkMinKeysPerSplit,
+              &n_splits, &tps);
   int64_t need = n_splits > 1 ? n_new * n_q_heads * n_splits * (cache->d + 2) * (int64_t)sizeof(float) : 0;
   if ((int64_t)ws_bytes < need) return fail(KV_EINVAL, "workspace of %zu bytes is smaller than the %lld needed", ws_bytes, (long long)need);
   if (need && (!workspace || !aligned16(workspace))) return fail(KV_EINVAL, "workspace must be a 16-byte aligned device pointer");

@@ -94,4 +94,8 @@ hipError_t launch_decode(const DecodeArgs& a, int kbits, int vbits, int d, int g
 hipError_t launch_chunk(const ChunkArgs& a, int kbits, int vbits, int d, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
 
+// Kernel symbols, for occupancy queries by the split planner.
+const void* decode_kernel_for(int kbits, int vbits, int d, int gp);
+const void* chunk_kernel_for(int kbits, int vbits, int d, bool q_fp32);
+
 }  // namespace kvq

@@ -12,9 +12,11 @@ constexpr int kDppHalfMirror = 0x141;  // lane i <- 7 - i within 8
 constexpr int kDppMirror = 0x140;      // lane i <- 15 - i within 16
 constexpr int kDppRor(int n) { return 0x120 + n; }  // rotate right by n within 16
 
+// Every control used here reads a valid lane, so bound_ctrl does not change the result;
+// this form lets the compiler fold the move into the consuming op (v_add_f32_dpp).
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), CTRL, 0xf, 0xf, false));
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, true));
 }
 
 __device__ __forceinline__ float readlane(float x, int lane) {
