@@ -12,7 +12,7 @@
 // Quantized keys are carried as fp16 hi + lo (code * scale = hi + lo exactly), so scores
 // are exact up to fp32 accumulation; fp32 queries are likewise carried as hi + lo.
 //
-// A workgroup (4 waves) owns 128 rows of one KV head and one split of the context.
+// A workgroup owns 256 rows of one KV head and one split of the context.
 // Per 64-key tile: the workgroup dequantizes K into LDS as [key][d] and V as [d][key]
 // (packed fp16 arithmetic on magic-number conversions of the codes), while the raw
 // codes of the next tile are already in flight; each wave computes S^T = K Q^T (lane =
@@ -23,6 +23,8 @@
 // (probabilities up to 256 stay exact in fp16), which makes the rescale of the
 // accumulators rare.
 #include "kvq_internal.h"
+
+#include <type_traits>
 
 #ifndef KVQ_CHUNK_KSPLIT
 #define KVQ_CHUNK_KSPLIT 1
@@ -102,39 +104,199 @@ __device__ __forceinline__ void k4_pairs(uint32_t w, half2_t (&c)[4]) {
 }
 
 template <int KB, int VB, int D, bool QSPLIT, bool KSPLIT_>
-__global__ __launch_bounds__(256, 2) void chunk_kernel(ChunkArgs a) {
+__global__ __launch_bounds__(kChunkThreads) void chunk_kernel(ChunkArgs a) {
   constexpr bool KSPLIT = KSPLIT_ && KB != 16;   // fp16 keys are exact already
   constexpr int NK = kChunkKeys;   // keys per tile
   constexpr int KSTR = D + 8;      // halves per LDS key row
-  constexpr int VSTR = NK + 8;     // halves per LDS transposed-value row
+  constexpr int VSTR = NK + 4;     // halves per LDS transposed-value row (34 dwords: no bank conflicts)
   constexpr int NDT = D / 32;      // 32-wide output blocks along d
   constexpr int NKS = D / 16;      // k-steps of Q.K^T
-  constexpr int KE = D / 4;        // key elements one thread dequantizes (4 threads per key)
+  constexpr int KE = D / 4;        // key elements one producer thread dequantizes (4 per key)
   constexpr int KW = KE * KB / 32; // their dwords
   constexpr int VW = VB / 4;       // dwords of 8 value elements of one key
   constexpr int VITEMS = (NK / 4) * (D / 8);  // (4 keys x 8 d) value items per tile
-  __shared__ __attribute__((aligned(16))) _Float16 s_k[NK * KSTR];
-  __shared__ __attribute__((aligned(16))) _Float16 s_kl[KSPLIT ? NK * KSTR : 8];
-  __shared__ __attribute__((aligned(16))) _Float16 s_vt[D * VSTR];
+  constexpr int KBUF = NK * KSTR, VBUF = D * VSTR;
+  static_assert(kChunkThreads == 768 && kChunkRows == 256, "8 consumer + 4 producer waves");
+  // two tile buffers: the producers fill one while the consumers read the other
+  __shared__ __attribute__((aligned(16))) _Float16 s_k[2 * KBUF];
+  __shared__ __attribute__((aligned(16))) _Float16 s_kl[KSPLIT ? 2 * KBUF : 8];
+  __shared__ __attribute__((aligned(16))) _Float16 s_vt[2 * VBUF];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int hl = lane >> 5, col = lane & 31;
-  const int head = blockIdx.y, split = blockIdx.z;
+  const bool producer = wave >= 8;
+  // Workgroups are dealt round-robin to the 8 XCDs.  Renumber them so that the row
+  // tiles of one (KV head, split), which all stream the same keys and values, sit on
+  // one XCD and share its L2.
+  int mt, head, split;
+  {
+    const uint32_t n_mt = gridDim.x, n = gridDim.x * gridDim.y * gridDim.z;
+    const uint32_t lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+    const uint32_t xcd = lin % kXcds, per = n / kXcds, rem = n % kXcds;
+    const uint32_t t = xcd * per + min(xcd, rem) + lin / kXcds;   // bijection on [0, n)
+    mt = (int)(t % n_mt);
+    head = (int)((t / n_mt) % gridDim.y);
+    split = (int)(t / (n_mt * gridDim.y));
+  }
   const int64_t rows = a.n_new * a.group;
-  const int64_t tile_r0 = (int64_t)blockIdx.x * kChunkRows;
-  const int64_t r0 = tile_r0 + wave * 32;
-  const int64_t my_row = r0 + col;
-  const bool valid = my_row < rows;
+  const int64_t tile_r0 = (int64_t)mt * kChunkRows;
   const int64_t base_pos = a.len - a.n_new;
-  const int64_t tok = valid ? my_row / a.group : 0;
-  const int qh = head * a.group + (valid ? (int)(my_row % a.group) : 0);
-  const int64_t pos = valid ? base_pos + tok : -1;
 
   const int64_t region = a.g.region();
   const uint8_t* kc = a.base + (int64_t)head * region;
   const uint8_t* ks = kc + a.g.off_ks();
   const uint8_t* vc = kc + a.g.off_vc();
   const uint8_t* vs = kc + a.g.off_vs();
+
+  const int64_t k_lo = (int64_t)split * a.tps;
+  const int64_t k_hi = min(k_lo + a.tps, a.len);
+  const int64_t last_row = min(tile_r0 + kChunkRows, rows) - 1;
+  const int64_t k_end = min(k_hi, base_pos + last_row / a.group + 1);
+  const int n_tiles = k_end > k_lo ? (int)((k_end - k_lo + NK - 1) / NK) : 0;
+  // tiles before n_safe are visible to every row of the workgroup: no mask work
+  const int64_t wg_min_pos = base_pos + tile_r0 / a.group;
+  const int n_safe = (int)max((int64_t)0, (min(k_end, wg_min_pos + 1) - k_lo) / NK);
+
+  if (producer) {
+    // ================= producers: fetch codes, dequantize into the free buffer ==========
+    const int pt = tid - 512;
+    const int k_key = pt >> 2, k_part = pt & 3;
+    const int v_kg = pt & 15, v_dg = pt >> 4;
+    const bool v_on = pt < VITEMS;
+    const uint32_t k_off = k_key * a.g.kc + k_part * (KW * 4);
+    const uint32_t ks_off = k_key * a.g.ks + 2 * ((k_part * KE) / kBlock);
+    const uint32_t v_off = 4 * v_kg * a.g.vc + v_dg * VB;
+    const uint32_t vs_off = 4 * v_kg * a.g.vs + 2 * (v_dg >> 2);
+    uint32_t kraw[KW];
+    uint16_t kscale = 0;
+    uint32_t vraw[4][VW];
+    uint16_t vscale[4] = {0, 0, 0, 0};
+    auto fetch = [&](int t) {
+      const int64_t kt0 = k_lo + (int64_t)t * NK;
+      load_dw<KW>(kc + kt0 * a.g.kc + k_off, kraw);
+      if constexpr (KB != 16) kscale = *reinterpret_cast<const uint16_t*>(ks + kt0 * a.g.ks + ks_off);
+      if (v_on) {
+        const uint8_t* vt = vc + kt0 * a.g.vc;
+        const uint8_t* vst = vs + kt0 * a.g.vs;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          load_dw<VW>(vt + kk * a.g.vc + v_off, vraw[kk]);
+          if constexpr (VB != 16) vscale[kk] = *reinterpret_cast<const uint16_t*>(vst + kk * a.g.vs + vs_off);
+        }
+      }
+    };
+    auto produce = [&](int buf) {
+      _Float16* bk = s_k + buf * KBUF;
+      _Float16* bkl = s_kl + (KSPLIT ? buf * KBUF : 0);
+      _Float16* bv = s_vt + buf * VBUF;
+      {
+        half2_t hi[KE / 2], lo[KE / 2];
+        if constexpr (KB == 16) {
+#pragma unroll
+          for (int i = 0; i < KE / 2; ++i) hi[i] = h2(kraw[i]);
+        } else {
+          const half2_t d2 = splat(kscale);
+#pragma unroll
+          for (int w = 0; w < KW; ++w) {
+            if constexpr (KB == 8) {
+              half2_t c[2];
+              k8_pairs(kraw[w], c);
+#pragma unroll
+              for (int j = 0; j < 2; ++j) {
+                hi[2 * w + j] = c[j] * d2;
+                if constexpr (KSPLIT) lo[2 * w + j] = __builtin_elementwise_fma(c[j], d2, -hi[2 * w + j]);
+              }
+            } else {
+              half2_t c[4];
+              k4_pairs(kraw[w], c);
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                hi[4 * w + j] = c[j] * d2;
+                if constexpr (KSPLIT) lo[4 * w + j] = __builtin_elementwise_fma(c[j], d2, -hi[4 * w + j]);
+              }
+            }
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < KE / 8; ++i) {
+          const int off = k_key * KSTR + k_part * KE + 8 * i;
+          *reinterpret_cast<uint4*>(&bk[off]) =
+              make_uint4(u32(hi[4 * i]), u32(hi[4 * i + 1]), u32(hi[4 * i + 2]), u32(hi[4 * i + 3]));
+          if constexpr (KSPLIT)
+            *reinterpret_cast<uint4*>(&bkl[off]) =
+                make_uint4(u32(lo[4 * i]), u32(lo[4 * i + 1]), u32(lo[4 * i + 2]), u32(lo[4 * i + 3]));
+        }
+      }
+      if (v_on) {
+        // keys (0, 1) and (2, 3) side by side per element: pr[e][pair] = (v_2p, v_2p+1)
+        uint32_t pr[8][2];
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          const uint32_t* wa = vraw[2 * p];
+          const uint32_t* wb = vraw[2 * p + 1];
+          half2_t d2 = hconst(1.f);
+          if constexpr (VB != 16) {
+            d2.x = __builtin_bit_cast(_Float16, vscale[2 * p]);
+            d2.y = __builtin_bit_cast(_Float16, vscale[2 * p + 1]);
+          }
+          if constexpr (VB == 4) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const uint32_t sel = (uint32_t)j | ((uint32_t)(4 + j) << 16) | 0x0c000c00u;  // [a.bj, 0, b.bj, 0]
+              const uint32_t q = __builtin_amdgcn_perm(wb[0], wa[0], sel);
+              const half2_t ce = h2((q & 0x000F000Fu) | kHalfBias1024) - hconst(1032.f);
+              const half2_t co = h2(((q >> 4) & 0x000F000Fu) | kHalfBias1024) - hconst(1032.f);
+              pr[2 * j][p] = u32(ce * d2);
+              pr[2 * j + 1][p] = u32(co * d2);
+            }
+          } else if constexpr (VB == 8) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+              const uint32_t xa = wa[i] ^ 0x80808080u, xb = wb[i] ^ 0x80808080u;
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const uint32_t sel = (uint32_t)j | ((uint32_t)(4 + j) << 16) | 0x0c000c00u;
+                const uint32_t q = __builtin_amdgcn_perm(xb, xa, sel) | kHalfBias1024;
+                pr[4 * i + j][p] = u32((h2(q) - hconst(1152.f)) * d2);
+              }
+            }
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              pr[2 * i][p] = __builtin_amdgcn_perm(wb[i], wa[i], 0x05040100u);
+              pr[2 * i + 1][p] = __builtin_amdgcn_perm(wb[i], wa[i], 0x07060302u);
+            }
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          *reinterpret_cast<uint2*>(&bv[(8 * v_dg + e) * VSTR + 4 * v_kg]) = make_uint2(pr[e][0], pr[e][1]);
+      }
+    };
+    if (n_tiles > 0) {
+      fetch(0);
+      produce(0);
+      if (n_tiles > 1) fetch(1);
+    }
+    __syncthreads();
+    for (int t = 0; t < n_tiles; ++t) {
+      if (t + 1 < n_tiles) {
+        produce((t + 1) & 1);                 // tile t + 1 into the buffer not being read
+        if (t + 2 < n_tiles) fetch(t + 2);    // its successor's codes fly meanwhile
+      }
+      __syncthreads();
+    }
+    return;
+  }
+
+  // ================= consumers: 32 query rows per wave =================================
+  const int hl = lane >> 5, col = lane & 31;
+  const int64_t r0 = tile_r0 + wave * 32;
+  const int64_t my_row = r0 + col;
+  const bool valid = my_row < rows;
+  const int64_t tok = valid ? my_row / a.group : 0;
+  const int qh = head * a.group + (valid ? (int)(my_row % a.group) : 0);
+  const int64_t pos = valid ? base_pos + tok : -1;
+  const bool wave_active = r0 < rows;
 
   // Q^T as the B operand: lane (col, hl) holds d = 16 k + 8 hl .. + 7 of its row.
   half8_t qv[NKS];
@@ -152,36 +314,6 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(ChunkArgs a) {
     }
   }
 
-  const int64_t k_lo = (int64_t)split * a.tps;
-  const int64_t k_hi = min(k_lo + a.tps, a.len);
-  const int64_t last_row = min(tile_r0 + kChunkRows, rows) - 1;
-  const int64_t k_end = min(k_hi, base_pos + last_row / a.group + 1);
-  const int64_t wave_min_pos = base_pos + r0 / a.group;
-  const bool wave_active = r0 < rows;
-
-  // this thread's share of a tile: key row tid / 4 (a quarter of it) and one value item
-  // of 4 keys x 8 elements
-  const int k_key = tid >> 2, k_part = tid & 3;
-  const int v_kg = tid & 15, v_dg = tid >> 4;
-  const bool v_on = tid < VITEMS;
-  uint32_t kraw[KW];
-  uint16_t kscale = 0;
-  uint32_t vraw[4][VW];
-  uint16_t vscale[4] = {0, 0, 0, 0};
-  auto fetch = [&](int64_t kt0) {
-    const int64_t key = kt0 + k_key;
-    load_dw<KW>(kc + key * a.g.kc + k_part * (KW * 4), kraw);
-    if constexpr (KB != 16) kscale = *reinterpret_cast<const uint16_t*>(ks + key * a.g.ks + 2 * ((k_part * KE) / kBlock));
-    if (v_on) {
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int64_t vk = kt0 + 4 * v_kg + kk;
-        load_dw<VW>(vc + vk * a.g.vc + v_dg * VB, vraw[kk]);
-        if constexpr (VB != 16) vscale[kk] = *reinterpret_cast<const uint16_t*>(vs + vk * a.g.vs + 2 * (v_dg >> 2));
-      }
-    }
-  };
-
   float m = -INFINITY, l = 0.f;
   float16_t o[NDT];
 #pragma unroll
@@ -189,172 +321,87 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(ChunkArgs a) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) o[t][v] = 0.f;
 
-  if (k_lo < k_end) fetch(k_lo);
-  for (int64_t kt0 = k_lo; kt0 < k_end; kt0 += NK) {
-    // ---- dequantize the fetched tile into LDS -------------------------------------
-    {
-      half2_t hi[KE / 2], lo[KE / 2];
-      if constexpr (KB == 16) {
+  // one 32-key half of a tile: S^T = K Q^T, online softmax, O^T += V^T P^T
+  auto half = [&](auto masked, const _Float16* bk, const _Float16* bkl, const _Float16* bv, int64_t kt0, int st) {
+    float16_t sv;
 #pragma unroll
-        for (int i = 0; i < KE / 2; ++i) hi[i] = h2(kraw[i]);
-      } else {
-        const half2_t d2 = splat(kscale);
+    for (int v = 0; v < 16; ++v) sv[v] = 0.f;
 #pragma unroll
-        for (int w = 0; w < KW; ++w) {
-          if constexpr (KB == 8) {
-            half2_t c[2];
-            k8_pairs(kraw[w], c);
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-              hi[2 * w + j] = c[j] * d2;
-              if constexpr (KSPLIT) lo[2 * w + j] = __builtin_elementwise_fma(c[j], d2, -hi[2 * w + j]);
-            }
-          } else {
-            half2_t c[4];
-            k4_pairs(kraw[w], c);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              hi[4 * w + j] = c[j] * d2;
-              if constexpr (KSPLIT) lo[4 * w + j] = __builtin_elementwise_fma(c[j], d2, -hi[4 * w + j]);
-            }
-          }
-        }
+    for (int k = 0; k < NKS; ++k) {
+      const int off = (32 * st + col) * KSTR + 16 * k + 8 * hl;
+      const half8_t ak = *reinterpret_cast<const half8_t*>(&bk[off]);
+      sv = __builtin_amdgcn_mfma_f32_32x32x16_f16(ak, qv[k], sv, 0, 0, 0);
+      if constexpr (KSPLIT) {
+        const half8_t al = *reinterpret_cast<const half8_t*>(&bkl[off]);
+        sv = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, qv[k], sv, 0, 0, 0);
       }
+      if constexpr (QSPLIT) sv = __builtin_amdgcn_mfma_f32_32x32x16_f16(ak, ql[k], sv, 0, 0, 0);
+    }
+    if constexpr (decltype(masked)::value) {
+      // keys kt0 + 32 st + [0, 32): offsets >= lim are past the range or in the future
+      const int64_t kb0 = kt0 + 32 * st;
+      const int lim = (int)max((int64_t)-1, min(min(k_end, pos + 1) - kb0, (int64_t)32));
 #pragma unroll
-      for (int i = 0; i < KE / 8; ++i) {
-        const int off = k_key * KSTR + k_part * KE + 8 * i;
-        *reinterpret_cast<uint4*>(&s_k[off]) =
-            make_uint4(u32(hi[4 * i]), u32(hi[4 * i + 1]), u32(hi[4 * i + 2]), u32(hi[4 * i + 3]));
-        if constexpr (KSPLIT)
-          *reinterpret_cast<uint4*>(&s_kl[off]) =
-              make_uint4(u32(lo[4 * i]), u32(lo[4 * i + 1]), u32(lo[4 * i + 2]), u32(lo[4 * i + 3]));
+      for (int v = 0; v < 16; ++v)
+        if (8 * (v >> 2) + 4 * hl + (v & 3) >= lim) sv[v] = -INFINITY;
+    }
+    // online softmax, one query row per lane pair (col, col + 32)
+    float mx = sv[0];
+#pragma unroll
+    for (int v = 1; v < 16; ++v) mx = fmaxf(mx, sv[v]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.qk_scale;
+    const bool move = mx > m + kLazyMax;
+    if (__any(move)) {
+      const float mn = move ? mx : m;
+      const float alpha = __builtin_amdgcn_exp2f(m - (mn == -INFINITY ? 0.f : mn));
+      l *= alpha;
+#pragma unroll
+      for (int t = 0; t < NDT; ++t)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[t][v] *= alpha;
+      m = mn;
+    }
+    const float mu = m == -INFINITY ? 0.f : m;
+    half8_t pb[2];
+#pragma unroll
+    for (int v = 0; v < 16; v += 2) {
+      half2_t pp;
+      pp.x = (_Float16)__builtin_amdgcn_exp2f(fmaf(sv[v], a.qk_scale, -mu));
+      pp.y = (_Float16)__builtin_amdgcn_exp2f(fmaf(sv[v + 1], a.qk_scale, -mu));
+      l = __builtin_amdgcn_fdot2(pp, hconst(1.f), l, false);   // sum of the rounded weights
+      pb[v >> 3][v & 7] = pp.x;
+      pb[v >> 3][(v & 7) + 1] = pp.y;
+    }
+#pragma unroll
+    for (int t = 0; t < NDT; ++t) {
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const _Float16* vp = &bv[(32 * t + col) * VSTR + 32 * st + 16 * kk + 4 * hl];
+        const half4_t lo4 = *reinterpret_cast<const half4_t*>(vp);
+        const half4_t hi4 = *reinterpret_cast<const half4_t*>(vp + 8);
+        half8_t av;
+        av[0] = lo4[0]; av[1] = lo4[1]; av[2] = lo4[2]; av[3] = lo4[3];
+        av[4] = hi4[0]; av[5] = hi4[1]; av[6] = hi4[2]; av[7] = hi4[3];
+        o[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, pb[kk], o[t], 0, 0, 0);
       }
     }
-    if (v_on) {
-      // keys (0, 1) and (2, 3) side by side per element: pr[e][pair] = (v_2p, v_2p+1)
-      uint32_t pr[8][2];
-#pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        const uint32_t* wa = vraw[2 * p];
-        const uint32_t* wb = vraw[2 * p + 1];
-        half2_t d2 = hconst(1.f);
-        if constexpr (VB != 16) {
-          d2.x = __builtin_bit_cast(_Float16, vscale[2 * p]);
-          d2.y = __builtin_bit_cast(_Float16, vscale[2 * p + 1]);
-        }
-        if constexpr (VB == 4) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const uint32_t sel = (uint32_t)j | ((uint32_t)(4 + j) << 16) | 0x0c000c00u;  // [a.bj, 0, b.bj, 0]
-            const uint32_t q = __builtin_amdgcn_perm(wb[0], wa[0], sel);
-            const half2_t ce = h2((q & 0x000F000Fu) | kHalfBias1024) - hconst(1032.f);
-            const half2_t co = h2(((q >> 4) & 0x000F000Fu) | kHalfBias1024) - hconst(1032.f);
-            pr[2 * j][p] = u32(ce * d2);
-            pr[2 * j + 1][p] = u32(co * d2);
-          }
-        } else if constexpr (VB == 8) {
-#pragma unroll
-          for (int i = 0; i < 2; ++i) {
-            const uint32_t xa = wa[i] ^ 0x80808080u, xb = wb[i] ^ 0x80808080u;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const uint32_t sel = (uint32_t)j | ((uint32_t)(4 + j) << 16) | 0x0c000c00u;
-              const uint32_t q = __builtin_amdgcn_perm(xb, xa, sel) | kHalfBias1024;
-              pr[4 * i + j][p] = u32((h2(q) - hconst(1152.f)) * d2);
-            }
-          }
-        } else {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            pr[2 * i][p] = __builtin_amdgcn_perm(wb[i], wa[i], 0x05040100u);
-            pr[2 * i + 1][p] = __builtin_amdgcn_perm(wb[i], wa[i], 0x07060302u);
-          }
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        *reinterpret_cast<uint2*>(&s_vt[(8 * v_dg + e) * VSTR + 4 * v_kg]) = make_uint2(pr[e][0], pr[e][1]);
-    }
-    __syncthreads();
-    if (kt0 + NK < k_end) fetch(kt0 + NK);   // the next tile's codes fly during the math below
-
+  };
+  auto consume = [&](auto masked, int t) {
     if (wave_active) {
-      // ---- S^T = K Q^T --------------------------------------------------------------
-      float16_t s[2];
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) s[st][v] = 0.f;
-#pragma unroll
-        for (int k = 0; k < NKS; ++k) {
-          const int off = (32 * st + col) * KSTR + 16 * k + 8 * hl;
-          const half8_t ak = *reinterpret_cast<const half8_t*>(&s_k[off]);
-          s[st] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ak, qv[k], s[st], 0, 0, 0);
-          if constexpr (KSPLIT) {
-            const half8_t al = *reinterpret_cast<const half8_t*>(&s_kl[off]);
-            s[st] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, qv[k], s[st], 0, 0, 0);
-          }
-          if constexpr (QSPLIT) s[st] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ak, ql[k], s[st], 0, 0, 0);
-        }
-      }
-      // ---- causal / range mask (only on tiles that reach the edge) ----------------
-      if (kt0 + NK > k_end || kt0 + NK - 1 > wave_min_pos) {
-#pragma unroll
-        for (int st = 0; st < 2; ++st)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int64_t key = kt0 + 32 * st + 8 * (v >> 2) + 4 * hl + (v & 3);
-            if (key >= k_end || key > pos) s[st][v] = -INFINITY;
-          }
-      }
-      // ---- online softmax, one query row per lane pair (col, col + 32) ------------
-      float mx = -INFINITY;
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[st][v]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.qk_scale;
-      const bool move = mx > m + kLazyMax;
-      if (__any(move)) {
-        const float mn = move ? mx : m;
-        const float alpha = __builtin_amdgcn_exp2f(m - (mn == -INFINITY ? 0.f : mn));
-        l *= alpha;
-#pragma unroll
-        for (int t = 0; t < NDT; ++t)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) o[t][v] *= alpha;
-        m = mn;
-      }
-      const float mu = m == -INFINITY ? 0.f : m;
-      half8_t pb[4];
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int v = 0; v < 16; v += 2) {
-          half2_t pp;
-          pp.x = (_Float16)__builtin_amdgcn_exp2f(fmaf(s[st][v], a.qk_scale, -mu));
-          pp.y = (_Float16)__builtin_amdgcn_exp2f(fmaf(s[st][v + 1], a.qk_scale, -mu));
-          l = __builtin_amdgcn_fdot2(pp, hconst(1.f), l, false);   // sum of the rounded weights
-          pb[2 * st + (v >> 3)][v & 7] = pp.x;
-          pb[2 * st + (v >> 3)][(v & 7) + 1] = pp.y;
-        }
-      // ---- O^T += V^T P^T ---------------------------------------------------------------
-#pragma unroll
-      for (int t = 0; t < NDT; ++t) {
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const _Float16* vp = &s_vt[(32 * t + col) * VSTR + 32 * (kk >> 1) + 16 * (kk & 1) + 4 * hl];
-          const half4_t lo4 = *reinterpret_cast<const half4_t*>(vp);
-          const half4_t hi4 = *reinterpret_cast<const half4_t*>(vp + 8);
-          half8_t av;
-          av[0] = lo4[0]; av[1] = lo4[1]; av[2] = lo4[2]; av[3] = lo4[3];
-          av[4] = hi4[0]; av[5] = hi4[1]; av[6] = hi4[2]; av[7] = hi4[3];
-          o[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, pb[kk], o[t], 0, 0, 0);
-        }
-      }
+      const int buf = t & 1;
+      const _Float16* bk = s_k + buf * KBUF;
+      const _Float16* bkl = s_kl + (KSPLIT ? buf * KBUF : 0);
+      const _Float16* bv = s_vt + buf * VBUF;
+      const int64_t kt0 = k_lo + (int64_t)t * NK;
+      half(masked, bk, bkl, bv, kt0, 0);
+      half(masked, bk, bkl, bv, kt0, 1);
     }
     __syncthreads();
-  }
+  };
+  __syncthreads();   // tile 0 is in place
+  int t = 0;
+  for (; t < n_safe && t < n_tiles; ++t) consume(std::false_type{}, t);
+  for (; t < n_tiles; ++t) consume(std::true_type{}, t);
 
   // ---- output -----------------------------------------------------------------------
   const float lt = l + __shfl_xor(l, 32);
@@ -363,22 +410,23 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(ChunkArgs a) {
   if (a.n_splits == 1) {
     const float inv = 1.f / lt;
 #pragma unroll
-    for (int t = 0; t < NDT; ++t)
+    for (int t2 = 0; t2 < NDT; ++t2)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const int d = 32 * t + 8 * g4 + 4 * hl;
-        float4 v = make_float4(o[t][4 * g4] * inv, o[t][4 * g4 + 1] * inv, o[t][4 * g4 + 2] * inv, o[t][4 * g4 + 3] * inv);
+        const int d = 32 * t2 + 8 * g4 + 4 * hl;
+        float4 v = make_float4(o[t2][4 * g4] * inv, o[t2][4 * g4 + 1] * inv, o[t2][4 * g4 + 2] * inv,
+                               o[t2][4 * g4 + 3] * inv);
         *reinterpret_cast<float4*>(a.out + orow * D + d) = v;
       }
   } else {
     float* p = a.ws + (orow * a.n_splits + split) * (D + 2);
 #pragma unroll
-    for (int t = 0; t < NDT; ++t)
+    for (int t2 = 0; t2 < NDT; ++t2)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const int d = 32 * t + 8 * g4 + 4 * hl;
+        const int d = 32 * t2 + 8 * g4 + 4 * hl;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) p[d + i] = o[t][4 * g4 + i];
+        for (int i = 0; i < 4; ++i) p[d + i] = o[t2][4 * g4 + i];
       }
     if (hl == 0) {
       p[D] = m;
@@ -398,9 +446,9 @@ hipError_t launch_t(const ChunkArgs& a, hipStream_t s) {
   const int64_t mt = (rows + kChunkRows - 1) / kChunkRows;
   dim3 grid((unsigned)mt, a.hkv, a.n_splits);
   if (a.q_dtype == 0)
-    hipLaunchKernelGGL((chunk_kernel<KB, VB, D, true, KVQ_CHUNK_KSPLIT != 0>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((chunk_kernel<KB, VB, D, true, KVQ_CHUNK_KSPLIT != 0>), grid, dim3(kChunkThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((chunk_kernel<KB, VB, D, false, KVQ_CHUNK_KSPLIT != 0>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((chunk_kernel<KB, VB, D, false, KVQ_CHUNK_KSPLIT != 0>), grid, dim3(kChunkThreads), 0, s, a);
   return hipGetLastError();
 }
 

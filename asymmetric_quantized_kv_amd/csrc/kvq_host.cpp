@@ -115,8 +115,8 @@ constexpr int kMaxSplitsChunk = 64;
 
 std::mutex g_plan_mu;
 
-// resident workgroups of `kernel` (256 threads) on `device`; 0 if the runtime cannot say
-int64_t resident_slots(int device, const void* kernel) {
+// resident workgroups of `kernel` (`threads` per workgroup) on `device`; 0 if unknown
+int64_t resident_slots(int device, const void* kernel, int threads = 256) {
   static int cus[64];
   static std::vector<std::pair<const void*, int>> per_cu;
   std::lock_guard<std::mutex> lk(g_plan_mu);
@@ -130,7 +130,7 @@ int64_t resident_slots(int device, const void* kernel) {
   for (auto& e : per_cu)
     if (e.first == kernel) n = e.second;
   if (n < 0) {
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, 256, 0) != hipSuccess) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess) {
       (void)hipGetLastError();
       n = 1;
     }
@@ -462,7 +462,8 @@ int64_t kv_chunk_workspace_bytes(const kv_cache* cache, int layer, int n_q_heads
   if (n_new < 1) return fail(KV_EINVAL, "n_new must be >= 1");
   int64_t rows = n_new * (n_q_heads / cache->hkv);
   int64_t base = ceil_div(rows, kChunkRows) * cache->hkv;
-  const int64_t slots = resident_slots(cache->device, chunk_kernel_for(cache->kbits, cache->vbits, cache->d, false));
+  const int64_t slots = resident_slots(cache->device, chunk_kernel_for(cache->kbits, cache->vbits, cache->d, false),
+                                       kChunkThreads);
   int64_t cap = split_cap(base, slots, kMaxSplitsChunk);
   if (cap <= 1) return 0;
   return n_new * n_q_heads * cap * (cache->d + 2) * (int64_t)sizeof(float);
@@ -489,7 +490,8 @@ int kv_attend_chunk(kv_cache* cache, int layer, const void* q, int q_dtype, int 
   const int64_t mtiles = ceil_div(rows, kChunkRows);
   if (mtiles > 0x7fffffff) return fail(KV_EUNSUPPORTED, "chunk of %lld rows is too large", (long long)rows);
   const int64_t base = mtiles * cache->hkv;
-  const int64_t slots = resident_slots(cache->device, chunk_kernel_for(cache->kbits, cache->vbits, cache->d, false));
+  const int64_t slots = resident_slots(cache->device, chunk_kernel_for(cache->kbits, cache->vbits, cache->d, false),
+                                       kChunkThreads);
   int n_splits;
   int64_t tps;
   plan_splits(base, slots, split_cap(base, slots, kMaxSplitsChunk), len, kChunkKeys, kChunkMinKeysPerSplit,

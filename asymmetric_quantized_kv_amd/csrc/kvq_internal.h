@@ -11,8 +11,10 @@ constexpr int kGranule = 256;       // capacity granule (tokens)
 constexpr int kMaxSessions = 64;    // sessions per decode launch (kernel-argument table)
 constexpr int kDecodeChunk = 128;   // tokens one wave scores before its softmax update
 constexpr int kDecodeWaveTokens = 4 * kDecodeChunk;  // split granularity of decode
-constexpr int kChunkRows = 128;     // query rows per chunk-prefill workgroup
+constexpr int kChunkThreads = 768;  // threads per chunk-prefill workgroup: 8 consumer + 4 producer waves
+constexpr int kChunkRows = 256;     // query rows per chunk-prefill workgroup (32 per consumer wave)
 constexpr int kChunkKeys = 64;      // keys per chunk-prefill tile
+constexpr uint32_t kXcds = 8;       // accelerator dies of an MI355X; workgroups are dealt round-robin
 
 __host__ __device__ constexpr int code_row_bytes(int bits, int d) {
   return bits == 16 ? 2 * d : (bits == 8 ? d : d / 2);
