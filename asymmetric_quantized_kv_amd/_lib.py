@@ -26,6 +26,15 @@ _SIGS = {
     "kv_attend_decode": (C.c_int, [C.c_void_p, C.c_int, C.c_int, C.c_void_p, C.c_int, C.c_int, C.c_float,
                                    C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
     "kv_decode_workspace_bytes": (C.c_int64, [C.c_void_p, C.c_int, C.c_int, C.c_int]),
+    "kv_decode_plan": (C.c_int, [C.c_void_p, C.c_int, C.c_int, C.c_int, C.POINTER(C.c_int),
+                                 C.POINTER(C.c_int64)]),
+    "kv_attend_decode_partial": (C.c_int, [C.c_void_p, C.c_int, C.c_int, C.c_void_p, C.c_int, C.c_int, C.c_float,
+                                           C.c_int, C.c_int64, C.c_void_p, C.c_size_t, C.c_void_p]),
+    "kv_merge_partials": (C.c_int, [C.c_void_p, C.c_int64, C.c_int, C.c_int, C.c_void_p, C.c_void_p]),
+    "kv_chunk_plan": (C.c_int, [C.c_void_p, C.c_int, C.c_int, C.c_int64, C.POINTER(C.c_int),
+                                C.POINTER(C.c_int64)]),
+    "kv_attend_chunk_partial": (C.c_int, [C.c_void_p, C.c_int, C.c_void_p, C.c_int, C.c_int, C.c_int64, C.c_float,
+                                          C.c_int, C.c_int64, C.c_void_p, C.c_size_t, C.c_void_p]),
     "kv_attend_chunk": (C.c_int, [C.c_void_p, C.c_int, C.c_void_p, C.c_int, C.c_int, C.c_int64, C.c_float,
                                   C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
     "kv_chunk_workspace_bytes": (C.c_int64, [C.c_void_p, C.c_int, C.c_int, C.c_int64]),
@@ -158,6 +167,68 @@ def kv_attend_decode(sessions, layer: int, q, sm_scale: float, out=None, workspa
                                   hq, float(sm_scale), _dev_ptr(out, "out"), _dev_ptr(workspace, "workspace"),
                                   workspace.numel() * workspace.element_size(), _stream(stream)))
     return out
+
+
+def kv_decode_plan(sessions, layer: int, n_q_heads: int):
+    """(n_splits, tokens_per_split) that kv_attend_decode uses for these sessions."""
+    n, t = C.c_int(), C.c_int64()
+    _check(lib().kv_decode_plan(_handles(sessions), len(sessions), layer, n_q_heads, C.byref(n), C.byref(t)))
+    return n.value, t.value
+
+
+def kv_attend_decode_partial(sessions, layer: int, q, sm_scale: float, n_splits: int, tokens_per_split: int,
+                             partials=None, stream=None):
+    """First pass only; returns partials (fp32 [n_sessions, n_q_heads, n_splits, head_dim + 2])."""
+    torch = _torch()
+    n_s, hq, d = q.shape
+    if n_s != len(sessions):
+        raise ValueError("q's first dimension must equal the number of sessions")
+    if partials is None:
+        partials = torch.empty((n_s, hq, n_splits, d + 2), dtype=torch.float32, device=q.device)
+    _check(lib().kv_attend_decode_partial(_handles(sessions), len(sessions), layer, _dev_ptr(q, "q"),
+                                          _dtype_code(q), hq, float(sm_scale), n_splits, tokens_per_split,
+                                          _dev_ptr(partials, "partials"),
+                                          partials.numel() * partials.element_size(), _stream(stream)))
+    return partials
+
+
+def kv_merge_partials(partials, out=None, stream=None):
+    """partials: fp32 [..., n_splits, head_dim + 2]; returns out (fp32 [..., head_dim])."""
+    torch = _torch()
+    if partials.dtype != torch.float32 or partials.dim() < 2:
+        raise ValueError("partials must be fp32 [..., n_splits, head_dim + 2]")
+    n_splits, d = partials.shape[-2], partials.shape[-1] - 2
+    lead = tuple(partials.shape[:-2])
+    rows = 1
+    for x in lead:
+        rows *= x
+    if out is None:
+        out = torch.empty(lead + (d,), dtype=torch.float32, device=partials.device)
+    _check(lib().kv_merge_partials(_dev_ptr(partials, "partials"), rows, n_splits, d, _dev_ptr(out, "out"),
+                                   _stream(stream)))
+    return out
+
+
+def kv_chunk_plan(cache: int, layer: int, n_q_heads: int, n_new: int):
+    """(n_splits, keys_per_split) that kv_attend_chunk uses."""
+    n, t = C.c_int(), C.c_int64()
+    _check(lib().kv_chunk_plan(cache, layer, n_q_heads, n_new, C.byref(n), C.byref(t)))
+    return n.value, t.value
+
+
+def kv_attend_chunk_partial(cache: int, layer: int, q, n_new: int, sm_scale: float, n_splits: int,
+                            keys_per_split: int, partials=None, stream=None):
+    """First pass only; returns partials (fp32 [n_new, n_q_heads, n_splits, head_dim + 2])."""
+    torch = _torch()
+    n, hq, d = q.shape
+    if n != n_new:
+        raise ValueError("q's first dimension must equal n_new")
+    if partials is None:
+        partials = torch.empty((n, hq, n_splits, d + 2), dtype=torch.float32, device=q.device)
+    _check(lib().kv_attend_chunk_partial(cache, layer, _dev_ptr(q, "q"), _dtype_code(q), hq, n_new,
+                                         float(sm_scale), n_splits, keys_per_split, _dev_ptr(partials, "partials"),
+                                         partials.numel() * partials.element_size(), _stream(stream)))
+    return partials
 
 
 def kv_chunk_workspace_bytes(cache: int, layer: int, n_q_heads: int, n_new: int) -> int:

@@ -407,7 +407,7 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(ChunkArgs a) {
   const float lt = l + __shfl_xor(l, 32);
   if (!valid) return;
   const int64_t orow = tok * a.hq + qh;
-  if (a.n_splits == 1) {
+  if (!a.partial) {
     const float inv = 1.f / lt;
 #pragma unroll
     for (int t2 = 0; t2 < NDT; ++t2)

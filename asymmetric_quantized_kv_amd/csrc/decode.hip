@@ -415,7 +415,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       }
     }
     const int64_t row = srow + g;
-    if (a.n_splits == 1) {
+    if (!a.partial) {
       a.out[row * D + e] = o / l;
     } else {
       float* p = a.ws + (row * a.n_splits + split) * (D + 2);

@@ -356,94 +356,236 @@ int kv_append_quant(kv_cache* cache, int layer, const void* k, const void* v, in
   return KV_OK;
 }
 
-int64_t kv_decode_workspace_bytes(kv_cache* const* sessions, int n_sessions, int layer, int n_q_heads) {
-  clear_err();
+}  // extern "C"
+
+namespace {
+
+constexpr int64_t kMaxSplitsDecode = 1 << 20;
+
+int64_t partial_bytes(int64_t rows, int n_splits, int d) {
+  return rows * n_splits * (int64_t)(d + 2) * (int64_t)sizeof(float);
+}
+
+int check_q_out(const void* q, int q_dtype, const void* out, const char* out_name) {
+  if (!dtype_ok(q_dtype)) return fail(KV_EINVAL, "q_dtype %d is not one of KV_F32/KV_BF16/KV_F16", q_dtype);
+  if (!q || !out) return fail(KV_EINVAL, "q and %s must not be NULL", out_name);
+  if (!aligned16(q) || !aligned16(out)) return fail(KV_EINVAL, "q and %s must be 16-byte aligned", out_name);
+  return KV_OK;
+}
+
+int check_workspace(const void* ws, size_t ws_bytes, int64_t need) {
+  if ((int64_t)ws_bytes < need)
+    return fail(KV_EINVAL, "workspace of %zu bytes is smaller than the %lld needed", ws_bytes, (long long)need);
+  if (need && (!ws || !aligned16(ws))) return fail(KV_EINVAL, "workspace must be a 16-byte aligned device pointer");
+  return KV_OK;
+}
+
+// A caller-chosen split: n_splits ranges of `per` tokens (a multiple of `gran`) that
+// together cover `len` tokens.
+int check_split(int n_splits, int64_t per, int64_t gran, int64_t len, const char* what) {
+  if (n_splits < 1) return fail(KV_EINVAL, "n_splits must be >= 1 (got %d)", n_splits);
+  if (per < 1 || per % gran || per > (int64_t(1) << 40))
+    return fail(KV_EINVAL, "%s must be a positive multiple of %lld (got %lld)", what, (long long)gran, (long long)per);
+  if ((int64_t)n_splits * per < len)
+    return fail(KV_EINVAL, "%d splits of %lld do not cover %lld cached tokens", n_splits, (long long)per, (long long)len);
+  return KV_OK;
+}
+
+// What a decode call checks and derives before its first launch.
+struct DecodePrep {
+  int hkv, d, group, gp, kbits, vbits, device;
+  int64_t max_len, base, slots;
+};
+
+int decode_prepare(kv_cache* const* sessions, int n_sessions, int layer, int n_q_heads, bool need_tokens,
+                   DecodePrep* p) {
   int rc = check_sessions(sessions, n_sessions, layer);
   if (rc) return rc;
   const kv_cache* s0 = sessions[0];
   if (n_q_heads < 1 || n_q_heads % s0->hkv)
     return fail(KV_EINVAL, "n_q_heads %d is not a positive multiple of n_kv_heads %d", n_q_heads, s0->hkv);
-  const int gp = decode_group_pad(n_q_heads / s0->hkv);
-  if (gp < 0) return fail(KV_EUNSUPPORTED, "decode group size %d > 16 is not built", n_q_heads / s0->hkv);
-  const int64_t base = (int64_t)n_sessions * s0->hkv;
-  const int64_t slots = resident_slots(s0->device, decode_kernel_for(s0->kbits, s0->vbits, s0->d, gp));
-  const int64_t cap = split_cap(base, slots, 1 << 20);
+  if (s0->hkv > 65535) return fail(KV_EUNSUPPORTED, "n_kv_heads %d exceeds one launch (65535)", s0->hkv);
+  p->hkv = s0->hkv;
+  p->d = s0->d;
+  p->kbits = s0->kbits;
+  p->vbits = s0->vbits;
+  p->device = s0->device;
+  p->group = n_q_heads / s0->hkv;
+  p->gp = decode_group_pad(p->group);
+  if (p->gp < 0) return fail(KV_EUNSUPPORTED, "decode group size %d > 16 is not built", p->group);
+  p->max_len = 0;
+  for (int i = 0; i < n_sessions; ++i) {
+    if (need_tokens && sessions[i]->len[layer] == 0)
+      return fail(KV_EEMPTY, "session %d has no cached token in layer %d", i, layer);
+    p->max_len = std::max(p->max_len, sessions[i]->len[layer]);
+  }
+  p->base = (int64_t)n_sessions * p->hkv;
+  p->slots = resident_slots(p->device, decode_kernel_for(p->kbits, p->vbits, p->d, p->gp));
+  return KV_OK;
+}
+
+void decode_plan(const DecodePrep& p, int* n_splits, int64_t* tps) {
+  plan_splits(p.base, p.slots, split_cap(p.base, p.slots, kMaxSplitsDecode), p.max_len, kDecodeWaveTokens,
+              kDecodeWaveTokens, n_splits, tps);
+}
+
+int decode_launch(kv_cache* const* sessions, int n_sessions, int layer, const DecodePrep& p, const void* q,
+                  int q_dtype, int n_q_heads, float sm_scale, int n_splits, int64_t tps, bool partial, float* ws,
+                  float* out, hipStream_t st) {
+  DecodeArgs a;
+  memset(&a, 0, sizeof(a));
+  a.hkv = p.hkv;
+  a.hq = n_q_heads;
+  a.group = p.group;
+  a.n_splits = n_splits;
+  a.partial = partial ? 1 : 0;
+  a.tps = tps;
+  a.q = q;
+  a.q_dtype = q_dtype;
+  a.qk_scale = sm_scale * 1.4426950408889634f;
+  a.ws = ws;
+  a.out = out;
+  const kv_cache* s0 = sessions[0];
+  a.kc = s0->g.kc;
+  a.ks = s0->g.ks;
+  a.vc = s0->g.vc;
+  a.vs = s0->g.vs;
+  for (int b0 = 0; b0 < n_sessions; b0 += kMaxSessions) {
+    const int nb = std::min(kMaxSessions, n_sessions - b0);
+    a.n_sess = nb;
+    a.sess0 = b0;
+    for (int i = 0; i < nb; ++i) {
+      const kv_cache* c = sessions[b0 + i];
+      a.sess[i].base = c->arena + (int64_t)layer * p.hkv * c->g.region();
+      a.sess[i].cap = c->g.cap;
+      a.sess[i].len = c->len[layer];
+    }
+    hipError_t e = launch_decode(a, p.kbits, p.vbits, p.d, p.gp, st);
+    if (e != hipSuccess) {
+      for (int i = 0; i < n_sessions; ++i) sessions[i]->poisoned = true;
+      return fail(KV_EHIP, "decode launch: %s", hipGetErrorString(e));
+    }
+  }
+  return KV_OK;
+}
+
+hipError_t merge_launch(const float* ws, int64_t rows, int n_splits, int d, float* out, hipStream_t st) {
+  MergeArgs m;
+  m.ws = ws;
+  m.out = out;
+  m.rows = rows;
+  m.n_splits = n_splits;
+  m.d = d;
+  return launch_merge(m, st);
+}
+
+// What a chunk call checks and derives before its first launch.
+struct ChunkPrep {
+  int group;
+  int64_t len, rows, mtiles, base, slots;
+};
+
+int chunk_prepare(const kv_cache* cache, int layer, int n_q_heads, int64_t n_new, bool need_tokens, ChunkPrep* p) {
+  int rc = check_cache(cache);
+  if (rc) return rc;
+  if (layer < 0 || layer >= cache->n_layers) return fail(KV_EINVAL, "layer %d out of range [0, %d)", layer, cache->n_layers);
+  if (n_q_heads < 1 || n_q_heads % cache->hkv)
+    return fail(KV_EINVAL, "n_q_heads %d is not a positive multiple of n_kv_heads %d", n_q_heads, cache->hkv);
+  if (cache->hkv > 65535) return fail(KV_EUNSUPPORTED, "n_kv_heads %d exceeds one launch (65535)", cache->hkv);
+  p->len = cache->len[layer];
+  if (need_tokens) {
+    if (p->len == 0) return fail(KV_EEMPTY, "layer %d has no cached token", layer);
+    if (n_new < 1 || n_new > p->len)
+      return fail(KV_EINVAL, "n_new %lld must be in [1, len = %lld] (append the chunk first)", (long long)n_new,
+                  (long long)p->len);
+  } else if (n_new < 1) {
+    return fail(KV_EINVAL, "n_new must be >= 1");
+  }
+  p->group = n_q_heads / cache->hkv;
+  p->rows = n_new * p->group;
+  p->mtiles = ceil_div(p->rows, kChunkRows);
+  if (p->mtiles > 0x7fffffff) return fail(KV_EUNSUPPORTED, "chunk of %lld rows is too large", (long long)p->rows);
+  p->base = p->mtiles * cache->hkv;
+  p->slots = resident_slots(cache->device, chunk_kernel_for(cache->kbits, cache->vbits, cache->d, false),
+                            kChunkThreads);
+  return KV_OK;
+}
+
+void chunk_plan(const ChunkPrep& p, int* n_splits, int64_t* tps) {
+  plan_splits(p.base, p.slots, split_cap(p.base, p.slots, kMaxSplitsChunk), p.len, kChunkKeys,
+              kChunkMinKeysPerSplit, n_splits, tps);
+}
+
+int chunk_launch(kv_cache* cache, int layer, const ChunkPrep& p, const void* q, int q_dtype, int n_q_heads,
+                 int64_t n_new, float sm_scale, int n_splits, int64_t tps, bool partial, float* ws, float* out,
+                 hipStream_t st) {
+  ChunkArgs a;
+  memset(&a, 0, sizeof(a));
+  a.base = cache->arena + (int64_t)layer * cache->hkv * cache->g.region();
+  a.g = cache->g;
+  a.len = p.len;
+  a.n_new = n_new;
+  a.hkv = cache->hkv;
+  a.hq = n_q_heads;
+  a.group = p.group;
+  a.n_splits = n_splits;
+  a.partial = partial ? 1 : 0;
+  a.tps = tps;
+  a.q = q;
+  a.q_dtype = q_dtype;
+  a.qk_scale = sm_scale * 1.4426950408889634f;
+  a.ws = ws;
+  a.out = out;
+  hipError_t e = launch_chunk(a, cache->kbits, cache->vbits, cache->d, st);
+  if (e != hipSuccess) return hip_fail(cache, e, "chunk launch");
+  return KV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t kv_decode_workspace_bytes(kv_cache* const* sessions, int n_sessions, int layer, int n_q_heads) {
+  clear_err();
+  DecodePrep p;
+  int rc = decode_prepare(sessions, n_sessions, layer, n_q_heads, false, &p);
+  if (rc) return rc;
+  const int64_t cap = split_cap(p.base, p.slots, kMaxSplitsDecode);
   if (cap <= 1) return 0;
-  return (int64_t)n_sessions * n_q_heads * cap * (s0->d + 2) * (int64_t)sizeof(float);
+  return (int64_t)n_sessions * n_q_heads * cap * (p.d + 2) * (int64_t)sizeof(float);
+}
+
+int kv_decode_plan(kv_cache* const* sessions, int n_sessions, int layer, int n_q_heads, int* n_splits,
+                   int64_t* tokens_per_split) {
+  clear_err();
+  if (!n_splits || !tokens_per_split) return fail(KV_EINVAL, "n_splits and tokens_per_split must not be NULL");
+  DecodePrep p;
+  int rc = decode_prepare(sessions, n_sessions, layer, n_q_heads, true, &p);
+  if (rc) return rc;
+  decode_plan(p, n_splits, tokens_per_split);
+  return KV_OK;
 }
 
 int kv_attend_decode(kv_cache* const* sessions, int n_sessions, int layer, const void* q,
                      int q_dtype, int n_q_heads, float sm_scale, float* out, void* workspace,
                      size_t ws_bytes, void* stream) {
   clear_err();
-  int rc = check_sessions(sessions, n_sessions, layer);
+  DecodePrep p;
+  int rc = decode_prepare(sessions, n_sessions, layer, n_q_heads, true, &p);
   if (rc) return rc;
-  const kv_cache* s0 = sessions[0];
-  const int hkv = s0->hkv, d = s0->d;
-  if (n_q_heads < 1 || n_q_heads % hkv)
-    return fail(KV_EINVAL, "n_q_heads %d is not a positive multiple of n_kv_heads %d", n_q_heads, hkv);
-  const int group = n_q_heads / hkv;
-  const int gp = decode_group_pad(group);
-  if (gp < 0) return fail(KV_EUNSUPPORTED, "decode group size %d > 16 is not built", group);
-  if (!dtype_ok(q_dtype)) return fail(KV_EINVAL, "q_dtype %d is not one of KV_F32/KV_BF16/KV_F16", q_dtype);
-  if (!q || !out) return fail(KV_EINVAL, "q and out must not be NULL");
-  if (!aligned16(q) || !aligned16(out)) return fail(KV_EINVAL, "q and out must be 16-byte aligned");
-  int64_t max_len = 0;
-  for (int i = 0; i < n_sessions; ++i) {
-    if (sessions[i]->len[layer] == 0) return fail(KV_EEMPTY, "session %d has no cached token in layer %d", i, layer);
-    max_len = std::max(max_len, sessions[i]->len[layer]);
-  }
-  const int64_t base = (int64_t)n_sessions * hkv;
-  const int64_t slots = resident_slots(s0->device, decode_kernel_for(s0->kbits, s0->vbits, d, gp));
+  if ((rc = check_q_out(q, q_dtype, out, "out"))) return rc;
   int n_splits;
   int64_t tps;
-  plan_splits(base, slots, split_cap(base, slots, 1 << 20), max_len, kDecodeWaveTokens, kDecodeWaveTokens,
-              &n_splits, &tps);
-  int64_t need = n_splits > 1 ? (int64_t)n_sessions * n_q_heads * n_splits * (d + 2) * (int64_t)sizeof(float) : 0;
-  if ((int64_t)ws_bytes < need) return fail(KV_EINVAL, "workspace of %zu bytes is smaller than the %lld needed", ws_bytes, (long long)need);
-  if (need && (!workspace || !aligned16(workspace))) return fail(KV_EINVAL, "workspace must be a 16-byte aligned device pointer");
-
-  DecodeArgs a;
-  memset(&a, 0, sizeof(a));
-  a.hkv = hkv;
-  a.hq = n_q_heads;
-  a.group = group;
-  a.n_splits = n_splits;
-  a.tps = tps;
-  a.q = q;
-  a.q_dtype = q_dtype;
-  a.qk_scale = sm_scale * 1.4426950408889634f;
-  a.ws = static_cast<float*>(workspace);
-  a.out = out;
-  a.kc = s0->g.kc;
-  a.ks = s0->g.ks;
-  a.vc = s0->g.vc;
-  a.vs = s0->g.vs;
+  decode_plan(p, &n_splits, &tps);
+  const int64_t need = n_splits > 1 ? partial_bytes(n_sessions * (int64_t)n_q_heads, n_splits, p.d) : 0;
+  if ((rc = check_workspace(workspace, ws_bytes, need))) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  for (int b0 = 0; b0 < n_sessions; b0 += kMaxSessions) {
-    int nb = std::min(kMaxSessions, n_sessions - b0);
-    a.n_sess = nb;
-    a.sess0 = b0;
-    for (int i = 0; i < nb; ++i) {
-      const kv_cache* c = sessions[b0 + i];
-      a.sess[i].base = c->arena + (int64_t)layer * hkv * c->g.region();
-      a.sess[i].cap = c->g.cap;
-      a.sess[i].len = c->len[layer];
-    }
-    hipError_t e = launch_decode(a, s0->kbits, s0->vbits, d, gp, st);
-    if (e != hipSuccess) {
-      for (int i = 0; i < n_sessions; ++i) sessions[i]->poisoned = true;
-      return fail(KV_EHIP, "decode launch: %s", hipGetErrorString(e));
-    }
-  }
+  float* ws = static_cast<float*>(workspace);
+  if ((rc = decode_launch(sessions, n_sessions, layer, p, q, q_dtype, n_q_heads, sm_scale, n_splits, tps,
+                          n_splits > 1, ws, out, st)))
+    return rc;
   if (n_splits > 1) {
-    MergeArgs m;
-    m.ws = a.ws;
-    m.out = out;
-    m.rows = (int64_t)n_sessions * n_q_heads;
-    m.n_splits = n_splits;
-    m.d = d;
-    hipError_t e = launch_merge(m, st);
+    hipError_t e = merge_launch(ws, (int64_t)n_sessions * n_q_heads, n_splits, p.d, out, st);
     if (e != hipSuccess) {
       for (int i = 0; i < n_sessions; ++i) sessions[i]->poisoned = true;
       return fail(KV_EHIP, "merge launch: %s", hipGetErrorString(e));
@@ -452,83 +594,99 @@ int kv_attend_decode(kv_cache* const* sessions, int n_sessions, int layer, const
   return KV_OK;
 }
 
+int kv_attend_decode_partial(kv_cache* const* sessions, int n_sessions, int layer, const void* q,
+                             int q_dtype, int n_q_heads, float sm_scale, int n_splits,
+                             int64_t tokens_per_split, float* partials, size_t partials_bytes,
+                             void* stream) {
+  clear_err();
+  DecodePrep p;
+  int rc = decode_prepare(sessions, n_sessions, layer, n_q_heads, true, &p);
+  if (rc) return rc;
+  if ((rc = check_q_out(q, q_dtype, partials, "partials"))) return rc;
+  if ((rc = check_split(n_splits, tokens_per_split, kDecodeWaveTokens, p.max_len, "tokens_per_split"))) return rc;
+  const int64_t need = partial_bytes(n_sessions * (int64_t)n_q_heads, n_splits, p.d);
+  if ((int64_t)partials_bytes < need)
+    return fail(KV_EINVAL, "partials buffer of %zu bytes is smaller than the %lld needed", partials_bytes, (long long)need);
+  return decode_launch(sessions, n_sessions, layer, p, q, q_dtype, n_q_heads, sm_scale, n_splits,
+                       tokens_per_split, true, partials, nullptr, static_cast<hipStream_t>(stream));
+}
+
+int kv_merge_partials(const float* partials, int64_t rows, int n_splits, int head_dim, float* out,
+                      void* stream) {
+  clear_err();
+  if (rows < 0) return fail(KV_EINVAL, "rows must be >= 0 (got %lld)", (long long)rows);
+  if (n_splits < 1) return fail(KV_EINVAL, "n_splits must be >= 1 (got %d)", n_splits);
+  if (head_dim < 1 || head_dim > (1 << 20)) return fail(KV_EINVAL, "head_dim %d out of range", head_dim);
+  if (rows > (int64_t)4 * 0x7fffffff) return fail(KV_EUNSUPPORTED, "%lld rows exceed one launch", (long long)rows);
+  if (rows == 0) return KV_OK;
+  if (!partials || !out) return fail(KV_EINVAL, "partials and out must not be NULL");
+  if (!aligned16(partials) || !aligned16(out)) return fail(KV_EINVAL, "partials and out must be 16-byte aligned");
+  hipError_t e = merge_launch(partials, rows, n_splits, head_dim, out, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(KV_EHIP, "merge launch: %s", hipGetErrorString(e));
+  return KV_OK;
+}
+
 int64_t kv_chunk_workspace_bytes(const kv_cache* cache, int layer, int n_q_heads, int64_t n_new) {
   clear_err();
-  int rc = check_cache(cache);
+  ChunkPrep p;
+  int rc = chunk_prepare(cache, layer, n_q_heads, n_new, false, &p);
   if (rc) return rc;
-  if (layer < 0 || layer >= cache->n_layers) return fail(KV_EINVAL, "layer %d out of range", layer);
-  if (n_q_heads < 1 || n_q_heads % cache->hkv)
-    return fail(KV_EINVAL, "n_q_heads %d is not a positive multiple of n_kv_heads %d", n_q_heads, cache->hkv);
-  if (n_new < 1) return fail(KV_EINVAL, "n_new must be >= 1");
-  int64_t rows = n_new * (n_q_heads / cache->hkv);
-  int64_t base = ceil_div(rows, kChunkRows) * cache->hkv;
-  const int64_t slots = resident_slots(cache->device, chunk_kernel_for(cache->kbits, cache->vbits, cache->d, false),
-                                       kChunkThreads);
-  int64_t cap = split_cap(base, slots, kMaxSplitsChunk);
+  const int64_t cap = split_cap(p.base, p.slots, kMaxSplitsChunk);
   if (cap <= 1) return 0;
-  return n_new * n_q_heads * cap * (cache->d + 2) * (int64_t)sizeof(float);
+  return partial_bytes(n_new * n_q_heads, (int)cap, cache->d);
+}
+
+int kv_chunk_plan(const kv_cache* cache, int layer, int n_q_heads, int64_t n_new, int* n_splits,
+                  int64_t* keys_per_split) {
+  clear_err();
+  if (!n_splits || !keys_per_split) return fail(KV_EINVAL, "n_splits and keys_per_split must not be NULL");
+  ChunkPrep p;
+  int rc = chunk_prepare(cache, layer, n_q_heads, n_new, true, &p);
+  if (rc) return rc;
+  chunk_plan(p, n_splits, keys_per_split);
+  return KV_OK;
 }
 
 int kv_attend_chunk(kv_cache* cache, int layer, const void* q, int q_dtype, int n_q_heads,
                     int64_t n_new, float sm_scale, float* out, void* workspace, size_t ws_bytes,
                     void* stream) {
   clear_err();
-  int rc = check_cache(cache);
+  ChunkPrep p;
+  int rc = chunk_prepare(cache, layer, n_q_heads, n_new, true, &p);
   if (rc) return rc;
-  if (layer < 0 || layer >= cache->n_layers) return fail(KV_EINVAL, "layer %d out of range [0, %d)", layer, cache->n_layers);
-  if (n_q_heads < 1 || n_q_heads % cache->hkv)
-    return fail(KV_EINVAL, "n_q_heads %d is not a positive multiple of n_kv_heads %d", n_q_heads, cache->hkv);
-  if (!dtype_ok(q_dtype)) return fail(KV_EINVAL, "q_dtype %d is not one of KV_F32/KV_BF16/KV_F16", q_dtype);
-  const int64_t len = cache->len[layer];
-  if (len == 0) return fail(KV_EEMPTY, "layer %d has no cached token", layer);
-  if (n_new < 1 || n_new > len)
-    return fail(KV_EINVAL, "n_new %lld must be in [1, len = %lld] (append the chunk first)", (long long)n_new, (long long)len);
-  if (!q || !out) return fail(KV_EINVAL, "q and out must not be NULL");
-  if (!aligned16(q) || !aligned16(out)) return fail(KV_EINVAL, "q and out must be 16-byte aligned");
-  const int group = n_q_heads / cache->hkv;
-  const int64_t rows = n_new * group;
-  const int64_t mtiles = ceil_div(rows, kChunkRows);
-  if (mtiles > 0x7fffffff) return fail(KV_EUNSUPPORTED, "chunk of %lld rows is too large", (long long)rows);
-  const int64_t base = mtiles * cache->hkv;
-  const int64_t slots = resident_slots(cache->device, chunk_kernel_for(cache->kbits, cache->vbits, cache->d, false),
-                                       kChunkThreads);
+  if ((rc = check_q_out(q, q_dtype, out, "out"))) return rc;
   int n_splits;
   int64_t tps;
-  plan_splits(base, slots, split_cap(base, slots, kMaxSplitsChunk), len, kChunkKeys, kChunkMinKeysPerSplit,
-              &n_splits, &tps);
-  int64_t need = n_splits > 1 ? n_new * n_q_heads * n_splits * (cache->d + 2) * (int64_t)sizeof(float) : 0;
-  if ((int64_t)ws_bytes < need) return fail(KV_EINVAL, "workspace of %zu bytes is smaller than the %lld needed", ws_bytes, (long long)need);
-  if (need && (!workspace || !aligned16(workspace))) return fail(KV_EINVAL, "workspace must be a 16-byte aligned device pointer");
-
-  ChunkArgs a;
-  a.base = cache->arena + (int64_t)layer * cache->hkv * cache->g.region();
-  a.g = cache->g;
-  a.len = len;
-  a.n_new = n_new;
-  a.hkv = cache->hkv;
-  a.hq = n_q_heads;
-  a.group = group;
-  a.n_splits = n_splits;
-  a.tps = tps;
-  a.q = q;
-  a.q_dtype = q_dtype;
-  a.qk_scale = sm_scale * 1.4426950408889634f;
-  a.ws = static_cast<float*>(workspace);
-  a.out = out;
+  chunk_plan(p, &n_splits, &tps);
+  const int64_t need = n_splits > 1 ? partial_bytes(n_new * n_q_heads, n_splits, cache->d) : 0;
+  if ((rc = check_workspace(workspace, ws_bytes, need))) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = launch_chunk(a, cache->kbits, cache->vbits, cache->d, st);
-  if (e != hipSuccess) return hip_fail(cache, e, "chunk launch");
+  float* ws = static_cast<float*>(workspace);
+  if ((rc = chunk_launch(cache, layer, p, q, q_dtype, n_q_heads, n_new, sm_scale, n_splits, tps, n_splits > 1, ws,
+                         out, st)))
+    return rc;
   if (n_splits > 1) {
-    MergeArgs m;
-    m.ws = a.ws;
-    m.out = out;
-    m.rows = n_new * n_q_heads;
-    m.n_splits = n_splits;
-    m.d = cache->d;
-    e = launch_merge(m, st);
+    hipError_t e = merge_launch(ws, n_new * n_q_heads, n_splits, cache->d, out, st);
     if (e != hipSuccess) return hip_fail(cache, e, "merge launch");
   }
   return KV_OK;
+}
+
+int kv_attend_chunk_partial(kv_cache* cache, int layer, const void* q, int q_dtype, int n_q_heads,
+                            int64_t n_new, float sm_scale, int n_splits, int64_t keys_per_split,
+                            float* partials, size_t partials_bytes, void* stream) {
+  clear_err();
+  ChunkPrep p;
+  int rc = chunk_prepare(cache, layer, n_q_heads, n_new, true, &p);
+  if (rc) return rc;
+  if ((rc = check_q_out(q, q_dtype, partials, "partials"))) return rc;
+  if ((rc = check_split(n_splits, keys_per_split, kChunkKeys, p.len, "keys_per_split"))) return rc;
+  if (n_splits > 65535) return fail(KV_EUNSUPPORTED, "n_splits %d exceeds one launch (65535)", n_splits);
+  const int64_t need = partial_bytes(n_new * n_q_heads, n_splits, cache->d);
+  if ((int64_t)partials_bytes < need)
+    return fail(KV_EINVAL, "partials buffer of %zu bytes is smaller than the %lld needed", partials_bytes, (long long)need);
+  return chunk_launch(cache, layer, p, q, q_dtype, n_q_heads, n_new, sm_scale, n_splits, keys_per_split, true,
+                      partials, nullptr, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

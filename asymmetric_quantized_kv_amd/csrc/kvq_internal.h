@@ -55,12 +55,13 @@ struct DecodeArgs {
   int sess0;              // global index of sess[0] (rows of q / out / workspace)
   int hkv, hq, group;
   int n_splits;
+  int partial;            // 1: write (o, m, l) partials to ws; 0: normalized out (n_splits == 1)
   int64_t tps;            // tokens per split, multiple of kDecodeWaveTokens
   const void* q;
   int q_dtype;
   float qk_scale;         // sm_scale * log2(e)
-  float* ws;              // [S][Hq][n_splits][D + 2] partials when n_splits > 1
-  float* out;             // [S][Hq][D] when n_splits == 1
+  float* ws;              // [S][Hq][n_splits][D + 2] partials when partial
+  float* out;             // [S][Hq][D] otherwise
   int32_t kc, ks, vc, vs; // row bytes (shared by all sessions)
 };
 
@@ -71,12 +72,13 @@ struct ChunkArgs {
   int64_t n_new;
   int hkv, hq, group;
   int n_splits;
+  int partial;            // 1: write (o, m, l) partials to ws; 0: normalized out (n_splits == 1)
   int64_t tps;            // keys per split, multiple of kChunkKeys
   const void* q;
   int q_dtype;
   float qk_scale;
-  float* ws;              // [n_new][Hq][n_splits][D + 2] partials when n_splits > 1
-  float* out;             // [n_new][Hq][D] when n_splits == 1
+  float* ws;              // [n_new][Hq][n_splits][D + 2] partials when partial
+  float* out;             // [n_new][Hq][D] otherwise
 };
 
 struct MergeArgs {

@@ -112,8 +112,8 @@ def main():
     dec_bytes = sum(kvq.kv_footprint_bytes(h) for h in caches["K8V4"])   # every row is cached
     sm = D ** -0.5
     out_dec = torch.empty((DEC_S, DEC_HQ, D), dtype=torch.float32, device=dev)
-    ws_dec = torch.empty(max(16, kvq.kv_decode_workspace_bytes(caches["K8V4"], 0, DEC_HQ)), dtype=torch.uint8,
-                         device=dev)
+    ws_dec = torch.empty(max([16] + [kvq.kv_decode_workspace_bytes(caches[L], 0, DEC_HQ) for L in layouts]),
+                         dtype=torch.uint8, device=dev)
 
     # ---- turn workload -------------------------------------------------------------
     c3 = I.config3()
@@ -129,48 +129,84 @@ def main():
     torch.cuda.synchronize()
     log(f"turn cache ready ({time.time() - t0:.1f} s)")
 
+    # The library's own split plans; the two passes of each attention are called one by
+    # one (kv_attend_*_partial, then kv_merge_partials) so that events between them time
+    # the partial kernels alone.  A one-split plan is the one-call path (no merge).
+    dec_plan = kvq.kv_decode_plan(caches["K8V4"], 0, DEC_HQ)
+    turn_plan = kvq.kv_chunk_plan(h3, 0, TURN_HQ, TURN_NEW)
+    log(f"plans: decode {dec_plan[0]} x {dec_plan[1]} tokens, chunk {turn_plan[0]} x {turn_plan[1]} keys")
+    part_dec = torch.empty((DEC_S, DEC_HQ, dec_plan[0], D + 2), dtype=torch.float32, device=dev)
+    part_turn = torch.empty((TURN_NEW, TURN_HQ, turn_plan[0], D + 2), dtype=torch.float32, device=dev)
+
+    def decode_pass1():
+        if dec_plan[0] == 1:
+            kvq.kv_attend_decode(caches["K8V4"], 0, q_dec, sm, out=out_dec, workspace=ws_dec)
+        else:
+            kvq.kv_attend_decode_partial(caches["K8V4"], 0, q_dec, sm, dec_plan[0], dec_plan[1], partials=part_dec)
+
+    def decode_pass2():
+        if dec_plan[0] > 1:
+            kvq.kv_merge_partials(part_dec, out=out_dec)
+
     def decode(L="K8V4"):
-        kvq.kv_attend_decode(caches[L], 0, q_dec, sm, out=out_dec, workspace=ws_dec)
+        if L != "K8V4":          # the one-call path under its own plan
+            kvq.kv_attend_decode(caches[L], 0, q_dec, sm, out=out_dec, workspace=ws_dec)
+            return
+        decode_pass1()
+        decode_pass2()
 
     def turn_append():
         kvq.kv_cache_truncate(h3, 0, TURN_CTX)
         kvq.kv_append_quant(h3, 0, k_new, v_new)
 
-    def turn_attend():
-        kvq.kv_attend_chunk(h3, 0, q_new, TURN_NEW, sm, out=out_turn, workspace=ws_turn)
+    def turn_pass1():
+        if turn_plan[0] == 1:
+            kvq.kv_attend_chunk(h3, 0, q_new, TURN_NEW, sm, out=out_turn, workspace=ws_turn)
+        else:
+            kvq.kv_attend_chunk_partial(h3, 0, q_new, TURN_NEW, sm, turn_plan[0], turn_plan[1], partials=part_turn)
+
+    def turn_pass2():
+        if turn_plan[0] > 1:
+            kvq.kv_merge_partials(part_turn, out=out_turn)
 
     for _ in range(args.warmup):
         decode()
         turn_append()
-        turn_attend()
+        turn_pass1()
+        turn_pass2()
     torch.cuda.synchronize()
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     for i in range(args.steps):
         ev[i][0].record(stream)
-        decode()
+        decode_pass1()
         ev[i][1].record(stream)
-        turn_append()
+        decode_pass2()
         ev[i][2].record(stream)
-        turn_attend()
+        turn_append()
         ev[i][3].record(stream)
+        turn_pass1()
+        ev[i][4].record(stream)
+        turn_pass2()
+        ev[i][5].record(stream)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - w0) * 1e3
-    dec_ms = [e[0].elapsed_time(e[1]) for e in ev]
-    app_ms = [e[1].elapsed_time(e[2]) for e in ev]
-    chk_ms = [e[2].elapsed_time(e[3]) for e in ev]
     mean = lambda xs: sum(xs) / len(xs)
-    dec_t, app_t, chk_t = mean(dec_ms), mean(app_ms), mean(chk_ms)
-    dec_gbps = dec_bytes / (dec_t * 1e-3) / 1e9
+    seg = [mean([e[j].elapsed_time(e[j + 1]) for e in ev]) for j in range(5)]
+    dec1_t, dec2_t, app_t, chk1_t, chk2_t = seg
+    dec_t, chk_t = dec1_t + dec2_t, chk1_t + chk2_t
+    dec_gbps = dec_bytes / (dec_t * 1e-3) / 1e9              # whole decode (both passes)
+    dec1_gbps = dec_bytes / (dec1_t * 1e-3) / 1e9            # the partial kernel alone
     turn_tok_s = TURN_NEW / ((app_t + chk_t) * 1e-3)
     # causal pairs of the turn: query j (position TURN_CTX + j) sees TURN_CTX + j + 1 keys
     pairs = TURN_HQ * sum(TURN_CTX + j + 1 for j in range(TURN_NEW))
     chunk_flop = 4.0 * D * pairs
-    chunk_tflops = chunk_flop / (chk_t * 1e-3) / 1e12
-    log(f"decode {dec_t:.4f} ms ({dec_gbps:.1f} GB/s), append {app_t:.4f} ms, chunk {chk_t:.4f} ms "
-        f"({chunk_tflops:.1f} TFLOP/s), wall {wall_ms / args.steps:.3f} ms/step")
+    chunk_tflops = chunk_flop / (chk1_t * 1e-3) / 1e12       # the chunk kernel alone
+    log(f"decode {dec_t:.4f} ms = partial {dec1_t:.4f} + merge {dec2_t:.4f} ({dec_gbps:.1f} GB/s; "
+        f"partial kernel {dec1_gbps:.1f} GB/s), append {app_t:.4f} ms, chunk {chk_t:.4f} ms = kernel "
+        f"{chk1_t:.4f} ({chunk_tflops:.1f} TFLOP/s) + merge {chk2_t:.4f}, wall {wall_ms / args.steps:.3f} ms/step")
 
     extra = {}
     if "K4V8" in layouts:
@@ -221,15 +257,21 @@ def main():
         "hbm_frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
         "chunk_append_tokens_per_s": round(turn_tok_s, 1),
         "decode_ms": round(dec_t, 4),
+        "decode_partial_ms": round(dec1_t, 4),
+        "decode_merge_ms": round(dec2_t, 4),
         "append_ms": round(app_t, 4),
         "chunk_ms": round(chk_t, 4),
+        "chunk_kernel_ms": round(chk1_t, 4),
+        "chunk_merge_ms": round(chk2_t, 4),
+        "decode_plan": {"n_splits": dec_plan[0], "tokens_per_split": dec_plan[1]},
+        "chunk_plan": {"n_splits": turn_plan[0], "keys_per_split": turn_plan[1]},
         "roofline": {
-            "bound": "hbm", "kernel": "decode (partial pass + split merge)",
-            "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": load_traffic("decode_k8v4"),
+            "bound": "hbm", "kernel": "decode_kernel<8,4,128,4,16> (split-K partial pass)",
+            "achieved": round(dec1_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(dec1_gbps / HBM_PEAK_GBPS, 4), "traffic": load_traffic("decode_k8v4"),
         },
         "roofline_chunk": {
-            "bound": "mfma", "kernel": "chunk prefill (+ split merge)",
+            "bound": "mfma", "kernel": "chunk_kernel<8,4,128> (bf16 queries)",
             "achieved": round(chunk_tflops, 1), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(chunk_tflops / MFMA_F16_PEAK_TFLOPS, 4), "traffic": load_traffic("chunk_k8v4"),
         },

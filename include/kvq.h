@@ -114,6 +114,45 @@ int kv_attend_decode(kv_cache* const* sessions, int n_sessions, int layer, const
 int64_t kv_decode_workspace_bytes(kv_cache* const* sessions, int n_sessions, int layer,
                                   int n_q_heads);
 
+/* The two passes of kv_attend_decode, callable one by one (to time or overlap them, or to
+ * merge partials computed elsewhere, e.g. on several devices).
+ *
+ * kv_decode_plan: the split kv_attend_decode uses for these sessions -- the context is cut
+ * into *n_splits ranges of *tokens_per_split tokens (a multiple of 512) covering the
+ * longest session.  Errors as kv_attend_decode (KV_EEMPTY for an empty session).
+ *
+ * kv_attend_decode_partial: the first pass alone, with a split of the caller's choice
+ * (n_splits >= 1; tokens_per_split a positive multiple of 512 with n_splits *
+ * tokens_per_split >= the longest session).  Split s of session b covers tokens
+ * [s * tokens_per_split, min((s + 1) * tokens_per_split, len_b)).  Writes, per row
+ * r = b * n_q_heads + h and split s, partials[(r * n_splits + s) * (head_dim + 2) + i]:
+ *   i <  head_dim:  o_i = sum_t 2^(x_t - m) v_t,i   (not normalized)
+ *   i == head_dim:  m,  the running max, max_t x_t - 8 <= m <= max_t x_t
+ *   i == head_dim+1: l = sum_t 2^(x_t - m)
+ * with x_t = sm_scale * log2(e) * q . k_t (base-2 units).  (o, m, l) is unique only up to
+ * the common rescale m -> m', o, l -> o, l * 2^(m - m'); o / l and m + log2(l) are not.
+ * A split with no token has m = -inf, l = 0, o = 0.  partials: device fp32 of at least
+ * n_sessions * n_q_heads * n_splits * (head_dim + 2) * 4 bytes (partials_bytes).
+ * The merge (below) of these partials is the attention of kv_attend_decode.
+ * (The log-sum-exp recombination of softmax sums over disjoint key ranges; the pages
+ * do not discuss splitting, which is an implementation choice for long contexts.) */
+int kv_decode_plan(kv_cache* const* sessions, int n_sessions, int layer, int n_q_heads,
+                   int* n_splits, int64_t* tokens_per_split);
+int kv_attend_decode_partial(kv_cache* const* sessions, int n_sessions, int layer,
+                             const void* q, int q_dtype, int n_q_heads, float sm_scale,
+                             int n_splits, int64_t tokens_per_split, float* partials,
+                             size_t partials_bytes, void* stream);
+
+/* Second pass: out[r][i] = sum_s 2^(m_s - M) o_s,i / sum_s 2^(m_s - M) l_s with
+ * M = max_s m_s over the n_splits partials of row r (layout as above); splits with
+ * m = -inf drop out.  partials: device fp32 [rows][n_splits][head_dim + 2]; out: device
+ * fp32 [rows][head_dim].  rows == 0 is a no-op.  The weights 2^(m_s - M) are fp32: a
+ * split with m_s < M - 126 weighs nothing, which is exact to fp32 rounding for partials
+ * as the partial passes write them (l >= 2^-8, |o_i| <= l max|v|).  Errors: KV_EINVAL
+ * (null or misaligned pointers, n_splits < 1, head_dim out of range), KV_EHIP. */
+int kv_merge_partials(const float* partials, int64_t rows, int n_splits, int head_dim,
+                      float* out, void* stream);
+
 /* Causal attention of the last n_new cached positions of `layer` (the turn just
  * appended) against everything cached so far: only the new tokens are processed
  * (openclawradar.com page, section "Principais Descobertas e Benchmarks").
@@ -130,6 +169,22 @@ int kv_attend_chunk(kv_cache* cache, int layer, const void* q, int q_dtype, int 
 /* Workspace bytes kv_attend_chunk needs; < 0 on bad arguments. */
 int64_t kv_chunk_workspace_bytes(const kv_cache* cache, int layer, int n_q_heads,
                                  int64_t n_new);
+
+/* The two passes of kv_attend_chunk, callable one by one.
+ * kv_chunk_plan: the split kv_attend_chunk uses -- the cached keys [0, len) are cut into
+ * *n_splits ranges of *keys_per_split keys (a multiple of 64).
+ * kv_attend_chunk_partial: the first pass with a split of the caller's choice
+ * (1 <= n_splits <= 65535; keys_per_split a positive multiple of 64 with n_splits *
+ * keys_per_split >= len).  Query row j sees the keys of split s that are also in
+ * [0, len - n_new + j].  Partials as for kv_attend_decode_partial with rows
+ * r = j * n_q_heads + h; a row that sees no key of a split gets m = -inf, l = 0, o = 0.
+ * kv_merge_partials turns them into the output of kv_attend_chunk. */
+int kv_chunk_plan(const kv_cache* cache, int layer, int n_q_heads, int64_t n_new,
+                  int* n_splits, int64_t* keys_per_split);
+int kv_attend_chunk_partial(kv_cache* cache, int layer, const void* q, int q_dtype,
+                            int n_q_heads, int64_t n_new, float sm_scale, int n_splits,
+                            int64_t keys_per_split, float* partials, size_t partials_bytes,
+                            void* stream);
 
 /* Device bytes of all planes: n_layers * n_kv_heads * cap * (K row + V row), the footprint
  * the KVSplit page tabulates (section "Uso de memoria conforme o comprimento da sequencia").

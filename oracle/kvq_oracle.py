@@ -28,6 +28,9 @@ What it computes, and where the pages say so
   Benchmarks".
 * Attention itself is the plain definition softmax(sigma * q.K^T) V, in fp64,
   over the dequantized cache.
+* The same attention in two passes (per-range partial softmax sums over disjoint
+  key ranges, then their log-sum-exp merge) is the exact identity the split
+  kernels rely on; the pages do not discuss splitting.
 
 Conventions fixed here (readings where the pages are silent; each is listed
 in the design notes of the repository):
@@ -52,6 +55,7 @@ __all__ = [
     "block_scale", "rhaz", "quantize_rows", "pack_codes", "unpack_codes",
     "pack_scales", "unpack_scales", "encode_rows", "dequant_rows", "OracleCache",
     "attend_decode", "attend_chunk", "attention_exact", "to_f32",
+    "split_partial", "merge_partials", "decode_partials", "chunk_partials", "LOG2E",
 ]
 
 #: layout id -> (name, key bits, value bits).  16 means the fp16 control.
@@ -314,3 +318,88 @@ def attend_chunk(cache: OracleCache, layer: int, q, n_new: int, sm_scale: float,
             o = (w @ vh) / w.sum(axis=1, keepdims=True)
             out[b0:b0 + len(rb), h * g:(h + 1) * g] = o.reshape(len(rb), g, dim)
     return out
+
+
+# --------------------------------------------------------------------------
+# attention in two passes: per-split partial sums and their merge (fp64)
+# --------------------------------------------------------------------------
+# Splitting the keys into disjoint ranges and recombining the per-range softmax sums
+# is exact: with x_t the score of key t in base-2 units, sum_t 2^x_t v_t and
+# sum_t 2^x_t are sums over the ranges, each kept relative to its own reference m.
+# The pages do not discuss it; it is how a long context is spread over workgroups
+# (or devices), and the library exposes both passes.
+LOG2E = 1.4426950408889634
+
+
+def split_partial(q, keys, values, sm_scale: float):
+    """(o, m, l) of query rows q [r, D] over one key range keys/values [n, D].
+
+    x_t = sm_scale * log2(e) * q . k_t;  m = max_t x_t;  l = sum_t 2^(x_t - m);
+    o = sum_t 2^(x_t - m) v_t.  An empty range gives m = -inf, l = 0, o = 0.
+    """
+    q64 = np.asarray(q, dtype=np.float64)
+    r, dim = q64.shape
+    keys = np.asarray(keys, dtype=np.float64)
+    if keys.shape[0] == 0:
+        return np.zeros((r, dim)), np.full(r, -np.inf), np.zeros(r)
+    x = (sm_scale * LOG2E) * (q64 @ keys.T)
+    m = x.max(axis=1)
+    w = np.exp2(x - m[:, None])
+    return w @ np.asarray(values, dtype=np.float64), m, w.sum(axis=1)
+
+
+def merge_partials(o, m, l):
+    """Normalized output from split partials o [.., S, D], m [.., S], l [.., S]:
+    M = max_s m_s, o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s; splits with
+    m = -inf (no key) weigh nothing."""
+    o, m, l = (np.asarray(a, dtype=np.float64) for a in (o, m, l))
+    big = m.max(axis=-1, keepdims=True)
+    w = np.where(np.isneginf(m), 0.0, np.exp2(m - np.where(np.isneginf(big), 0.0, big)))
+    return (w[..., None] * o).sum(axis=-2) / (w * l).sum(axis=-1)[..., None]
+
+
+def decode_partials(caches, layer: int, q, sm_scale: float, n_splits: int, per_split: int):
+    """Per session, q head and split s (tokens [s * per_split, min((s + 1) * per_split, len))):
+    (o [S, Hq, n_splits, D], m [S, Hq, n_splits], l [S, Hq, n_splits])."""
+    q = to_f32(q)
+    n_s, hq, dim = q.shape
+    o = np.zeros((n_s, hq, n_splits, dim))
+    m = np.full((n_s, hq, n_splits), -np.inf)
+    l = np.zeros((n_s, hq, n_splits))
+    for b, c in enumerate(caches):
+        g = hq // c.Hkv
+        total = c.len[layer]
+        for h in range(c.Hkv):
+            kh, vh = c.keys(layer, h), c.values(layer, h)
+            for sp in range(n_splits):
+                a, e = min(sp * per_split, total), min((sp + 1) * per_split, total)
+                o[b, h * g:(h + 1) * g, sp], m[b, h * g:(h + 1) * g, sp], l[b, h * g:(h + 1) * g, sp] = \
+                    split_partial(q[b, h * g:(h + 1) * g], kh[a:e], vh[a:e], sm_scale)
+    return o, m, l
+
+
+def chunk_partials(cache: OracleCache, layer: int, q, n_new: int, sm_scale: float, n_splits: int,
+                   per_split: int, rows=None):
+    """Per new token j (position len - n_new + j), q head and split s: the partials over the
+    keys of [s * per_split, (s + 1) * per_split) that j sees (t <= its position).
+    ``rows`` restricts the computation to those tokens.  Shapes as decode_partials with
+    the token index first."""
+    q = to_f32(q)
+    total = cache.len[layer]
+    if not 0 < n_new <= total:
+        raise ValueError("chunk must already be appended")
+    rows = np.arange(n_new) if rows is None else np.asarray(rows)
+    hq, dim = q.shape[1], q.shape[2]
+    g = hq // cache.Hkv
+    o = np.zeros((len(rows), hq, n_splits, dim))
+    m = np.full((len(rows), hq, n_splits), -np.inf)
+    l = np.zeros((len(rows), hq, n_splits))
+    for h in range(cache.Hkv):
+        kh, vh = cache.keys(layer, h, total), cache.values(layer, h, total)
+        for i, j in enumerate(rows):
+            end = total - n_new + int(j) + 1                    # keys [0, end) are visible
+            for sp in range(n_splits):
+                a, e = min(sp * per_split, end), min((sp + 1) * per_split, end)
+                o[i, h * g:(h + 1) * g, sp], m[i, h * g:(h + 1) * g, sp], l[i, h * g:(h + 1) * g, sp] = \
+                    split_partial(q[j, h * g:(h + 1) * g], kh[a:e], vh[a:e], sm_scale)
+    return o, m, l

@@ -78,6 +78,23 @@ def test_null_handles_are_rejected(built_library):
     assert L.kv_attend_decode(None, 1, 0, None, 0, 4, 0.1, None, None, 0, None) == kvq.KV_EINVAL
     assert L.kv_attend_chunk(None, 0, None, 0, 4, 1, 0.1, None, None, 0, None) == kvq.KV_EINVAL
     assert L.kv_footprint_bytes(None) == kvq.KV_EINVAL
+    n, t = C.c_int(), C.c_int64()
+    assert L.kv_decode_plan(None, 1, 0, 4, C.byref(n), C.byref(t)) == kvq.KV_EINVAL
+    assert L.kv_chunk_plan(None, 0, 4, 1, C.byref(n), C.byref(t)) == kvq.KV_EINVAL
+    assert L.kv_attend_decode_partial(None, 1, 0, None, 0, 4, 0.1, 1, 512, None, 0, None) == kvq.KV_EINVAL
+    assert L.kv_attend_chunk_partial(None, 0, None, 0, 4, 1, 0.1, 1, 64, None, 0, None) == kvq.KV_EINVAL
+
+
+def test_merge_checks_arguments_on_the_host(built_library):
+    L = built_library
+    assert L.kv_merge_partials(None, 0, 1, 64, None, None) == kvq.KV_OK          # nothing to merge
+    assert L.kv_merge_partials(None, 4, 1, 64, None, None) == kvq.KV_EINVAL      # null buffers
+    assert L.kv_merge_partials(None, 4, 0, 64, None, None) == kvq.KV_EINVAL      # no split
+    assert "n_splits" in kvq.kv_last_error()
+    assert L.kv_merge_partials(None, -1, 1, 64, None, None) == kvq.KV_EINVAL     # negative rows
+    assert L.kv_merge_partials(None, 4, 1, 0, None, None) == kvq.KV_EINVAL       # head_dim
+    assert L.kv_merge_partials(C.c_void_p(8), 4, 1, 64, C.c_void_p(24), None) == kvq.KV_EINVAL  # misaligned
+    assert "aligned" in kvq.kv_last_error()
     assert L.kv_cache_len(None, 0) == kvq.KV_EINVAL
     assert L.kv_cache_reset(None) == kvq.KV_EINVAL
     assert L.kv_cache_truncate(None, 0, 0) == kvq.KV_EINVAL

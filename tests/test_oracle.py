@@ -411,3 +411,92 @@ def test_decode_rejects_empty_cache():
     c = O.OracleCache(2, 1, 1, 64, 10)
     with pytest.raises(ValueError):
         O.attend_decode([c], 0, np.zeros((1, 1, 64), np.float32), 0.125)
+
+
+# ---------------------------------------------------------------------------
+# two-pass attention: split partials and their merge
+# ---------------------------------------------------------------------------
+def brute_partial(q, keys, values, scale):
+    """Python-loop (o, m, l) of one query row over a key range, base-2 scores."""
+    if not keys:
+        return [0.0] * len(q), -math.inf, 0.0
+    xs = [scale * math.log2(math.e) * math.fsum(a * b for a, b in zip(q, k)) for k in keys]
+    m = max(xs)
+    ws = [2.0 ** (x - m) for x in xs]
+    o = [math.fsum(w * v[i] for w, v in zip(ws, values)) for i in range(len(q))]
+    return o, m, math.fsum(ws)
+
+
+def test_split_partial_matches_bruteforce():
+    k, v, q = I.workload_small(31, 9, 1, 64, 2, 1)
+    c = O.OracleCache(2, 1, 1, 64, 9)
+    c.append(0, k, v)
+    kh, vh = c.keys(0, 0), c.values(0, 0)
+    for a, e in [(0, 9), (2, 5), (8, 9), (4, 4)]:
+        o, m, l = O.split_partial(q[0].astype(np.float64), kh[a:e], vh[a:e], 0.2)
+        for h in range(2):
+            bo, bm, bl = brute_partial(q[0, h].astype(float).tolist(), kh[a:e].tolist(), vh[a:e].tolist(), 0.2)
+            assert m[h] == bm if math.isinf(bm) else abs(m[h] - bm) <= 1e-12
+            assert abs(l[h] - bl) <= 1e-12 and np.max(np.abs(o[h] - bo)) <= 1e-12
+
+
+def test_split_partial_closed_forms():
+    """One key: o = v, l = 1, m = its score.  Two keys: m = the larger score,
+    l = 1 + 2^-|x1 - x2|, o = v_max + 2^-|x1 - x2| v_min.  No key: (0, -inf, 0)."""
+    q = np.array([[1.0, -2.0, 0.5, 0.0]])
+    k = np.array([[0.5, 0.25, -1.0, 3.0], [2.0, -1.0, 0.0, 1.0]])
+    v = np.array([[1.0, 2.0, 3.0, 4.0], [-1.0, 0.0, 1.0, 8.0]])
+    x = 0.5 * O.LOG2E * (q @ k.T)[0]
+    o, m, l = O.split_partial(q, k[:1], v[:1], 0.5)
+    assert np.array_equal(o[0], v[0]) and l[0] == 1.0 and abs(m[0] - x[0]) <= 1e-15
+    o, m, l = O.split_partial(q, k, v, 0.5)
+    hi, lo = (1, 0) if x[1] > x[0] else (0, 1)
+    r = 2.0 ** -(abs(x[1] - x[0]))
+    assert m[0] == x[hi] and abs(l[0] - (1 + r)) <= 1e-15
+    assert np.max(np.abs(o[0] - (v[hi] + r * v[lo]))) <= 1e-14
+    o, m, l = O.split_partial(q, k[:0], v[:0], 0.5)
+    assert m[0] == -np.inf and l[0] == 0 and not o.any()
+
+
+@pytest.mark.parametrize("layout", [0, 2, 3])
+def test_decode_partials_merge_to_attention(layout):
+    """Merging the partials of any cut of the context into ranges gives the attention
+    over the whole context (the identity the split kernels rely on); ranges past the
+    end are empty and weigh nothing."""
+    k, v, q = I.workload_small(32, 300, 2, 64, 8, 2)
+    caches = []
+    for b in range(2):
+        c = O.OracleCache(layout, 1, 2, 64, 300)
+        c.append(0, k[: 300 - 77 * b], v[: 300 - 77 * b])      # ragged lengths
+        caches.append(c)
+    want = O.attend_decode(caches, 0, q, 0.125)
+    for n_splits, per in [(1, 512), (3, 128), (5, 64), (7, 64), (2, 1024)]:
+        o, m, l = O.decode_partials(caches, 0, q, 0.125, n_splits, per)
+        got = O.merge_partials(o, m, l)
+        assert np.max(np.abs(got - want)) <= 1e-12, (n_splits, per)
+        empty = np.arange(n_splits) * per >= 223
+        assert np.all(np.isneginf(m[1][:, empty])) and not l[1][:, empty].any()
+
+
+def test_chunk_partials_merge_to_chunk_attention():
+    k, v, q = I.workload_small(33, 200, 2, 64, 6, 40)
+    c = O.OracleCache(2, 1, 2, 64, 200)
+    c.append(0, k, v)
+    want = O.attend_chunk(c, 0, q, 40, 0.125)
+    for n_splits, per in [(1, 256), (4, 64), (16, 64)]:
+        o, m, l = O.chunk_partials(c, 0, q, 40, 0.125, n_splits, per)
+        assert np.max(np.abs(O.merge_partials(o, m, l) - want)) <= 1e-12
+    # token 0 (position 160) sees keys [0, 161): the 4th split of 64 ([192, 256)) is empty for it
+    o, m, l = O.chunk_partials(c, 0, q, 40, 0.125, 4, 64, rows=[0, 39])
+    assert np.all(np.isneginf(m[0, :, 3])) and np.all(np.isfinite(m[1, :, 3]))
+
+
+def test_merge_is_invariant_to_the_reference_of_each_split():
+    """(o, m, l) and (o 2^c, m - c, l 2^c) describe the same split: the merge agrees."""
+    k, v, q = I.workload_small(34, 150, 1, 64, 2, 1)
+    c = O.OracleCache(2, 1, 1, 64, 150)
+    c.append(0, k, v)
+    o, m, l = O.decode_partials([c], 0, q, 0.125, 3, 64)
+    shift = np.array([0.0, 3.5, -7.0])
+    got = O.merge_partials(o * np.exp2(shift)[..., None], m - shift, l * np.exp2(shift))
+    assert np.max(np.abs(got - O.merge_partials(o, m, l))) <= 1e-12
