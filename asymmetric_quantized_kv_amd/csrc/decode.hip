@@ -12,9 +12,11 @@
 // elements of a token belong to one lane (LPT lanes per token), and each lane holds
 // two tokens per step, t and t + 64 / LPT.  A chunk is processed in three phases:
 //   A  scores: integer dot products (v_dot4_i32_i8) of the 8/4-bit key codes with the
-//      query split into two int8 digits, or fp16 dot2 for the fp16 control; partial
-//      sums are reduced over the LPT lanes with DPP;
-//   B  one lane per token: exact running max of the chunk per query head, p = 2^(s-m),
+//      query (one scale per head) split into two int8 digits, or fp16 dot2 for the fp16
+//      control; the lanes of one block add their integers, scale by the block's d, and
+//      the block sums are reduced over the LPT lanes with DPP;
+//   B  one lane per token: the query's scale turns the raw score into a base-2 logit;
+//      exact running max of the chunk per query head, p = 2^(s-m),
 //      the accumulators rescaled only when the max moved;
 //   C  values: v_dot2_f32_f16 over the token pair with weights w = p*d in fp16 and
 //      the value codes laid into fp16 subnormal bit patterns (u * 2^-24), so that no
@@ -23,6 +25,10 @@
 // writes either the normalized output (one split) or (o, m, l) for the merge kernel.
 #include "kvq_internal.h"
 #include "wave_ops.h"
+
+#ifndef KVQ_DECODE_DEPTH
+#define KVQ_DECODE_DEPTH 4   // steps of key/value codes requested ahead of the one computing
+#endif
 
 namespace kvq {
 namespace {
@@ -38,21 +44,61 @@ __device__ __forceinline__ half2_t pack_rne(float a, float b) {
   return r;
 }
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Buffer resource over `bytes` bytes at p (raw, byte-addressed); loads through it take a
+// per-lane 32-bit offset and a wave-uniform offset, so addresses cost no vector ALU.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint8_t* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p), 0, (int)bytes, 0x00020000);
+}
+
 template <int W>
-__device__ __forceinline__ void load_dwords(const uint8_t* p, uint32_t (&o)[W]) {
+__device__ __forceinline__ void buf_dwords(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint32_t (&o)[W]) {
   if constexpr (W % 4 == 0) {
 #pragma unroll
     for (int i = 0; i < W / 4; ++i) {
-      uint4 t = reinterpret_cast<const uint4*>(p)[i];
+      const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(r, (int)(voff + 16 * i), (int)soff, 0);
       o[4 * i] = t.x; o[4 * i + 1] = t.y; o[4 * i + 2] = t.z; o[4 * i + 3] = t.w;
     }
   } else if constexpr (W == 2) {
-    uint2 t = *reinterpret_cast<const uint2*>(p);
+    const u32x2 t = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0);
     o[0] = t.x; o[1] = t.y;
   } else {
     static_assert(W == 1, "dword count");
-    o[0] = *reinterpret_cast<const uint32_t*>(p);
+    o[0] = __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
   }
+}
+
+__device__ __forceinline__ uint16_t buf_u16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, (int)soff, 0);
+}
+
+// a . b over four signed bytes, starting a new sum (the VOP3 form takes the zero as an
+// inline constant; the accumulating two-operand form would need a register cleared first)
+__device__ __forceinline__ int sdot4_start(int a, int b) {
+  int r;
+  asm("v_dot4_i32_i8 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
+// Integer sum over aligned groups of N consecutive lanes (N = 1, 2, 4).
+template <int N>
+__device__ __forceinline__ int group_sum_i(int x) {
+  if constexpr (N >= 2) x += __builtin_amdgcn_mov_dpp(x, kDppXor1, 0xf, 0xf, true);
+  if constexpr (N >= 4) x += __builtin_amdgcn_mov_dpp(x, kDppXor2, 0xf, 0xf, true);
+  return x;
+}
+
+// Float sum over groups of N lanes that are NI-aligned and already hold the sum of
+// their NI-lane subgroup (NI | N; N <= 16).
+template <int N, int NI>
+__device__ __forceinline__ float group_sum_rest(float x) {
+  if constexpr (NI < 2 && N >= 2) x += dpp<kDppXor1>(x);
+  if constexpr (NI < 4 && N >= 4) x += dpp<kDppXor2>(x);
+  if constexpr (NI < 8 && N >= 8) x += dpp<kDppHalfMirror>(x);
+  if constexpr (NI < 16 && N >= 16) x += dpp<kDppMirror>(x);
+  return x;
 }
 
 __device__ __forceinline__ float load_q(const void* q, int dt, int64_t i) {
@@ -73,14 +119,18 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   constexpr int KW = KB == 16 ? E / 2 : (KB == 8 ? E / 4 : E / 8);  // key dwords per token per lane
   constexpr int VW = VB == 16 ? E / 2 : (VB == 8 ? E / 4 : E / 8);  // value dwords per token per lane
   constexpr int QW = KB == 16 ? E / 2 : E / 4;                       // query dwords per head
+  constexpr int KC = code_row_bytes(KB, D), KS = scale_row_bytes(KB, D);  // row bytes per plane
+  constexpr int VC = code_row_bytes(VB, D), VS = scale_row_bytes(VB, D);
+  constexpr int LPB = kBlock / E;      // lanes per block (their key codes share one scale)
   static_assert(E <= kBlock && kBlock % E == 0, "a lane stays inside one block");
   static_assert(CT % STEP == 0 && CT == 128, "chunk shape");
 
   __shared__ float s_q[GP][D];
-  __shared__ float s_qs[GP][NB];
+  __shared__ float s_qs[GP];
   __shared__ __attribute__((aligned(16))) int8_t s_qa[GP][D];
   __shared__ __attribute__((aligned(16))) int8_t s_qb[GP][D];
-  __shared__ float s_sc[4][CT][GP];
+  __shared__ float s_sc[4][CT][GP];                        // raw scores of a chunk
+  __shared__ __attribute__((aligned(16))) uint32_t s_w[4][CT / 2][GP];  // fp16 p of token pairs
   __shared__ float s_o[4][GP][D];
   __shared__ float s_ml[4][2][GP];
 
@@ -90,11 +140,11 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const int64_t srow = (int64_t)(a.sess0 + sl) * a.hq + (int64_t)head * a.group;  // first q row
   const int64_t ts = (int64_t)split * a.tps;
   const int64_t te = min(ts + a.tps, S.len);
-  const int64_t region = S.cap * (int64_t)(a.kc + a.ks + a.vc + a.vs);
+  const int64_t region = S.cap * (int64_t)(KC + KS + VC + VS);
   const uint8_t* kc = S.base + (int64_t)head * region;
-  const uint8_t* ks = kc + S.cap * a.kc;
-  const uint8_t* vc = ks + S.cap * a.ks;
-  const uint8_t* vs = vc + S.cap * a.vc;
+  const uint8_t* ks = kc + S.cap * KC;
+  const uint8_t* vc = ks + S.cap * KS;
+  const uint8_t* vs = vc + S.cap * VC;
 
   // ---- query preparation: fp32 copy, then per (head, block) two int8 digits -------
   for (int i = tid; i < GP * D; i += 256) {
@@ -102,24 +152,25 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     s_q[g][e] = g < a.group ? load_q(a.q, a.q_dtype, (srow + g) * D + e) : 0.f;
   }
   __syncthreads();
-  if (tid < GP * NB) {
-    const int g = tid / NB, b = tid % NB;
+  // one scale per query head: q ~= sq * (256 * qa + qb), |qa| <= 127, qb in [-128, 127];
+  // the integer dot products then carry 16 bits of the query
+  if (tid < GP) {
+    const int g = tid;
     if constexpr (KB == 16) {
-      s_qs[g][b] = a.qk_scale;
+      s_qs[g] = a.qk_scale;
     } else {
       float amax = 0.f;
-      for (int e = 0; e < kBlock; ++e) amax = fmaxf(amax, fabsf(s_q[g][b * kBlock + e]));
-      // q ~= sq * (256 * qa + qb), |qa| <= 127, qb in [-128, 127]
+      for (int e = 0; e < D; ++e) amax = fmaxf(amax, fabsf(s_q[g][e]));
       const float sq = amax / 32512.f;
-      for (int e = 0; e < kBlock; ++e) {
-        float v = sq > 0.f ? rintf(s_q[g][b * kBlock + e] / sq) : 0.f;
+      for (int e = 0; e < D; ++e) {
+        float v = sq > 0.f ? rintf(s_q[g][e] / sq) : 0.f;
         v = fminf(fmaxf(v, -32512.f), 32512.f);
         int Q = (int)v;
         int qa = (Q + 128) >> 8;  // floor((Q + 128) / 256)
-        s_qa[g][b * kBlock + e] = (int8_t)qa;
-        s_qb[g][b * kBlock + e] = (int8_t)(Q - 256 * qa);
+        s_qa[g][e] = (int8_t)qa;
+        s_qb[g][e] = (int8_t)(Q - 256 * qa);
       }
-      s_qs[g][b] = sq * a.qk_scale;
+      s_qs[g] = sq * a.qk_scale;
     }
   }
   __syncthreads();
@@ -127,10 +178,10 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const int sub = lane % LPT, grp = lane / LPT, e0 = sub * E, blk = e0 / kBlock;
   uint32_t qa_r[GP][QW], qb_r[GP][QW];
   int corr_a[GP], corr_b[GP];
-  float qsc[GP];
+  float qsc[GP];        // raw score -> base-2 logit, applied once per token in phase B
 #pragma unroll
   for (int g = 0; g < GP; ++g) {
-    qsc[g] = s_qs[g][blk];
+    qsc[g] = s_qs[g];
     corr_a[g] = 0;
     corr_b[g] = 0;
     if constexpr (KB == 16) {
@@ -177,42 +228,66 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     for (int e = 0; e < E; ++e) acc[g][e] = 0.f;
   }
 
-  const uint32_t koff = grp * a.kc + sub * (KW * 4), ksoff = grp * a.ks + blk * 2;
-  const uint32_t voff = grp * a.vc + sub * (VW * 4), vsoff = grp * a.vs + blk * 2;
+  const uint32_t koff = grp * KC + sub * (KW * 4), ksoff = grp * KS + blk * 2;
+  const uint32_t voff = grp * VC + sub * (VW * 4), vsoff = grp * VS + blk * 2;
   const int64_t n_chunks = te > ts ? (te - ts + CT - 1) / CT : 0;
-  for (int64_t c = __builtin_amdgcn_readfirstlane(wave); c < n_chunks; c += 4) {
+  // Load pipeline: step s of a phase uses ring slot s % R, and the codes of the step
+  // PD steps ahead are requested before step s computes.  The last PD steps of phase A
+  // request the first value steps of the chunk, and the last PD steps of phase C the
+  // first key steps of the wave's next chunk, so the pipeline never drains.
+  constexpr int PD = KVQ_DECODE_DEPTH < NS ? KVQ_DECODE_DEPTH : NS - 1, R = PD + 1;
+  static_assert(PD >= 1, "prefetch depth");
+  uint32_t kbuf[R][2][KW], vbuf[R][2][VW];
+  uint16_t kscl[R][2], vscl[R][2];
+  // address = chunk resource + loop-invariant lane offset + constant step offset
+  struct Rsrc { __amdgpu_buffer_rsrc_t kc, ks, vc, vs; };
+  // an empty range (n = 0) makes every load through it return 0 without touching memory
+  auto chunk_rsrc = [&](int64_t c, int n) {
     const int64_t c0 = ts + c * CT;
-    // wave-uniform chunk bases; per-lane offsets inside a chunk fit 32 bits
-    const uint8_t* kcc = kc + c0 * a.kc;
-    const uint8_t* ksc = ks + c0 * a.ks;
-    const uint8_t* vcc = vc + c0 * a.vc;
-    const uint8_t* vsc = vs + c0 * a.vs;
+    return Rsrc{make_rsrc(kc + c0 * KC, n * KC), make_rsrc(ks + c0 * KS, n * KS),
+                make_rsrc(vc + c0 * VC, n * VC), make_rsrc(vs + c0 * VS, n * VS)};
+  };
+  auto load_k = [&](const Rsrc& r, int s) {
+    const int slot = s % R;
+    buf_dwords<KW>(r.kc, koff, s * STEP * KC, kbuf[slot][0]);
+    buf_dwords<KW>(r.kc, koff + TPS * KC, s * STEP * KC, kbuf[slot][1]);
+    if constexpr (KB != 16) {
+      kscl[slot][0] = buf_u16(r.ks, ksoff, s * STEP * KS);
+      kscl[slot][1] = buf_u16(r.ks, ksoff + TPS * KS, s * STEP * KS);
+    }
+  };
+  auto load_v = [&](const Rsrc& r, int s) {
+    const int slot = s % R;
+    buf_dwords<VW>(r.vc, voff, s * STEP * VC, vbuf[slot][0]);
+    buf_dwords<VW>(r.vc, voff + TPS * VC, s * STEP * VC, vbuf[slot][1]);
+    if constexpr (VB != 16) {
+      vscl[slot][0] = buf_u16(r.vs, vsoff, s * STEP * VS);
+      vscl[slot][1] = buf_u16(r.vs, vsoff + TPS * VS, s * STEP * VS);
+    }
+  };
+  int64_t c = __builtin_amdgcn_readfirstlane(wave);
+  Rsrc rc = chunk_rsrc(c, CT);
+  if (c < n_chunks) {
+#pragma unroll
+    for (int s = 0; s < PD; ++s) load_k(rc, s);
+  }
+  for (; c < n_chunks; c += 4) {
+    const int64_t c0 = ts + c * CT;
     const bool tail = c0 + CT > te;
-    // ---- phase A: scores (codes of step s + 1 in flight while step s computes) ----
-    uint32_t kbuf[2][2][KW];
-    uint16_t kscl[2][2] = {{0, 0}, {0, 0}};
-    // address = uniform base (chunk, step, token half) + one loop-invariant lane offset
-    auto load_k = [&](int s, int slot) {
-      const uint8_t* c0p = kcc + (int64_t)(s * STEP) * a.kc;
-      load_dwords<KW>(c0p + koff, kbuf[slot][0]);
-      load_dwords<KW>(c0p + (int64_t)TPS * a.kc + koff, kbuf[slot][1]);
-      if constexpr (KB != 16) {
-        const uint8_t* s0p = ksc + (int64_t)(s * STEP) * a.ks;
-        kscl[slot][0] = *reinterpret_cast<const uint16_t*>(s0p + ksoff);
-        kscl[slot][1] = *reinterpret_cast<const uint16_t*>(s0p + (int64_t)TPS * a.ks + ksoff);
-      }
-    };
-    load_k(0, 0);
+    const bool more = c + 4 < n_chunks;
+    const Rsrc rn = chunk_rsrc(c + 4, more ? CT : 0);
+    // ---- phase A: scores ----------------------------------------------------------
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       const int la = s * STEP + grp, lb = la + TPS;
-      if (s + 1 < NS) load_k(s + 1, (s + 1) & 1);
-      const uint32_t* ka = kbuf[s & 1][0];
-      const uint32_t* kb = kbuf[s & 1][1];
+      if (s + PD < NS) load_k(rc, s + PD);
+      else load_v(rc, s + PD - NS);
+      const uint32_t* ka = kbuf[s % R][0];
+      const uint32_t* kb = kbuf[s % R][1];
       float da = 1.f, db = 1.f;
       if constexpr (KB != 16) {
-        da = h2f(kscl[s & 1][0]);
-        db = h2f(kscl[s & 1][1]);
+        da = h2f(kscl[s % R][0]);
+        db = h2f(kscl[s % R][1]);
       }
       float pa[GP], pb[GP];
 #pragma unroll
@@ -224,14 +299,17 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
             xa = __builtin_amdgcn_fdot2(as_h2(qa_r[g][j]), as_h2(ka[j]), xa, false);
             xb = __builtin_amdgcn_fdot2(as_h2(qa_r[g][j]), as_h2(kb[j]), xb, false);
           }
-          pa[g] = xa * qsc[g];
-          pb[g] = xb * qsc[g];
+          pa[g] = group_sum<LPT>(xa);
+          pb[g] = group_sum<LPT>(xb);
         } else {
           // one chain per token: high digit, times 256, then the low digit
           int ha = corr_a[g], hb = corr_a[g];
           if constexpr (KB == 8) {
+            // the first product starts the chain (8-bit keys need no offset correction)
+            ha = sdot4_start((int)ka[0], (int)qa_r[g][0]);
+            hb = sdot4_start((int)kb[0], (int)qa_r[g][0]);
 #pragma unroll
-            for (int j = 0; j < KW; ++j) {
+            for (int j = 1; j < KW; ++j) {
               ha = __builtin_amdgcn_sdot4((int)ka[j], (int)qa_r[g][j], ha, false);
               hb = __builtin_amdgcn_sdot4((int)kb[j], (int)qa_r[g][j], hb, false);
             }
@@ -266,11 +344,16 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
               hb = __builtin_amdgcn_sdot4((int)bo[j], (int)qb_r[g][2 * j + 1], hb, false);
             }
           }
-          pa[g] = (float)ha * (da * qsc[g]);
-          pb[g] = (float)hb * (db * qsc[g]);
+          // lanes of one block add their integers, then one scale per block
+          ha = group_sum_i<LPB>(ha);
+          hb = group_sum_i<LPB>(hb);
+          float xa = (float)ha * da, xb = (float)hb * db;
+          asm volatile("" : "+v"(xa), "+v"(xb));   // no multiply-add re-fusion across the DPP
+          pa[g] = group_sum_rest<LPT, LPB>(xa);
+          pb[g] = group_sum_rest<LPT, LPB>(xb);
         }
-        pa[g] = group_sum<LPT>(pa[g]);
-        pb[g] = group_sum<LPT>(pb[g]);
+        // keep the last reduction step out of the store's branch (so it fuses with DPP)
+        asm volatile("" : "+v"(pa[g]), "+v"(pb[g]));
       }
       if (sub == 0) {
 #pragma unroll
@@ -281,25 +364,15 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    // the first value codes of the chunk fly during the softmax statistics
-    uint32_t vbuf[2][2][VW];
-    uint16_t vscl[2][2] = {{0, 0}, {0, 0}};
-    auto load_v = [&](int s, int slot) {
-      const uint8_t* c0p = vcc + (int64_t)(s * STEP) * a.vc;
-      load_dwords<VW>(c0p + voff, vbuf[slot][0]);
-      load_dwords<VW>(c0p + (int64_t)TPS * a.vc + voff, vbuf[slot][1]);
-      if constexpr (VB != 16) {
-        const uint8_t* s0p = vsc + (int64_t)(s * STEP) * a.vs;
-        vscl[slot][0] = *reinterpret_cast<const uint16_t*>(s0p + vsoff);
-        vscl[slot][1] = *reinterpret_cast<const uint16_t*>(s0p + (int64_t)TPS * a.vs + vsoff);
-      }
-    };
-    load_v(0, 0);
+    // (the first value codes of the chunk fly during the softmax statistics)
     wave_lds_sync();
     // ---- phase B: softmax statistics, one lane per token ------------------------
+    const int wr0 = lane % STEP, wr1 = (lane + 64) % STEP;
+    const int wpair0 = (lane / STEP) * TPS + wr0 % TPS, whalf0 = wr0 / TPS;
+    const int wpair1 = ((lane + 64) / STEP) * TPS + wr1 % TPS, whalf1 = wr1 / TPS;
 #pragma unroll
     for (int g = 0; g < GP; ++g) {
-      float sa = s_sc[wave][lane][g], sb = s_sc[wave][lane + 64][g];
+      float sa = s_sc[wave][lane][g] * qsc[g], sb = s_sc[wave][lane + 64][g] * qsc[g];
       if (tail) {  // tokens past the cached length score -inf
         if (c0 + lane >= te) sa = -INFINITY;
         if (c0 + lane + 64 >= te) sb = -INFINITY;
@@ -309,8 +382,9 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       const float mu = mn == -INFINITY ? 0.f : mn;
       const float alpha = __builtin_amdgcn_exp2f(m[g] - mu);
       const float p0 = __builtin_amdgcn_exp2f(sa - mu), p1 = __builtin_amdgcn_exp2f(sb - mu);
-      s_sc[wave][lane][g] = p0;
-      s_sc[wave][lane + 64][g] = p1;
+      // phase C pairs token 16 s + r with 16 s + r + 8 (r < 8) in one fp16x2 word
+      reinterpret_cast<_Float16*>(&s_w[wave][wpair0][g])[whalf0] = (_Float16)p0;
+      reinterpret_cast<_Float16*>(&s_w[wave][wpair1][g])[whalf1] = (_Float16)p1;
       lsum[g] = lsum[g] * alpha + (p0 + p1);
       if (alpha != 1.f) {  // wave-uniform
 #pragma unroll
@@ -323,19 +397,17 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     // ---- phase C: values (codes of step s + 1 in flight while step s computes) ---
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      const int la = s * STEP + grp, lb = la + TPS;
-      if (s + 1 < NS) load_v(s + 1, (s + 1) & 1);
-      const uint32_t* va = vbuf[s & 1][0];
-      const uint32_t* vb = vbuf[s & 1][1];
-      float da = 1.f, db = 1.f;
-      if constexpr (VB != 16) {
-        da = h2f(vscl[s & 1][0]);
-        db = h2f(vscl[s & 1][1]);
-      }
+      if (s + PD < NS) load_v(rc, s + PD);
+      else load_k(rn, s + PD - NS);   // the next chunk (none: an empty range, no traffic)
+      const uint32_t* va = vbuf[s % R][0];
+      const uint32_t* vb = vbuf[s % R][1];
+      // weights of the token pair: fp16 p times the tokens' value scales (packed fp16)
       half2_t w[GP];
+      const uint32_t* wp = &s_w[wave][s * TPS + grp][0];
 #pragma unroll
       for (int g = 0; g < GP; ++g) {
-        w[g] = pack_rne(s_sc[wave][la][g] * da, s_sc[wave][lb][g] * db);
+        w[g] = as_h2(wp[g]);
+        if constexpr (VB != 16) w[g] = w[g] * as_h2((uint32_t)vscl[s % R][0] | ((uint32_t)vscl[s % R][1] << 16));
         wsum[g] = __builtin_amdgcn_fdot2(w[g], as_h2(0x3C003C00u), wsum[g], false);
       }
 #pragma unroll
@@ -375,6 +447,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
     wave_lds_sync();
+    rc = rn;
   }
 
   // ---- epilogue: wave partials -> workgroup partial -------------------------------

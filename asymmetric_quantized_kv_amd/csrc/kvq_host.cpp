@@ -445,11 +445,6 @@ int decode_launch(kv_cache* const* sessions, int n_sessions, int layer, const De
   a.qk_scale = sm_scale * 1.4426950408889634f;
   a.ws = ws;
   a.out = out;
-  const kv_cache* s0 = sessions[0];
-  a.kc = s0->g.kc;
-  a.ks = s0->g.ks;
-  a.vc = s0->g.vc;
-  a.vs = s0->g.vs;
   for (int b0 = 0; b0 < n_sessions; b0 += kMaxSessions) {
     const int nb = std::min(kMaxSessions, n_sessions - b0);
     a.n_sess = nb;

@@ -62,7 +62,6 @@ struct DecodeArgs {
   float qk_scale;         // sm_scale * log2(e)
   float* ws;              // [S][Hq][n_splits][D + 2] partials when partial
   float* out;             // [S][Hq][D] otherwise
-  int32_t kc, ks, vc, vs; // row bytes (shared by all sessions)
 };
 
 struct ChunkArgs {

@@ -34,12 +34,26 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// Maximum over the wave, for values that are never NaN: max with DPP operands inside
+// each row of 16 lanes, then the row broadcasts carry rows 0-2 into row 3, and lane 63
+// holds the result.  (Written out because the compiler keeps a canonicalizing copy
+// around every max of a DPP-moved value.)  Each DPP read of a register written by the
+// previous VALU op needs two wait states, hence the s_nop 1 before it.
 __device__ __forceinline__ float wave_max(float x) {
-  x = fmaxf(x, dpp<kDppXor1>(x));
-  x = fmaxf(x, dpp<kDppXor2>(x));
-  x = fmaxf(x, dpp<kDppHalfMirror>(x));
-  x = fmaxf(x, dpp<kDppMirror>(x));
-  return fmaxf(fmaxf(readlane(x, 0), readlane(x, 16)), fmaxf(readlane(x, 32), readlane(x, 48)));
+  asm("s_nop 1\n\t"
+      "v_max_f32_dpp %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "s_nop 1\n\t"
+      "v_max_f32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "s_nop 1\n\t"
+      "v_max_f32_dpp %0, %0, %0 row_half_mirror row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "s_nop 1\n\t"
+      "v_max_f32_dpp %0, %0, %0 row_mirror row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "s_nop 1\n\t"
+      "v_max_f32_dpp %0, %0, %0 row_bcast:15 row_mask:0xa bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_max_f32_dpp %0, %0, %0 row_bcast:31 row_mask:0xc bank_mask:0xf"
+      : "+v"(x));
+  return readlane(x, 63);
 }
 
 __device__ __forceinline__ float wave_sum(float x) {
