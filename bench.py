@@ -196,6 +196,11 @@ def main():
     mean = lambda xs: sum(xs) / len(xs)
     seg = [mean([e[j].elapsed_time(e[j + 1]) for e in ev]) for j in range(5)]
     dec1_t, dec2_t, app_t, chk1_t, chk2_t = seg
+    # a one-split plan launches no merge: the events around the empty second pass time nothing
+    if dec_plan[0] == 1:
+        dec2_t = 0.0
+    if turn_plan[0] == 1:
+        chk2_t = 0.0
     dec_t, chk_t = dec1_t + dec2_t, chk1_t + chk2_t
     dec_gbps = dec_bytes / (dec_t * 1e-3) / 1e9              # whole decode (both passes)
     dec1_gbps = dec_bytes / (dec1_t * 1e-3) / 1e9            # the partial kernel alone
@@ -266,7 +271,8 @@ def main():
         "decode_plan": {"n_splits": dec_plan[0], "tokens_per_split": dec_plan[1]},
         "chunk_plan": {"n_splits": turn_plan[0], "keys_per_split": turn_plan[1]},
         "roofline": {
-            "bound": "hbm", "kernel": "decode_kernel<8,4,128,4,16> (split-K partial pass)",
+            "bound": "hbm", "kernel": "decode_kernel<8,4,128,4,16> ("
+                                      + ("one split: normalized output" if dec_plan[0] == 1 else "split-K partial pass") + ")",
             "achieved": round(dec1_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(dec1_gbps / HBM_PEAK_GBPS, 4), "traffic": load_traffic("decode_k8v4"),
         },
