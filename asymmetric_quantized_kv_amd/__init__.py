@@ -13,5 +13,5 @@ from ._lib import (  # noqa: F401
     kv_decode_workspace_bytes, kv_decode_plan, kv_attend_decode_partial, kv_merge_partials,
     kv_attend_chunk, kv_chunk_workspace_bytes, kv_chunk_plan, kv_attend_chunk_partial, kv_footprint_bytes,
     kv_layout_footprint_bytes, kv_cache_len, kv_cache_reset, kv_cache_truncate, kv_cache_plane, kv_cache_copy_plane,
-    kv_last_error, kv_last_status, read_plane,
+    kv_session_bytes, kv_session_save, kv_session_load, kv_last_error, kv_last_status, read_plane,
 )

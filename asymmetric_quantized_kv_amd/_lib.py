@@ -47,6 +47,9 @@ _SIGS = {
                                  C.POINTER(C.c_int64)]),
     "kv_cache_copy_plane": (C.c_int, [C.c_void_p, C.c_int, C.c_int, C.c_int, C.c_int64, C.c_int64,
                                       C.c_void_p, C.c_void_p]),
+    "kv_session_bytes": (C.c_int64, [C.c_void_p]),
+    "kv_session_save": (C.c_int, [C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
+    "kv_session_load": (C.c_int, [C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
     "kv_last_error": (C.c_char_p, []),
     "kv_last_status": (C.c_int, []),
 }
@@ -288,6 +291,36 @@ def kv_cache_copy_plane(cache: int, layer: int, kv_head: int, plane: int, row0: 
     _check(lib().kv_cache_copy_plane(cache, layer, kv_head, plane, row0, n_rows, _dev_ptr(dst, "dst"),
                                      _stream(stream)))
     return dst
+
+
+def kv_session_bytes(cache: int) -> int:
+    return _check(lib().kv_session_bytes(cache))
+
+
+def _host_ptr(buf, name: str) -> tuple[int, int]:
+    """(address, bytes) of a host buffer: a CPU torch tensor (pinned or not) or a numpy array."""
+    if hasattr(buf, "is_cuda"):
+        if buf.is_cuda:
+            raise ValueError(f"{name} must be host memory")
+        if not buf.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        return buf.data_ptr(), buf.numel() * buf.element_size()
+    if not buf.flags["C_CONTIGUOUS"]:
+        raise ValueError(f"{name} must be contiguous")
+    return buf.ctypes.data, buf.nbytes
+
+
+def kv_session_save(cache: int, dst, stream=None):
+    """Write the session's saved form into the host buffer dst (uint8, >= kv_session_bytes)."""
+    p, n = _host_ptr(dst, "dst")
+    _check(lib().kv_session_save(cache, p, n, _stream(stream)))
+    return dst
+
+
+def kv_session_load(cache: int, src, stream=None) -> None:
+    """Restore a saved session from the host buffer src into cache."""
+    p, n = _host_ptr(src, "src")
+    _check(lib().kv_session_load(cache, p, n, _stream(stream)))
 
 
 def read_plane(cache: int, layer: int, kv_head: int, plane: int, row0: int, n_rows: int):

@@ -137,9 +137,19 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int split = blockIdx.x, head = blockIdx.y, sl = blockIdx.z;
   const SessionRef S = a.sess[sl];
-  const int64_t srow = (int64_t)(a.sess0 + sl) * a.hq + (int64_t)head * a.group;  // first q row
+  const int64_t srow = S.row * a.hq + (int64_t)head * a.group;  // first q row
   const int64_t ts = (int64_t)split * a.tps;
   const int64_t te = min(ts + a.tps, S.len);
+  if (ts >= S.len) {
+    // a split past this session's end (shorter sessions in a batch): an empty partial
+    if (a.partial) {
+      for (int i = tid; i < a.group * (D + 2); i += 256) {
+        const int g = i / (D + 2), e = i % (D + 2);
+        a.ws[((srow + g) * a.n_splits + split) * (D + 2) + e] = e == D ? -INFINITY : 0.f;
+      }
+    }
+    return;
+  }
   const int64_t region = S.cap * (int64_t)(KC + KS + VC + VS);
   const uint8_t* kc = S.base + (int64_t)head * region;
   const uint8_t* ks = kc + S.cap * KC;
@@ -154,15 +164,16 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   __syncthreads();
   // one scale per query head: q ~= sq * (256 * qa + qb), |qa| <= 127, qb in [-128, 127];
   // the integer dot products then carry 16 bits of the query
-  if (tid < GP) {
-    const int g = tid;
+  // (wave w prepares heads w, w + 4, ...: lanes split the elements, a DPP max gives amax)
+  for (int g = wave; g < GP; g += 4) {
     if constexpr (KB == 16) {
-      s_qs[g] = a.qk_scale;
+      if (lane == 0) s_qs[g] = a.qk_scale;
     } else {
       float amax = 0.f;
-      for (int e = 0; e < D; ++e) amax = fmaxf(amax, fabsf(s_q[g][e]));
+      for (int e = lane; e < D; e += 64) amax = fmaxf(amax, fabsf(s_q[g][e]));
+      amax = wave_max(amax);
       const float sq = amax / 32512.f;
-      for (int e = 0; e < D; ++e) {
+      for (int e = lane; e < D; e += 64) {
         float v = sq > 0.f ? rintf(s_q[g][e] / sq) : 0.f;
         v = fminf(fmaxf(v, -32512.f), 32512.f);
         int Q = (int)v;
@@ -170,7 +181,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         s_qa[g][e] = (int8_t)qa;
         s_qb[g][e] = (int8_t)(Q - 256 * qa);
       }
-      s_qs[g] = sq * a.qk_scale;
+      if (lane == 0) s_qs[g] = sq * a.qk_scale;
     }
   }
   __syncthreads();

@@ -311,6 +311,117 @@ int kv_cache_plane(const kv_cache* cache, int layer, int kv_head, int plane, con
   return KV_OK;
 }
 
+// ---- session offload and restore ------------------------------------------------------
+// Saved form: a header (magic, version, layout, n_layers, n_kv_heads, head_dim, then one
+// int64 length per layer), padded to 64 bytes, then for every (layer, KV head) the first
+// len[layer] rows of its planes KC, KS, VC, VS in that order.
+namespace {
+constexpr uint32_t kSessionMagic = 0x5351564bu;   // "KVQS"
+constexpr uint32_t kSessionVersion = 1;
+struct SessionHeader {
+  uint32_t magic, version;
+  int32_t layout, n_layers, n_kv_heads, head_dim;
+  int64_t reserved;
+};
+static_assert(sizeof(SessionHeader) == 32, "header layout");
+
+int64_t session_data_offset(int n_layers) { return round_up((int64_t)sizeof(SessionHeader) + 8 * (int64_t)n_layers, 64); }
+
+int64_t session_bytes(const kv_cache* c, const int64_t* lens) {
+  int64_t b = session_data_offset(c->n_layers);
+  const int64_t row = (int64_t)c->g.kc + c->g.ks + c->g.vc + c->g.vs;
+  for (int l = 0; l < c->n_layers; ++l) b += lens[l] * c->hkv * row;
+  return b;
+}
+
+// one asynchronous copy per (layer, KV head, plane); to_host: cache -> buf, else buf -> cache
+hipError_t session_copy(const kv_cache* c, uint8_t* buf, const int64_t* lens, bool to_host, hipStream_t st) {
+  int64_t off = session_data_offset(c->n_layers);
+  const Geom& g = c->g;
+  const int64_t pl_off[4] = {g.off_kc(), g.off_ks(), g.off_vc(), g.off_vs()};
+  const int64_t pl_row[4] = {g.kc, g.ks, g.vc, g.vs};
+  for (int l = 0; l < c->n_layers; ++l) {
+    for (int h = 0; h < c->hkv; ++h) {
+      uint8_t* region = c->arena + ((int64_t)l * c->hkv + h) * g.region();
+      for (int p = 0; p < 4; ++p) {
+        const int64_t n = lens[l] * pl_row[p];
+        if (n == 0) continue;
+        hipError_t e = to_host ? hipMemcpyAsync(buf + off, region + pl_off[p], (size_t)n, hipMemcpyDefault, st)
+                               : hipMemcpyAsync(region + pl_off[p], buf + off, (size_t)n, hipMemcpyDefault, st);
+        if (e != hipSuccess) return e;
+        off += n;
+      }
+    }
+  }
+  return hipSuccess;
+}
+}  // namespace
+
+int64_t kv_session_bytes(const kv_cache* cache) {
+  clear_err();
+  if (!cache) return fail(KV_EINVAL, "cache is NULL");
+  return session_bytes(cache, cache->len.data());
+}
+
+int kv_session_save(const kv_cache* cache, void* dst, size_t dst_bytes, void* stream) {
+  clear_err();
+  int rc = check_cache(cache);
+  if (rc) return rc;
+  if (!dst) return fail(KV_EINVAL, "dst is NULL");
+  const int64_t need = session_bytes(cache, cache->len.data());
+  if ((int64_t)dst_bytes < need)
+    return fail(KV_EINVAL, "buffer of %zu bytes is smaller than the %lld the session needs", dst_bytes, (long long)need);
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, dst) == hipSuccess && attr.type == hipMemoryTypeDevice)
+    return fail(KV_EINVAL, "dst must be host memory (the header is written by the host)");
+  (void)hipGetLastError();
+  SessionHeader hd{kSessionMagic, kSessionVersion, cache->layout, cache->n_layers, cache->hkv, cache->d, 0};
+  uint8_t* out = static_cast<uint8_t*>(dst);
+  memcpy(out, &hd, sizeof(hd));
+  memcpy(out + sizeof(hd), cache->len.data(), 8 * (size_t)cache->n_layers);
+  hipError_t e = session_copy(cache, out, cache->len.data(), true, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(const_cast<kv_cache*>(cache), e, "session save copy");
+  return KV_OK;
+}
+
+int kv_session_load(kv_cache* cache, const void* src, size_t src_bytes, void* stream) {
+  clear_err();
+  int rc = check_cache(cache);
+  if (rc) return rc;
+  if (!src) return fail(KV_EINVAL, "src is NULL");
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, src) == hipSuccess && attr.type == hipMemoryTypeDevice)
+    return fail(KV_EINVAL, "src must be host memory (the header is read by the host)");
+  (void)hipGetLastError();
+  if (src_bytes < sizeof(SessionHeader)) return fail(KV_EINVAL, "buffer of %zu bytes holds no session header", src_bytes);
+  SessionHeader hd;
+  memcpy(&hd, src, sizeof(hd));
+  if (hd.magic != kSessionMagic || hd.version != kSessionVersion)
+    return fail(KV_EINVAL, "not a saved session (magic %08x, version %u)", hd.magic, hd.version);
+  if (hd.layout != cache->layout || hd.n_layers != cache->n_layers || hd.n_kv_heads != cache->hkv ||
+      hd.head_dim != cache->d)
+    return fail(KV_EINVAL, "saved session (layout %d, %d layers, %d KV heads, head_dim %d) does not match the cache",
+                hd.layout, hd.n_layers, hd.n_kv_heads, hd.head_dim);
+  if ((int64_t)src_bytes < session_data_offset(cache->n_layers))
+    return fail(KV_EINVAL, "buffer of %zu bytes is shorter than the session header", src_bytes);
+  std::vector<int64_t> lens(cache->n_layers);
+  memcpy(lens.data(), static_cast<const uint8_t*>(src) + sizeof(hd), 8 * lens.size());
+  for (int l = 0; l < cache->n_layers; ++l) {
+    if (lens[l] < 0) return fail(KV_EINVAL, "saved length %lld of layer %d is negative", (long long)lens[l], l);
+    if (lens[l] > cache->max_tokens)
+      return fail(KV_ECAPACITY, "saved length %lld of layer %d exceeds max_tokens %lld", (long long)lens[l], l,
+                  (long long)cache->max_tokens);
+  }
+  const int64_t need = session_bytes(cache, lens.data());
+  if ((int64_t)src_bytes < need)
+    return fail(KV_EINVAL, "buffer of %zu bytes is shorter than the %lld the saved session needs", src_bytes, (long long)need);
+  hipError_t e = session_copy(cache, const_cast<uint8_t*>(static_cast<const uint8_t*>(src)), lens.data(), false,
+                              static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(cache, e, "session load copy");
+  cache->len = lens;
+  return KV_OK;
+}
+
 int kv_cache_copy_plane(const kv_cache* cache, int layer, int kv_head, int plane, int64_t row0,
                         int64_t n_rows, void* dst, void* stream) {
   const void* p = nullptr;
@@ -395,6 +506,7 @@ int check_split(int n_splits, int64_t per, int64_t gran, int64_t len, const char
 struct DecodePrep {
   int hkv, d, group, gp, kbits, vbits, device;
   int64_t max_len, base, slots;
+  std::vector<int64_t> lens;   // cached tokens of each session in the layer
 };
 
 int decode_prepare(kv_cache* const* sessions, int n_sessions, int layer, int n_q_heads, bool need_tokens,
@@ -414,9 +526,11 @@ int decode_prepare(kv_cache* const* sessions, int n_sessions, int layer, int n_q
   p->gp = decode_group_pad(p->group);
   if (p->gp < 0) return fail(KV_EUNSUPPORTED, "decode group size %d > 16 is not built", p->group);
   p->max_len = 0;
+  p->lens.resize(n_sessions);
   for (int i = 0; i < n_sessions; ++i) {
     if (need_tokens && sessions[i]->len[layer] == 0)
       return fail(KV_EEMPTY, "session %d has no cached token in layer %d", i, layer);
+    p->lens[i] = sessions[i]->len[layer];
     p->max_len = std::max(p->max_len, sessions[i]->len[layer]);
   }
   p->base = (int64_t)n_sessions * p->hkv;
@@ -424,9 +538,44 @@ int decode_prepare(kv_cache* const* sessions, int n_sessions, int layer, int n_q
   return KV_OK;
 }
 
+// Splits per session for a decode call: every session is cut at the same tokens_per_split,
+// so a session of len tokens keeps ceil(len / tps) workgroups per KV head busy and the
+// splits past its end exit at once.  With lengths that differ a lot, many splits let the
+// long sessions spread over the device while short ones take one workgroup each.
+constexpr int64_t kDecodeWgFixedTokens = 256;   // per-workgroup overhead, in streamed tokens
+
+int64_t decode_split_cap(const DecodePrep& p) {
+  const int64_t slots = p.slots > 0 ? p.slots : 1024;
+  return std::max<int64_t>(1, std::min<int64_t>(kMaxSplitsDecode, ceil_div(2 * slots, p.hkv)));
+}
+
 void decode_plan(const DecodePrep& p, int* n_splits, int64_t* tps) {
-  plan_splits(p.base, p.slots, split_cap(p.base, p.slots, kMaxSplitsDecode), p.max_len, kDecodeWaveTokens,
-              kDecodeWaveTokens, n_splits, tps);
+  const int64_t slots = p.slots > 0 ? p.slots : 1024;
+  const int64_t gran = kDecodeWaveTokens;
+  const int64_t cap = decode_split_cap(p);
+  double best = 0;
+  *n_splits = 1;
+  *tps = round_up(std::max<int64_t>(p.max_len, 1), gran);
+  for (int64_t s = 1; s <= cap; ++s) {
+    const int64_t t = round_up(ceil_div(p.max_len, s), gran);
+    const int64_t n = ceil_div(p.max_len, t);
+    if (n != s && s > 1) continue;
+    int64_t busy = 0;   // workgroups per KV head that hold tokens
+    for (int64_t len : p.lens) busy += std::max<int64_t>(1, ceil_div(len, t));
+    // rounds of the busy workgroups times (the tokens each one streams + a fixed cost of
+    // kDecodeWgFixedTokens for its query preparation and epilogue), a small charge for the
+    // empty workgroups, and the merge's read of n partials per row
+    const int64_t rows = (int64_t)p.lens.size() * p.hkv * p.group;
+    const double cost = (double)ceil_div(busy * p.hkv, slots) * (double)(t + kDecodeWgFixedTokens) +
+                        0.02 * (double)gran * (double)((n * (int64_t)p.lens.size() - busy) * p.hkv) / (double)slots +
+                        (n > 1 ? (double)rows * n * (p.d + 2) * 4.0 / (double)(208 * slots) : 0.0);
+    if (s == 1 || cost < best * 0.98) {
+      best = cost;
+      *n_splits = (int)n;
+      *tps = t;
+    }
+    if (t == gran) break;
+  }
 }
 
 int decode_launch(kv_cache* const* sessions, int n_sessions, int layer, const DecodePrep& p, const void* q,
@@ -445,15 +594,21 @@ int decode_launch(kv_cache* const* sessions, int n_sessions, int layer, const De
   a.qk_scale = sm_scale * 1.4426950408889634f;
   a.ws = ws;
   a.out = out;
+  // Longest sessions first: workgroups are dispatched in launch order, so the long
+  // sessions' splits start early and the short ones fill the tail.
+  std::vector<int> order(n_sessions);
+  for (int i = 0; i < n_sessions; ++i) order[i] = i;
+  std::stable_sort(order.begin(), order.end(), [&](int x, int y) { return p.lens[x] > p.lens[y]; });
   for (int b0 = 0; b0 < n_sessions; b0 += kMaxSessions) {
     const int nb = std::min(kMaxSessions, n_sessions - b0);
     a.n_sess = nb;
-    a.sess0 = b0;
     for (int i = 0; i < nb; ++i) {
-      const kv_cache* c = sessions[b0 + i];
+      const int r = order[b0 + i];
+      const kv_cache* c = sessions[r];
       a.sess[i].base = c->arena + (int64_t)layer * p.hkv * c->g.region();
       a.sess[i].cap = c->g.cap;
       a.sess[i].len = c->len[layer];
+      a.sess[i].row = r;
     }
     hipError_t e = launch_decode(a, p.kbits, p.vbits, p.d, p.gp, st);
     if (e != hipSuccess) {
@@ -545,7 +700,7 @@ int64_t kv_decode_workspace_bytes(kv_cache* const* sessions, int n_sessions, int
   DecodePrep p;
   int rc = decode_prepare(sessions, n_sessions, layer, n_q_heads, false, &p);
   if (rc) return rc;
-  const int64_t cap = split_cap(p.base, p.slots, kMaxSplitsDecode);
+  const int64_t cap = decode_split_cap(p);
   if (cap <= 1) return 0;
   return (int64_t)n_sessions * n_q_heads * cap * (p.d + 2) * (int64_t)sizeof(float);
 }

@@ -47,12 +47,12 @@ struct SessionRef {
   const uint8_t* base;    // arena + layer * Hkv * region of this session
   int64_t cap;
   int64_t len;
+  int64_t row;            // index of the session in the call (rows of q / out / workspace)
 };
 
 struct DecodeArgs {
   SessionRef sess[kMaxSessions];
   int n_sess;             // sessions in this launch
-  int sess0;              // global index of sess[0] (rows of q / out / workspace)
   int hkv, hq, group;
   int n_splits;
   int partial;            // 1: write (o, m, l) partials to ws; 0: normalized out (n_splits == 1)

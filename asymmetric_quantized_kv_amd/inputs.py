@@ -20,7 +20,7 @@ import numpy as np
 __all__ = [
     "bf16_round", "bf16_bits", "normal", "outlier_channels", "workload_small",
     "config1", "config2", "config3", "config4_session", "config4_queries",
-    "config5_chunk", "CONFIGS",
+    "config5_chunk", "ragged_lengths", "CONFIGS",
 ]
 
 
@@ -159,6 +159,13 @@ def config5_chunk(c: int, seed: int = 5, chunk: int = 4096):
     v = bf16_round(normal((chunk, 8, 128), seed, 2, c))
     q = bf16_round(normal((chunk, 40, 128), seed, 3, c))
     return k, v, q
+
+
+def ragged_lengths(n_sessions: int = 64, lo: int = 512, hi: int = 32_768, seed: int = 7) -> np.ndarray:
+    """Cached lengths of a batch of sessions at different points of their conversations:
+    log-uniform integers in [lo, hi] (int64)."""
+    u = _rng(seed, 0x5A6).random(n_sessions)
+    return np.floor(np.exp(np.log(lo) + u * (np.log(hi + 1) - np.log(lo)))).astype(np.int64).clip(lo, hi)
 
 
 CONFIGS = {

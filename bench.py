@@ -227,6 +227,60 @@ def main():
         extra["decode_k4v8_GBps"] = round(dec_bytes / (t48 * 1e-3) / 1e9, 1)
         extra["decode_k4v8_ms"] = round(t48, 4)
 
+    # session offload / restore of the 100,500-token turn cache through pinned host memory
+    # (host-link rate, PCIe included: context for a cache hit, not the metric)
+    sess_bytes = kvq.kv_session_bytes(h3)
+    host_buf = torch.empty(sess_bytes, dtype=torch.uint8, pin_memory=True)
+    h3b = kvq.kv_cache_create("K8V4", 1, TURN_HKV, D, TURN_CTX + TURN_NEW)
+    kvq.kv_session_save(h3, host_buf)
+    kvq.kv_session_load(h3b, host_buf)
+    torch.cuda.synchronize()
+    ev_s = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    n_rep = 5
+    ev_s[0].record(stream)
+    for _ in range(n_rep):
+        kvq.kv_session_save(h3, host_buf)
+    ev_s[1].record(stream)
+    for _ in range(n_rep):
+        kvq.kv_session_load(h3b, host_buf)
+    ev_s[2].record(stream)
+    torch.cuda.synchronize()
+    t_save, t_load = ev_s[0].elapsed_time(ev_s[1]) / n_rep, ev_s[1].elapsed_time(ev_s[2]) / n_rep
+    extra["session_offload"] = {
+        "workload": "K8V4 session of 100,500 tokens x 8 KV heads x D 128, pinned host buffer",
+        "bytes": sess_bytes, "save_ms": round(t_save, 3), "load_ms": round(t_load, 3),
+        "save_GBps": round(sess_bytes / (t_save * 1e-3) / 1e9, 1), "load_GBps": round(sess_bytes / (t_load * 1e-3) / 1e9, 1),
+    }
+    kvq.kv_cache_destroy(h3b)
+    del host_buf
+    log(f"session offload {sess_bytes / 1e6:.1f} MB: save {t_save:.3f} ms, load {t_load:.3f} ms")
+
+    # ragged batch: the same 64 K8V4 sessions cut back to log-uniform lengths (512..32,768),
+    # decoded with the library's plan (the caches are not used at full length afterwards)
+    rag_lens = I.ragged_lengths(DEC_S, 512, DEC_T)
+    for h, n in zip(caches["K8V4"], rag_lens):
+        kvq.kv_cache_truncate(h, 0, int(n))
+    rag_bytes = int(rag_lens.sum()) * DEC_HKV * 208
+    rag_plan = kvq.kv_decode_plan(caches["K8V4"], 0, DEC_HQ)
+    ws_rag = torch.empty(max(16, kvq.kv_decode_workspace_bytes(caches["K8V4"], 0, DEC_HQ)), dtype=torch.uint8,
+                         device=dev)
+    for _ in range(args.warmup):
+        kvq.kv_attend_decode(caches["K8V4"], 0, q_dec, sm, out=out_dec, workspace=ws_rag)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        kvq.kv_attend_decode(caches["K8V4"], 0, q_dec, sm, out=out_dec, workspace=ws_rag)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t_rag = e0.elapsed_time(e1) / args.steps
+    extra["ragged_decode"] = {
+        "workload": "64 K8V4 sessions, log-uniform lengths 512..32,768 (seeded), Hq 32 / Hkv 8 / D 128",
+        "cache_bytes": rag_bytes, "ms": round(t_rag, 4), "GBps": round(rag_bytes / (t_rag * 1e-3) / 1e9, 1),
+        "hbm_frac": round(rag_bytes / (t_rag * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "plan": {"n_splits": rag_plan[0], "tokens_per_split": rag_plan[1]},
+    }
+    log(f"ragged decode {t_rag:.4f} ms ({extra['ragged_decode']['GBps']} GB/s), plan {rag_plan}")
+
     if args.copy_calibration:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         b = torch.empty_like(a)

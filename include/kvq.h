@@ -219,6 +219,34 @@ int kv_cache_plane(const kv_cache* cache, int layer, int kv_head, int plane,
 int kv_cache_copy_plane(const kv_cache* cache, int layer, int kv_head, int plane,
                         int64_t row0, int64_t n_rows, void* dst, void* stream);
 
+/* Session offload and restore: the packed cache of a session leaves the GPU between turns
+ * and comes back for the next one, so a cache hit costs a host-link transfer of the
+ * quantized bytes instead of a re-prefill of the context (openclawradar.com page, "Principais
+ * Descobertas e Benchmarks": sessions are kept between turns; "KV Cache Offloading for
+ * Context-Intensive Tasks", gist.science: KV moved to host memory and reloaded on demand).
+ *
+ * Saved form: a 32-byte header (magic "KVQS", version 1, layout, n_layers, n_kv_heads,
+ * head_dim as 32-bit integers, 8 reserved bytes), one int64 cached length per layer, zero
+ * padding to a multiple of 64 bytes, then for every layer and KV head the first len[layer]
+ * rows of the planes KC, KS, VC, VS in that order (row bytes as kv_cache_plane reports).
+ *
+ * kv_session_bytes: size of that form for the cache as it stands; < 0 for a NULL cache.
+ * kv_session_save: writes it to dst, which must be host memory (pinned memory from
+ *   hipHostMalloc gives the full host-link rate; pageable memory makes the copies
+ *   synchronous).  The header is written by the host during the call; the plane bytes
+ *   land when `stream` passes the call.  The cache is unchanged.
+ *   Errors: KV_EINVAL (NULL or device dst, dst_bytes too small), KV_EHIP.
+ * kv_session_load: replaces the contents of `cache` with a saved session read from host
+ *   memory src.  The header must match the cache's (layout, n_layers, n_kv_heads,
+ *   head_dim).  Lengths take the saved values when the call is enqueued; rows past them
+ *   are left as they are.
+ *   Errors: KV_EINVAL (NULL or device src, bad magic or version, shape mismatch, src_bytes
+ *   too small), KV_ECAPACITY (a saved length above max_tokens), KV_EHIP.  On an error
+ *   the cache is unchanged. */
+int64_t kv_session_bytes(const kv_cache* cache);
+int kv_session_save(const kv_cache* cache, void* dst, size_t dst_bytes, void* stream);
+int kv_session_load(kv_cache* cache, const void* src, size_t src_bytes, void* stream);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char* kv_last_error(void);
 

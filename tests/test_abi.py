@@ -83,6 +83,9 @@ def test_null_handles_are_rejected(built_library):
     assert L.kv_chunk_plan(None, 0, 4, 1, C.byref(n), C.byref(t)) == kvq.KV_EINVAL
     assert L.kv_attend_decode_partial(None, 1, 0, None, 0, 4, 0.1, 1, 512, None, 0, None) == kvq.KV_EINVAL
     assert L.kv_attend_chunk_partial(None, 0, None, 0, 4, 1, 0.1, 1, 64, None, 0, None) == kvq.KV_EINVAL
+    assert L.kv_session_bytes(None) == kvq.KV_EINVAL
+    assert L.kv_session_save(None, None, 0, None) == kvq.KV_EINVAL
+    assert L.kv_session_load(None, None, 0, None) == kvq.KV_EINVAL
 
 
 def test_merge_checks_arguments_on_the_host(built_library):

@@ -193,3 +193,41 @@ def test_partial_entry_points_reject_bad_splits():
     finally:
         torch.cuda.synchronize()
         kvq.kv_cache_destroy(h)
+
+
+def test_ragged_batch_spreads_the_long_session():
+    """Lengths that differ by four orders of magnitude: the plan cuts the long session into
+    many splits (the short ones keep one busy split each, the rest exit empty), and the
+    result still matches the oracle, pass by pass."""
+    log("ragged batch plan")
+    torch = torch_mod()
+    lens = [20000, 300, 50, 4096, 1, 700]
+    hkv, g, d = 2, 4, 128
+    hq = hkv * g
+    q = I.bf16_round(I.normal((len(lens), hq, d), 980, 9))
+    sessions, ocs = [], []
+    try:
+        for i, n in enumerate(lens):
+            k, v, _ = I.workload_small(981 + i, n, hkv, d, hq, 1, bf16=True, n_outliers=4)
+            h = kvq.kv_cache_create("K8V4", 1, hkv, d, n)
+            sessions.append(h)
+            kvq.kv_append_quant(h, 0, dev(k, "bf16"), dev(v, "bf16"))
+            oc = O.OracleCache(O.LAYOUT_IDS["K8V4"], 1, hkv, d, n)
+            oc.append(0, k, v)
+            ocs.append(oc)
+        scale = d ** -0.5
+        qd = dev(q, "bf16")
+        n_splits, per = kvq.kv_decode_plan(sessions, 0, hq)
+        log(f"  plan {n_splits} x {per}")
+        assert n_splits > 4 and n_splits * per >= max(lens)
+        want = O.attend_decode(ocs, 0, q, scale)
+        err = max_err(kvq.kv_attend_decode(sessions, 0, qd, scale), want)
+        log(f"  one call err {err:.3e}")
+        assert err <= TOL
+        p = kvq.kv_attend_decode_partial(sessions, 0, qd, scale, n_splits, per)
+        o, m, l = O.decode_partials(ocs, 0, q, scale, n_splits, per)
+        compare_partials(p, o, m, l, f"{n_splits} x {per}")
+    finally:
+        torch.cuda.synchronize()
+        for h in sessions:
+            kvq.kv_cache_destroy(h)
