@@ -21,6 +21,9 @@ STATUS_NAMES = {0: "KV_OK", -1: "KV_EINVAL", -2: "KV_ECAPACITY", -3: "KV_ENOMEM"
 
 _SIGS = {
     "kv_cache_create": (C.c_void_p, [C.c_int, C.c_int, C.c_int, C.c_int, C.c_int64]),
+    "kv_cache_create_layered": (C.c_void_p, [C.POINTER(C.c_int), C.c_int, C.c_int, C.c_int, C.c_int64]),
+    "kv_cache_layout": (C.c_int, [C.c_void_p, C.c_int]),
+    "kv_layered_footprint_bytes": (C.c_int64, [C.POINTER(C.c_int), C.c_int, C.c_int, C.c_int, C.c_int64]),
     "kv_cache_destroy": (None, [C.c_void_p]),
     "kv_append_quant": (C.c_int, [C.c_void_p, C.c_int, C.c_void_p, C.c_void_p, C.c_int, C.c_int64, C.c_void_p]),
     "kv_attend_decode": (C.c_int, [C.c_void_p, C.c_int, C.c_int, C.c_void_p, C.c_int, C.c_int, C.c_float,
@@ -132,6 +135,29 @@ def kv_cache_create(layout, n_layers: int, n_kv_heads: int, head_dim: int, max_t
     if not h:
         raise KVError(lib().kv_last_status(), kv_last_error())
     return h
+
+
+def _layout_array(layouts):
+    ids = [LAYOUT_IDS[x] if isinstance(x, str) else int(x) for x in layouts]
+    return (C.c_int * len(ids))(*ids), len(ids)
+
+
+def kv_cache_create_layered(layouts, n_kv_heads: int, head_dim: int, max_tokens: int) -> int:
+    """A cache whose layer l uses layouts[l] (names or codes)."""
+    arr, n = _layout_array(layouts)
+    h = lib().kv_cache_create_layered(arr, n, n_kv_heads, head_dim, max_tokens)
+    if not h:
+        raise KVError(lib().kv_last_status(), kv_last_error())
+    return h
+
+
+def kv_cache_layout(cache: int, layer: int) -> int:
+    return _check(lib().kv_cache_layout(cache, layer))
+
+
+def kv_layered_footprint_bytes(layouts, n_kv_heads: int, head_dim: int, max_tokens: int) -> int:
+    arr, n = _layout_array(layouts)
+    return _check(lib().kv_layered_footprint_bytes(arr, n, n_kv_heads, head_dim, max_tokens))
 
 
 def kv_cache_destroy(cache: int) -> None:

@@ -17,11 +17,18 @@
 
 using namespace kvq;
 
-struct kv_cache {
-  int layout, n_layers, hkv, d;
-  int64_t max_tokens;
-  int kbits, vbits;
+// One layer's storage: its layout (K and V bits may differ from layer to layer), plane
+// geometry and byte offset in the arena.
+struct LayerGeom {
+  int layout, kbits, vbits;
   Geom g;
+  int64_t base;
+};
+
+struct kv_cache {
+  int n_layers, hkv, d;
+  int64_t max_tokens;
+  std::vector<LayerGeom> lg;
   uint8_t* arena;
   int64_t bytes;
   std::vector<int64_t> len;
@@ -80,6 +87,14 @@ Geom make_geom(int kb, int vb, int d, int64_t max_tokens) {
   g.vc = code_row_bytes(vb, d);
   g.vs = scale_row_bytes(vb, d);
   return g;
+}
+
+uint8_t* layer_base(const kv_cache* c, int layer) { return c->arena + c->lg[layer].base; }
+
+bool uniform_layout(const kv_cache* c) {
+  for (const LayerGeom& l : c->lg)
+    if (l.layout != c->lg[0].layout) return false;
+  return true;
 }
 
 int check_cache(const kv_cache* c) {
@@ -173,11 +188,14 @@ int check_sessions(kv_cache* const* sessions, int n_sessions, int layer) {
     const kv_cache* c = sessions[i];
     if (!c) return fail(KV_EINVAL, "session %d is NULL", i);
     if (c->poisoned) return fail(KV_EHIP, "session %d is poisoned by an earlier HIP error", i);
-    if (c->layout != s0->layout || c->n_layers != s0->n_layers || c->hkv != s0->hkv || c->d != s0->d)
-      return fail(KV_EINVAL, "session %d does not share (layout, n_layers, n_kv_heads, head_dim) with session 0", i);
+    if (c->n_layers != s0->n_layers || c->hkv != s0->hkv || c->d != s0->d)
+      return fail(KV_EINVAL, "session %d does not share (n_layers, n_kv_heads, head_dim) with session 0", i);
     if (c->device != s0->device) return fail(KV_EINVAL, "session %d lives on another device", i);
   }
   if (layer < 0 || layer >= s0->n_layers) return fail(KV_EINVAL, "layer %d out of range [0, %d)", layer, s0->n_layers);
+  for (int i = 1; i < n_sessions; ++i)
+    if (sessions[i]->lg[layer].layout != s0->lg[layer].layout)
+      return fail(KV_EINVAL, "session %d stores layer %d in another layout than session 0", i, layer);
   return KV_OK;
 }
 
@@ -200,18 +218,47 @@ int64_t kv_layout_footprint_bytes(int layout, int n_layers, int n_kv_heads, int 
   return (int64_t)n_layers * n_kv_heads * g.region();
 }
 
-kv_cache* kv_cache_create(int layout, int n_layers, int n_kv_heads, int head_dim,
-                          int64_t max_tokens) {
+int64_t kv_layered_footprint_bytes(const int* layouts, int n_layers, int n_kv_heads, int head_dim,
+                                   int64_t max_tokens) {
   clear_err();
-  if (check_shape(layout, n_layers, n_kv_heads, head_dim, max_tokens)) return nullptr;
+  if (!layouts) return fail(KV_EINVAL, "layouts is NULL");
+  if (n_layers < 1) return fail(KV_EINVAL, "n_layers must be >= 1 (got %d)", n_layers);
+  int64_t total = 0;
+  for (int l = 0; l < n_layers; ++l) {
+    const int64_t b = kv_layout_footprint_bytes(layouts[l], 1, n_kv_heads, head_dim, max_tokens);
+    if (b < 0) return b;
+    total += b;
+  }
+  return total;
+}
+
+kv_cache* kv_cache_create_layered(const int* layouts, int n_layers, int n_kv_heads, int head_dim,
+                                  int64_t max_tokens) {
+  clear_err();
+  if (!layouts) {
+    fail(KV_EINVAL, "layouts is NULL");
+    return nullptr;
+  }
+  if (n_layers < 1) {
+    fail(KV_EINVAL, "n_layers must be >= 1 (got %d)", n_layers);
+    return nullptr;
+  }
+  for (int l = 0; l < n_layers; ++l)
+    if (check_shape(layouts[l], 1, n_kv_heads, head_dim, max_tokens)) return nullptr;
   if (head_dim != 64 && head_dim != 128) {
     fail(KV_EUNSUPPORTED, "head_dim %d is valid but only 64 and 128 are built", head_dim);
     return nullptr;
   }
-  int kb, vb;
-  layout_bits(layout, &kb, &vb);
-  Geom g = make_geom(kb, vb, head_dim, max_tokens);
-  int64_t bytes = (int64_t)n_layers * n_kv_heads * g.region();
+  std::vector<LayerGeom> lg(n_layers);
+  int64_t bytes = 0;
+  for (int l = 0; l < n_layers; ++l) {
+    LayerGeom& x = lg[l];
+    x.layout = layouts[l];
+    layout_bits(x.layout, &x.kbits, &x.vbits);
+    x.g = make_geom(x.kbits, x.vbits, head_dim, max_tokens);
+    x.base = bytes;
+    bytes += (int64_t)n_kv_heads * x.g.region();
+  }
   const char* fault = getenv("KVQ_FAULT");
   if (fault && strcmp(fault, "alloc") == 0) {
     fail(KV_ENOMEM, "hipMalloc of %lld bytes failed (forced by KVQ_FAULT=alloc)", (long long)bytes);
@@ -237,20 +284,32 @@ kv_cache* kv_cache_create(int layout, int n_layers, int n_kv_heads, int head_dim
     return nullptr;
   }
   kv_cache* c = new kv_cache;
-  c->layout = layout;
   c->n_layers = n_layers;
   c->hkv = n_kv_heads;
   c->d = head_dim;
   c->max_tokens = max_tokens;
-  c->kbits = kb;
-  c->vbits = vb;
-  c->g = g;
+  c->lg = std::move(lg);
   c->arena = static_cast<uint8_t*>(p);
   c->bytes = bytes;
   c->len.assign(n_layers, 0);
   c->device = dev;
   c->poisoned = false;
   return c;
+}
+
+kv_cache* kv_cache_create(int layout, int n_layers, int n_kv_heads, int head_dim,
+                          int64_t max_tokens) {
+  clear_err();
+  if (check_shape(layout, n_layers, n_kv_heads, head_dim, max_tokens)) return nullptr;
+  std::vector<int> layouts(n_layers, layout);
+  return kv_cache_create_layered(layouts.data(), n_layers, n_kv_heads, head_dim, max_tokens);
+}
+
+int kv_cache_layout(const kv_cache* cache, int layer) {
+  clear_err();
+  if (!cache) return fail(KV_EINVAL, "cache is NULL");
+  if (layer < 0 || layer >= cache->n_layers) return fail(KV_EINVAL, "layer %d out of range", layer);
+  return cache->lg[layer].layout;
 }
 
 void kv_cache_destroy(kv_cache* cache) {
@@ -296,8 +355,8 @@ int kv_cache_plane(const kv_cache* cache, int layer, int kv_head, int plane, con
   if (!ptr || !row_bytes) return fail(KV_EINVAL, "ptr and row_bytes must not be NULL");
   if (layer < 0 || layer >= cache->n_layers) return fail(KV_EINVAL, "layer %d out of range", layer);
   if (kv_head < 0 || kv_head >= cache->hkv) return fail(KV_EINVAL, "kv_head %d out of range", kv_head);
-  const Geom& g = cache->g;
-  const uint8_t* region = cache->arena + ((int64_t)layer * cache->hkv + kv_head) * g.region();
+  const Geom& g = cache->lg[layer].g;
+  const uint8_t* region = layer_base(cache, layer) + (int64_t)kv_head * g.region();
   int64_t off, rb;
   switch (plane) {
     case KV_PLANE_KC: off = g.off_kc(); rb = g.kc; break;
@@ -312,12 +371,13 @@ int kv_cache_plane(const kv_cache* cache, int layer, int kv_head, int plane, con
 }
 
 // ---- session offload and restore ------------------------------------------------------
-// Saved form: a header (magic, version, layout, n_layers, n_kv_heads, head_dim, then one
-// int64 length per layer), padded to 64 bytes, then for every (layer, KV head) the first
-// len[layer] rows of its planes KC, KS, VC, VS in that order.
+// Saved form: a header (magic, version, layout or -1 when layers differ, n_layers,
+// n_kv_heads, head_dim), one int64 length and one int32 layout per layer, padded to 64
+// bytes, then for every (layer, KV head) the first len[layer] rows of its planes KC, KS,
+// VC, VS in that order.
 namespace {
 constexpr uint32_t kSessionMagic = 0x5351564bu;   // "KVQS"
-constexpr uint32_t kSessionVersion = 1;
+constexpr uint32_t kSessionVersion = 2;
 struct SessionHeader {
   uint32_t magic, version;
   int32_t layout, n_layers, n_kv_heads, head_dim;
@@ -325,24 +385,28 @@ struct SessionHeader {
 };
 static_assert(sizeof(SessionHeader) == 32, "header layout");
 
-int64_t session_data_offset(int n_layers) { return round_up((int64_t)sizeof(SessionHeader) + 8 * (int64_t)n_layers, 64); }
+int64_t session_data_offset(int n_layers) {
+  return round_up((int64_t)sizeof(SessionHeader) + 12 * (int64_t)n_layers, 64);
+}
 
 int64_t session_bytes(const kv_cache* c, const int64_t* lens) {
   int64_t b = session_data_offset(c->n_layers);
-  const int64_t row = (int64_t)c->g.kc + c->g.ks + c->g.vc + c->g.vs;
-  for (int l = 0; l < c->n_layers; ++l) b += lens[l] * c->hkv * row;
+  for (int l = 0; l < c->n_layers; ++l) {
+    const Geom& g = c->lg[l].g;
+    b += lens[l] * c->hkv * ((int64_t)g.kc + g.ks + g.vc + g.vs);
+  }
   return b;
 }
 
 // one asynchronous copy per (layer, KV head, plane); to_host: cache -> buf, else buf -> cache
 hipError_t session_copy(const kv_cache* c, uint8_t* buf, const int64_t* lens, bool to_host, hipStream_t st) {
   int64_t off = session_data_offset(c->n_layers);
-  const Geom& g = c->g;
-  const int64_t pl_off[4] = {g.off_kc(), g.off_ks(), g.off_vc(), g.off_vs()};
-  const int64_t pl_row[4] = {g.kc, g.ks, g.vc, g.vs};
   for (int l = 0; l < c->n_layers; ++l) {
+    const Geom& g = c->lg[l].g;
+    const int64_t pl_off[4] = {g.off_kc(), g.off_ks(), g.off_vc(), g.off_vs()};
+    const int64_t pl_row[4] = {g.kc, g.ks, g.vc, g.vs};
     for (int h = 0; h < c->hkv; ++h) {
-      uint8_t* region = c->arena + ((int64_t)l * c->hkv + h) * g.region();
+      uint8_t* region = layer_base(c, l) + (int64_t)h * g.region();
       for (int p = 0; p < 4; ++p) {
         const int64_t n = lens[l] * pl_row[p];
         if (n == 0) continue;
@@ -375,10 +439,17 @@ int kv_session_save(const kv_cache* cache, void* dst, size_t dst_bytes, void* st
   if (hipPointerGetAttributes(&attr, dst) == hipSuccess && attr.type == hipMemoryTypeDevice)
     return fail(KV_EINVAL, "dst must be host memory (the header is written by the host)");
   (void)hipGetLastError();
-  SessionHeader hd{kSessionMagic, kSessionVersion, cache->layout, cache->n_layers, cache->hkv, cache->d, 0};
+  const int32_t layout = uniform_layout(cache) ? cache->lg[0].layout : -1;
+  SessionHeader hd{kSessionMagic, kSessionVersion, layout, cache->n_layers, cache->hkv, cache->d, 0};
   uint8_t* out = static_cast<uint8_t*>(dst);
+  const int64_t data = session_data_offset(cache->n_layers);
+  memset(out, 0, (size_t)data);
   memcpy(out, &hd, sizeof(hd));
   memcpy(out + sizeof(hd), cache->len.data(), 8 * (size_t)cache->n_layers);
+  for (int l = 0; l < cache->n_layers; ++l) {
+    const int32_t lay = cache->lg[l].layout;
+    memcpy(out + sizeof(hd) + 8 * (size_t)cache->n_layers + 4 * (size_t)l, &lay, 4);
+  }
   hipError_t e = session_copy(cache, out, cache->len.data(), true, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(const_cast<kv_cache*>(cache), e, "session save copy");
   return KV_OK;
@@ -398,15 +469,19 @@ int kv_session_load(kv_cache* cache, const void* src, size_t src_bytes, void* st
   memcpy(&hd, src, sizeof(hd));
   if (hd.magic != kSessionMagic || hd.version != kSessionVersion)
     return fail(KV_EINVAL, "not a saved session (magic %08x, version %u)", hd.magic, hd.version);
-  if (hd.layout != cache->layout || hd.n_layers != cache->n_layers || hd.n_kv_heads != cache->hkv ||
-      hd.head_dim != cache->d)
-    return fail(KV_EINVAL, "saved session (layout %d, %d layers, %d KV heads, head_dim %d) does not match the cache",
-                hd.layout, hd.n_layers, hd.n_kv_heads, hd.head_dim);
+  if (hd.n_layers != cache->n_layers || hd.n_kv_heads != cache->hkv || hd.head_dim != cache->d)
+    return fail(KV_EINVAL, "saved session (%d layers, %d KV heads, head_dim %d) does not match the cache",
+                hd.n_layers, hd.n_kv_heads, hd.head_dim);
   if ((int64_t)src_bytes < session_data_offset(cache->n_layers))
     return fail(KV_EINVAL, "buffer of %zu bytes is shorter than the session header", src_bytes);
+  const uint8_t* in = static_cast<const uint8_t*>(src);
   std::vector<int64_t> lens(cache->n_layers);
-  memcpy(lens.data(), static_cast<const uint8_t*>(src) + sizeof(hd), 8 * lens.size());
+  memcpy(lens.data(), in + sizeof(hd), 8 * lens.size());
   for (int l = 0; l < cache->n_layers; ++l) {
+    int32_t lay;
+    memcpy(&lay, in + sizeof(hd) + 8 * lens.size() + 4 * (size_t)l, 4);
+    if (lay != cache->lg[l].layout)
+      return fail(KV_EINVAL, "layer %d was saved in layout %d, the cache stores layout %d", l, lay, cache->lg[l].layout);
     if (lens[l] < 0) return fail(KV_EINVAL, "saved length %lld of layer %d is negative", (long long)lens[l], l);
     if (lens[l] > cache->max_tokens)
       return fail(KV_ECAPACITY, "saved length %lld of layer %d exceeds max_tokens %lld", (long long)lens[l], l,
@@ -415,8 +490,7 @@ int kv_session_load(kv_cache* cache, const void* src, size_t src_bytes, void* st
   const int64_t need = session_bytes(cache, lens.data());
   if ((int64_t)src_bytes < need)
     return fail(KV_EINVAL, "buffer of %zu bytes is shorter than the %lld the saved session needs", src_bytes, (long long)need);
-  hipError_t e = session_copy(cache, const_cast<uint8_t*>(static_cast<const uint8_t*>(src)), lens.data(), false,
-                              static_cast<hipStream_t>(stream));
+  hipError_t e = session_copy(cache, const_cast<uint8_t*>(in), lens.data(), false, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(cache, e, "session load copy");
   cache->len = lens;
   return KV_OK;
@@ -429,7 +503,7 @@ int kv_cache_copy_plane(const kv_cache* cache, int layer, int kv_head, int plane
   int rc = kv_cache_plane(cache, layer, kv_head, plane, &p, &rb);
   if (rc) return rc;
   if (!dst) return fail(KV_EINVAL, "dst is NULL");
-  if (row0 < 0 || n_rows < 0 || row0 + n_rows > cache->g.cap)
+  if (row0 < 0 || n_rows < 0 || row0 + n_rows > cache->lg[layer].g.cap)
     return fail(KV_EINVAL, "rows [%lld, %lld) outside the plane", (long long)row0, (long long)(row0 + n_rows));
   if (cache->poisoned) return fail(KV_EHIP, "cache is poisoned by an earlier HIP error");
   if (rb == 0 || n_rows == 0) return KV_OK;
@@ -456,12 +530,13 @@ int kv_append_quant(kv_cache* cache, int layer, const void* k, const void* v, in
   AppendArgs a;
   a.src[0] = k;
   a.src[1] = v;
-  a.layer_base = cache->arena + (int64_t)layer * cache->hkv * cache->g.region();
-  a.g = cache->g;
+  const LayerGeom& L = cache->lg[layer];
+  a.layer_base = layer_base(cache, layer);
+  a.g = L.g;
   a.t0 = cache->len[layer];
   a.n = n_new;
   a.hkv = cache->hkv;
-  hipError_t e = launch_append(a, cache->kbits, cache->vbits, dtype, cache->d, static_cast<hipStream_t>(stream));
+  hipError_t e = launch_append(a, L.kbits, L.vbits, dtype, cache->d, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(cache, e, "append launch");
   cache->len[layer] += n_new;
   return KV_OK;
@@ -519,8 +594,8 @@ int decode_prepare(kv_cache* const* sessions, int n_sessions, int layer, int n_q
   if (s0->hkv > 65535) return fail(KV_EUNSUPPORTED, "n_kv_heads %d exceeds one launch (65535)", s0->hkv);
   p->hkv = s0->hkv;
   p->d = s0->d;
-  p->kbits = s0->kbits;
-  p->vbits = s0->vbits;
+  p->kbits = s0->lg[layer].kbits;
+  p->vbits = s0->lg[layer].vbits;
   p->device = s0->device;
   p->group = n_q_heads / s0->hkv;
   p->gp = decode_group_pad(p->group);
@@ -605,8 +680,8 @@ int decode_launch(kv_cache* const* sessions, int n_sessions, int layer, const De
     for (int i = 0; i < nb; ++i) {
       const int r = order[b0 + i];
       const kv_cache* c = sessions[r];
-      a.sess[i].base = c->arena + (int64_t)layer * p.hkv * c->g.region();
-      a.sess[i].cap = c->g.cap;
+      a.sess[i].base = layer_base(c, layer);
+      a.sess[i].cap = c->lg[layer].g.cap;
       a.sess[i].len = c->len[layer];
       a.sess[i].row = r;
     }
@@ -656,7 +731,7 @@ int chunk_prepare(const kv_cache* cache, int layer, int n_q_heads, int64_t n_new
   p->mtiles = ceil_div(p->rows, kChunkRows);
   if (p->mtiles > 0x7fffffff) return fail(KV_EUNSUPPORTED, "chunk of %lld rows is too large", (long long)p->rows);
   p->base = p->mtiles * cache->hkv;
-  p->slots = resident_slots(cache->device, chunk_kernel_for(cache->kbits, cache->vbits, cache->d, false),
+  p->slots = resident_slots(cache->device, chunk_kernel_for(cache->lg[layer].kbits, cache->lg[layer].vbits, cache->d, false),
                             kChunkThreads);
   return KV_OK;
 }
@@ -671,8 +746,8 @@ int chunk_launch(kv_cache* cache, int layer, const ChunkPrep& p, const void* q, 
                  hipStream_t st) {
   ChunkArgs a;
   memset(&a, 0, sizeof(a));
-  a.base = cache->arena + (int64_t)layer * cache->hkv * cache->g.region();
-  a.g = cache->g;
+  a.base = layer_base(cache, layer);
+  a.g = cache->lg[layer].g;
   a.len = p.len;
   a.n_new = n_new;
   a.hkv = cache->hkv;
@@ -686,7 +761,7 @@ int chunk_launch(kv_cache* cache, int layer, const ChunkPrep& p, const void* q, 
   a.qk_scale = sm_scale * 1.4426950408889634f;
   a.ws = ws;
   a.out = out;
-  hipError_t e = launch_chunk(a, cache->kbits, cache->vbits, cache->d, st);
+  hipError_t e = launch_chunk(a, cache->lg[layer].kbits, cache->lg[layer].vbits, cache->d, st);
   if (e != hipSuccess) return hip_fail(cache, e, "chunk launch");
   return KV_OK;
 }

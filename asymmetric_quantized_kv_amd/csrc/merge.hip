@@ -1,9 +1,13 @@
 // Second pass of split attention: combine per-split partials (o unnormalized,
 // m = running max in log2 units, l = sum of 2^(s - m)) into the normalized output,
 //   M = max_s m_s,  o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
-// One wave per output row; lanes stride over head_dim.  Splits that saw no token
-// carry m = -inf and l = 0 and drop out.
+// One wave per output row.  Lane s loads split s's (m, l), so the statistics of up to 64
+// splits take one round trip; the weights w_s = 2^(m_s - M) / L then go to every lane
+// through readlane, and each lane sums the splits for its elements of head_dim with the
+// loads of several splits in flight.  Splits that saw no token carry m = -inf, l = 0 and
+// weigh nothing.
 #include "kvq_internal.h"
+#include "wave_ops.h"
 
 namespace kvq {
 namespace {
@@ -11,24 +15,44 @@ namespace {
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= a.rows) return;
+  if (row >= a.rows) return;   // wave-uniform
   const int stride = a.d + 2;
   const float* p = a.ws + row * a.n_splits * stride;
+  // statistics, 64 splits at a time
   float M = -INFINITY;
-  for (int s = 0; s < a.n_splits; ++s) M = fmaxf(M, p[s * stride + a.d]);
-  float l = 0.f;
-  for (int s = 0; s < a.n_splits; ++s) {
-    const float ms = p[s * stride + a.d];
-    if (ms != -INFINITY) l += __builtin_amdgcn_exp2f(ms - M) * p[s * stride + a.d + 1];
+  for (int s0 = 0; s0 < a.n_splits; s0 += 64) {
+    const float ms = s0 + lane < a.n_splits ? p[(s0 + lane) * stride + a.d] : -INFINITY;
+    M = fmaxf(M, wave_max(ms));
   }
-  const float inv = 1.f / l;
-  for (int e = lane; e < a.d; e += 64) {
-    float o = 0.f;
-    for (int s = 0; s < a.n_splits; ++s) {
+  float L = 0.f;
+  for (int s0 = 0; s0 < a.n_splits; s0 += 64) {
+    const int s = s0 + lane;
+    float w = 0.f;
+    if (s < a.n_splits) {
       const float ms = p[s * stride + a.d];
-      if (ms != -INFINITY) o += __builtin_amdgcn_exp2f(ms - M) * p[s * stride + e];
+      if (ms != -INFINITY) w = __builtin_amdgcn_exp2f(ms - M) * p[s * stride + a.d + 1];
     }
-    a.out[row * a.d + e] = o * inv;
+    L += wave_sum(w);
+  }
+  const float inv = 1.f / L;
+  for (int e0 = 0; e0 < a.d; e0 += 64) {
+    const int e = e0 + lane;
+    float o = 0.f;
+    for (int s0 = 0; s0 < a.n_splits; s0 += 64) {
+      const int s = s0 + lane;
+      float w = 0.f;   // this lane's split weight, handed to every lane below
+      if (s < a.n_splits) {
+        const float ms = p[s * stride + a.d];
+        if (ms != -INFINITY) w = __builtin_amdgcn_exp2f(ms - M) * inv;
+      }
+      const int n = min(64, a.n_splits - s0);
+#pragma unroll 8
+      for (int j = 0; j < n; ++j) {
+        const float wj = readlane(w, j);
+        if (e < a.d) o = fmaf(wj, p[(s0 + j) * stride + e], o);
+      }
+    }
+    if (e < a.d) a.out[row * a.d + e] = o;
   }
 }
 

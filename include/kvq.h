@@ -82,6 +82,18 @@ typedef struct kv_cache kv_cache;
 kv_cache* kv_cache_create(int layout, int n_layers, int n_kv_heads, int head_dim,
                           int64_t max_tokens);
 
+/* The same with a layout per layer: layer l stores its keys and values as layouts[l]
+ * (layer-specific quantization, planned in the KVSplit page, section "Configuracao
+ * recomendada e roadmap").
+ * layouts: host array of n_layers layout codes.  Every entry point then works per layer
+ * in that layer's layout; a decode call over several sessions needs them to share the
+ * layer's layout.  Errors as kv_cache_create. */
+kv_cache* kv_cache_create_layered(const int* layouts, int n_layers, int n_kv_heads, int head_dim,
+                                  int64_t max_tokens);
+
+/* Layout code of one layer; < 0 on bad arguments. */
+int kv_cache_layout(const kv_cache* cache, int layer);
+
 /* Free the arena.  The caller ensures no queued work still uses the cache.  NULL is a no-op. */
 void kv_cache_destroy(kv_cache* cache);
 
@@ -195,6 +207,10 @@ int64_t kv_footprint_bytes(const kv_cache* cache);
 int64_t kv_layout_footprint_bytes(int layout, int n_layers, int n_kv_heads, int head_dim,
                                   int64_t max_tokens);
 
+/* The footprint of a cache with a layout per layer: the sum of the layers' footprints. */
+int64_t kv_layered_footprint_bytes(const int* layouts, int n_layers, int n_kv_heads, int head_dim,
+                                   int64_t max_tokens);
+
 /* Cached tokens of `layer` (as enqueued); < 0 on bad arguments. */
 int64_t kv_cache_len(const kv_cache* cache, int layer);
 
@@ -225,10 +241,11 @@ int kv_cache_copy_plane(const kv_cache* cache, int layer, int kv_head, int plane
  * Descobertas e Benchmarks": sessions are kept between turns; "KV Cache Offloading for
  * Context-Intensive Tasks", gist.science: KV moved to host memory and reloaded on demand).
  *
- * Saved form: a 32-byte header (magic "KVQS", version 1, layout, n_layers, n_kv_heads,
- * head_dim as 32-bit integers, 8 reserved bytes), one int64 cached length per layer, zero
- * padding to a multiple of 64 bytes, then for every layer and KV head the first len[layer]
- * rows of the planes KC, KS, VC, VS in that order (row bytes as kv_cache_plane reports).
+ * Saved form: a 32-byte header (magic "KVQS", version 2, the layout of every layer or -1
+ * when layers differ, n_layers, n_kv_heads, head_dim as 32-bit integers, 8 zero bytes), one
+ * int64 cached length per layer, one int32 layout per layer, zero padding to a multiple of
+ * 64 bytes, then for every layer and KV head the first len[layer] rows of the planes KC,
+ * KS, VC, VS in that order (row bytes as kv_cache_plane reports).
  *
  * kv_session_bytes: size of that form for the cache as it stands; < 0 for a NULL cache.
  * kv_session_save: writes it to dst, which must be host memory (pinned memory from
@@ -237,8 +254,8 @@ int kv_cache_copy_plane(const kv_cache* cache, int layer, int kv_head, int plane
  *   land when `stream` passes the call.  The cache is unchanged.
  *   Errors: KV_EINVAL (NULL or device dst, dst_bytes too small), KV_EHIP.
  * kv_session_load: replaces the contents of `cache` with a saved session read from host
- *   memory src.  The header must match the cache's (layout, n_layers, n_kv_heads,
- *   head_dim).  Lengths take the saved values when the call is enqueued; rows past them
+ *   memory src.  The header must match the cache's (n_layers, n_kv_heads, head_dim and
+ *   every layer's layout).  Lengths take the saved values when the call is enqueued; rows past them
  *   are left as they are.
  *   Errors: KV_EINVAL (NULL or device src, bad magic or version, shape mismatch, src_bytes
  *   too small), KV_ECAPACITY (a saved length above max_tokens), KV_EHIP.  On an error

@@ -53,7 +53,7 @@ __all__ = [
     "LAYOUTS", "LAYOUT_IDS", "BLOCK", "GRANULE", "layout_bits", "code_row_bytes",
     "scale_row_bytes", "capacity", "layout_footprint_bytes", "f32_to_f16",
     "block_scale", "rhaz", "quantize_rows", "pack_codes", "unpack_codes",
-    "pack_scales", "unpack_scales", "encode_rows", "dequant_rows", "OracleCache",
+    "pack_scales", "unpack_scales", "encode_rows", "dequant_rows", "OracleCache", "OracleLayeredCache",
     "attend_decode", "attend_chunk", "attention_exact", "to_f32",
     "split_partial", "merge_partials", "decode_partials", "chunk_partials", "LOG2E",
 ]
@@ -255,6 +255,42 @@ class OracleCache:
         t1 = self.len[layer] if t1 is None else t1
         return dequant_rows(self.Vc[layer, kv_head, :t1], self.Vs[layer, kv_head, :t1],
                             self.vbits, self.D)
+
+
+class OracleLayeredCache:
+    """A cache whose layer l stores its keys and values in layouts[l] (layer-specific
+    quantization, planned on the KVSplit page, section "Configuracao recomendada e
+    roadmap"): one single-layer OracleCache per layer, with the same interface."""
+
+    def __init__(self, layouts, n_kv_heads: int, head_dim: int, max_tokens: int):
+        self.layouts = [int(x) for x in layouts]
+        self.layers = [OracleCache(lay, 1, n_kv_heads, head_dim, max_tokens) for lay in self.layouts]
+        self.L, self.Hkv, self.D = len(self.layouts), n_kv_heads, head_dim
+        self.max_tokens, self.cap = int(max_tokens), capacity(max_tokens)
+
+    @property
+    def len(self):
+        return [c.len[0] for c in self.layers]
+
+    def footprint_bytes(self) -> int:
+        return sum(c.footprint_bytes() for c in self.layers)
+
+    def append(self, layer: int, k, v) -> None:
+        self.layers[layer].append(0, k, v)
+
+    def reset(self) -> None:
+        for c in self.layers:
+            c.reset()
+
+    def plane(self, layer: int, name: str) -> np.ndarray:
+        """Plane `name` (Kc, Ks, Vc, Vs) of one layer: [Hkv, cap, row bytes]."""
+        return getattr(self.layers[layer], name)[0]
+
+    def keys(self, layer: int, kv_head: int, t1: int | None = None) -> np.ndarray:
+        return self.layers[layer].keys(0, kv_head, t1)
+
+    def values(self, layer: int, kv_head: int, t1: int | None = None) -> np.ndarray:
+        return self.layers[layer].values(0, kv_head, t1)
 
 
 # --------------------------------------------------------------------------

@@ -49,6 +49,15 @@ def test_layout_footprint_matches_oracle(layout):
         assert kvq.kv_layout_footprint_bytes(layout, L, hkv, d, t) == O.layout_footprint_bytes(layout, L, hkv, d, t)
 
 
+def test_layered_footprint_matches_oracle():
+    for layouts in ([2], [0, 1, 2, 3, 4], [1] * 11 + [4] * 11, [3, 0, 3]):
+        for hkv, d, t in ((4, 64, 8192), (8, 128, 100_500), (3, 96, 1)):
+            want = O.OracleLayeredCache(layouts, hkv, d, t).footprint_bytes()
+            assert kvq.kv_layered_footprint_bytes(layouts, hkv, d, t) == want
+    with pytest.raises(kvq.KVError):
+        kvq.kv_layered_footprint_bytes([2, 9], 4, 64, 100)
+
+
 @pytest.mark.parametrize("args,code", [
     ((7, 1, 4, 64, 100), kvq.KV_EINVAL),       # layout
     ((2, 0, 4, 64, 100), kvq.KV_EINVAL),       # n_layers
@@ -83,6 +92,8 @@ def test_null_handles_are_rejected(built_library):
     assert L.kv_chunk_plan(None, 0, 4, 1, C.byref(n), C.byref(t)) == kvq.KV_EINVAL
     assert L.kv_attend_decode_partial(None, 1, 0, None, 0, 4, 0.1, 1, 512, None, 0, None) == kvq.KV_EINVAL
     assert L.kv_attend_chunk_partial(None, 0, None, 0, 4, 1, 0.1, 1, 64, None, 0, None) == kvq.KV_EINVAL
+    assert L.kv_cache_layout(None, 0) == kvq.KV_EINVAL
+    assert L.kv_cache_create_layered(None, 2, 4, 64, 100) is None and kvq.kv_last_status() == kvq.KV_EINVAL
     assert L.kv_session_bytes(None) == kvq.KV_EINVAL
     assert L.kv_session_save(None, None, 0, None) == kvq.KV_EINVAL
     assert L.kv_session_load(None, None, 0, None) == kvq.KV_EINVAL

@@ -33,16 +33,18 @@ def parse_saved(buf: np.ndarray, oc: O.OracleCache):
     """Split a saved session (documented format) into header fields and per-plane rows."""
     magic, version, layout, n_layers, hkv, d, _ = struct.unpack_from("<IIiiiiq", buf, 0)
     lens = list(struct.unpack_from(f"<{n_layers}q", buf, 32))
-    off = -(-(32 + 8 * n_layers) // 64) * 64
+    layouts = list(struct.unpack_from(f"<{n_layers}i", buf, 32 + 8 * n_layers))
+    off = -(-(32 + 12 * n_layers) // 64) * 64
     planes = {}
     for l in range(n_layers):
         for h in range(hkv):
             for name, _ in PLANES:
-                rb = getattr(oc, name).shape[-1]
+                plane = oc.plane(l, name) if hasattr(oc, "plane") else getattr(oc, name)[l]
+                rb = plane.shape[-1]
                 n = lens[l] * rb
                 planes[(l, h, name)] = buf[off:off + n].reshape(lens[l], rb)
                 off += n
-    return (magic, version, layout, n_layers, hkv, d), lens, planes, off
+    return (magic, version, layout, n_layers, hkv, d), lens, layouts, planes, off
 
 
 def filled_pair(layout, dtype="bf16"):
@@ -71,8 +73,10 @@ def test_save_restore_round_trip(layout, pinned):
         kvq.kv_session_save(h, buf)
         torch.cuda.synchronize()
         host = buf.numpy() if pinned else buf
-        hdr, lens, planes, end = parse_saved(host, oc)
-        assert hdr == (0x5351564B, 1, O.LAYOUT_IDS[layout], 2, 3, 64) and lens == [700, 333] and end == nbytes
+        hdr, lens, layouts, planes, end = parse_saved(host, oc)
+        lid = O.LAYOUT_IDS[layout]
+        assert hdr == (0x5351564B, 2, lid, 2, 3, 64) and lens == [700, 333] and layouts == [lid, lid]
+        assert end == nbytes
         for (l, hh, name), rows in planes.items():
             assert np.array_equal(rows, getattr(oc, name)[l, hh, :lens[l]]), (l, hh, name)
         kvq.kv_session_load(h2, buf)

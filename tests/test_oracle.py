@@ -500,3 +500,34 @@ def test_merge_is_invariant_to_the_reference_of_each_split():
     shift = np.array([0.0, 3.5, -7.0])
     got = O.merge_partials(o * np.exp2(shift)[..., None], m - shift, l * np.exp2(shift))
     assert np.max(np.abs(got - O.merge_partials(o, m, l))) <= 1e-12
+
+
+# ---------------------------------------------------------------------------
+# layer-specific layouts
+# ---------------------------------------------------------------------------
+def test_layered_footprint_is_the_mix_of_printed_rows():
+    """Half the 22 layers in K8V8 and half in K4V4 take the mean of the two printed
+    footprints at 8192 tokens, (93.50 + 49.50) / 2 = 71.50 MiB; FP16 with K8V4 gives
+    (176.00 + 71.50) / 2 = 123.75 MiB."""
+    mib = 2 ** 20
+    mix = [1] * 11 + [4] * 11
+    c = O.OracleLayeredCache(mix, 4, 64, 8192)
+    assert c.footprint_bytes() == 71.50 * mib
+    c2 = O.OracleLayeredCache([0, 2] * 11, 4, 64, 8192)
+    assert c2.footprint_bytes() == 123.75 * mib
+
+
+def test_layered_layers_equal_uniform_caches():
+    """Layer l of a layered cache holds exactly the bytes a uniform cache of layouts[l]
+    holds after the same appends, and attention over it is the same."""
+    layouts = [0, 1, 2, 3, 4]
+    lc = O.OracleLayeredCache(layouts, 2, 64, 300)
+    for l, lay in enumerate(layouts):
+        k, v, q = I.workload_small(60 + l, 50 + 40 * l, 2, 64, 4, 1, n_outliers=2)
+        lc.append(l, k, v)
+        uc = O.OracleCache(lay, 1, 2, 64, 300)
+        uc.append(0, k, v)
+        for name in ("Kc", "Ks", "Vc", "Vs"):
+            assert np.array_equal(lc.plane(l, name), getattr(uc, name)[0])
+        assert np.array_equal(O.attend_decode([lc], l, q, 0.125), O.attend_decode([uc], 0, q, 0.125))
+    assert lc.len == [50, 90, 130, 170, 210]
