@@ -54,13 +54,14 @@ __all__ = [
     "scale_row_bytes", "capacity", "layout_footprint_bytes", "f32_to_f16",
     "block_scale", "rhaz", "quantize_rows", "pack_codes", "unpack_codes",
     "pack_scales", "unpack_scales", "encode_rows", "dequant_rows", "OracleCache", "OracleLayeredCache",
+    "E4M3_MAX", "e4m3_values", "e4m3_encode", "mx_scale_exponent", "mx_quantize_rows", "mx_dequant_rows",
     "attend_decode", "attend_chunk", "attention_exact", "to_f32",
     "split_partial", "merge_partials", "decode_partials", "chunk_partials", "LOG2E",
 ]
 
 #: layout id -> (name, key bits, value bits).  16 means the fp16 control.
 LAYOUTS = {0: ("FP16", 16, 16), 1: ("K8V8", 8, 8), 2: ("K8V4", 8, 4),
-           3: ("K4V8", 4, 8), 4: ("K4V4", 4, 4)}
+           3: ("K4V8", 4, 8), 4: ("K4V4", 4, 4), 5: ("KF8V4", "f8", 4)}
 LAYOUT_IDS = {v[0]: k for k, v in LAYOUTS.items()}
 BLOCK = 32          # elements per quantization block (reading; see module doc)
 GRANULE = 256       # capacity granule in tokens (reading; see module doc)
@@ -73,14 +74,17 @@ def layout_bits(layout: int) -> tuple[int, int]:
     return kb, vb
 
 
-def code_row_bytes(bits: int, head_dim: int) -> int:
-    """Bytes of codes per (token, KV head): 2D for fp16, D for 8-bit, D/2 for 4-bit."""
-    return {16: 2 * head_dim, 8: head_dim, 4: head_dim // 2}[bits]
+def code_row_bytes(bits, head_dim: int) -> int:
+    """Bytes of codes per (token, KV head): 2D for fp16, D for 8-bit and fp8, D/2 for 4-bit."""
+    return {16: 2 * head_dim, 8: head_dim, "f8": head_dim, 4: head_dim // 2}[bits]
 
 
-def scale_row_bytes(bits: int, head_dim: int) -> int:
-    """Bytes of fp16 scales per (token, KV head): one per 32-element block; none for fp16."""
-    return 0 if bits == 16 else 2 * (head_dim // BLOCK)
+def scale_row_bytes(bits, head_dim: int) -> int:
+    """Bytes of scales per (token, KV head), one per 32-element block: fp16 (2 bytes) for
+    8/4-bit codes, a power-of-two exponent byte for fp8 codes; none for fp16."""
+    if bits == 16:
+        return 0
+    return (1 if bits == "f8" else 2) * (head_dim // BLOCK)
 
 
 def capacity(max_tokens: int) -> int:
@@ -185,19 +189,98 @@ def unpack_scales(packed) -> np.ndarray:
     return p.view("<f2").reshape(p.shape[0], -1)
 
 
-def encode_rows(x, bits: int):
+def encode_rows(x, bits):
     """Rows [n, D] -> (code bytes [n, cb], scale bytes [n, sb] or None)."""
+    if bits == "f8":
+        return mx_quantize_rows(x)
     codes, d16 = quantize_rows(x, bits)
     return pack_codes(codes, bits), (None if d16 is None else pack_scales(d16))
 
 
-def dequant_rows(code_bytes, scale_bytes, bits: int, head_dim: int) -> np.ndarray:
+def dequant_rows(code_bytes, scale_bytes, bits, head_dim: int) -> np.ndarray:
     """x_hat = q * d per element (exact in fp64), or the fp16 value for the control."""
+    if bits == "f8":
+        return mx_dequant_rows(code_bytes, scale_bytes)
     c = unpack_codes(code_bytes, bits, head_dim)
     if bits == 16:
         return c.astype(np.float64)
     d = unpack_scales(scale_bytes).astype(np.float64)
     return c.astype(np.float64) * np.repeat(d, BLOCK, axis=1)
+
+
+# --------------------------------------------------------------------------
+# fp8 keys: OCP MX "MXFP8" blocks (reading of the offloading page's FP8 alternative,
+# "KV Cache Offloading for Context-Intensive Tasks", section on quantization)
+# --------------------------------------------------------------------------
+# Each 32-element block stores one shared power-of-two scale X = 2^e as a biased exponent
+# byte (e + 127) and 32 elements y = x / X as OCP FP8 E4M3 codes: sign, 4 exponent bits
+# (bias 7), 3 mantissa bits, subnormals, no infinities, S.1111.111 = NaN, largest 448.
+# e = floor(log2(amax)) - 8 (8 = the largest E4M3 exponent), clamped to [-127, 127]
+# (e = -127 for an all-zero block); elements round to nearest, ties to even, saturate at
+# +-448, and a result of zero is stored as +0.
+E4M3_MAX = 448.0
+
+
+def e4m3_values() -> np.ndarray:
+    """The value of each of the 256 E4M3 codes (NaN for 0x7F and 0xFF)."""
+    v = np.empty(256, np.float64)
+    for c in range(256):
+        sign = -1.0 if c & 0x80 else 1.0
+        e, m = (c >> 3) & 15, c & 7
+        if e == 15 and m == 7:
+            v[c] = np.nan
+        elif e == 0:
+            v[c] = sign * m * 2.0 ** -9
+        else:
+            v[c] = sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return v
+
+
+def e4m3_encode(y) -> np.ndarray:
+    """E4M3 codes of exact values y (fp64): round to nearest, ties to even, saturate."""
+    y = np.asarray(y, dtype=np.float64)
+    a = np.abs(y)
+    code = np.zeros(y.shape, np.int64)
+    sat = a >= E4M3_MAX
+    sub = a < 2.0 ** -6
+    norm = ~sat & ~sub
+    code[sat] = 0x7E
+    code[sub] = np.rint(a[sub] * 2.0 ** 9).astype(np.int64)          # 8 lands on 2^-6 = 0x08
+    _, k = np.frexp(a[norm])
+    e = k.astype(np.int64) - 1                                        # floor(log2 a), -6..8
+    m = np.rint(a[norm] * np.exp2(3.0 - e)).astype(np.int64)           # 8..16
+    up = m == 16
+    e[up] += 1
+    m[up] = 8
+    code[norm] = ((e + 7) << 3) | (m - 8)
+    code[norm & (code == 0x7F)] = 0x7E
+    code[(y < 0) & (code != 0)] |= 0x80
+    return code.astype(np.uint8)
+
+
+def mx_scale_exponent(amax32) -> np.ndarray:
+    """e of X = 2^e for block maxima amax (fp32): floor(log2 amax) - 8 in [-127, 127]."""
+    a = np.asarray(amax32, dtype=np.float64)
+    _, k = np.frexp(a)
+    e = np.where(a > 0, k.astype(np.int64) - 1 - 8, -127)
+    return np.clip(e, -127, 127)
+
+
+def mx_quantize_rows(x):
+    """Rows [n, D] -> (E4M3 code bytes [n, D], scale exponent bytes [n, D/32])."""
+    x32 = to_f32(x)
+    n, dim = x32.shape
+    xb = x32.reshape(n, dim // BLOCK, BLOCK).astype(np.float64)
+    e = mx_scale_exponent(np.max(np.abs(xb), axis=2).astype(np.float32))
+    codes = e4m3_encode(xb * np.exp2(-e.astype(np.float64))[:, :, None])
+    return codes.reshape(n, dim), (e + 127).astype(np.uint8)
+
+
+def mx_dequant_rows(code_bytes, scale_bytes) -> np.ndarray:
+    """x_hat = E4M3 value * 2^(scale byte - 127), exact in fp64."""
+    c = np.asarray(code_bytes, dtype=np.uint8)
+    e = np.asarray(scale_bytes, dtype=np.uint8).astype(np.float64) - 127.0
+    return e4m3_values()[c] * np.repeat(np.exp2(e), BLOCK, axis=1)
 
 
 # --------------------------------------------------------------------------

@@ -531,3 +531,75 @@ def test_layered_layers_equal_uniform_caches():
             assert np.array_equal(lc.plane(l, name), getattr(uc, name)[0])
         assert np.array_equal(O.attend_decode([lc], l, q, 0.125), O.attend_decode([uc], 0, q, 0.125))
     assert lc.len == [50, 90, 130, 170, 210]
+
+
+# ---------------------------------------------------------------------------
+# fp8 keys (MXFP8 blocks)
+# ---------------------------------------------------------------------------
+def test_e4m3_table_structure():
+    """The code table of the OCP E4M3 definition: zero, subnormals k * 2^-9, normals
+    (1 + m/8) 2^(e-7), largest 448, NaN only at S.1111.111, symmetric in the sign bit,
+    and strictly increasing over the positive codes."""
+    v = O.e4m3_values()
+    assert v[0x00] == 0 and v[0x01] == 2.0 ** -9 and v[0x07] == 7 * 2.0 ** -9
+    assert v[0x08] == 2.0 ** -6 and v[0x38] == 1.0 and v[0x3F] == 1.875 and v[0x7E] == 448
+    assert np.isnan(v[0x7F]) and np.isnan(v[0xFF]) and np.sum(np.isnan(v)) == 2
+    assert np.array_equal(v[0x80:0xFF], -v[0x00:0x7F])
+    assert np.all(np.diff(v[0x00:0x7F]) > 0)
+
+
+def brute_e4m3(y: float) -> int:
+    """Nearest finite E4M3 code by exhaustive search: ties to the even code, saturate, +0."""
+    v = O.e4m3_values()
+    pos = [(c, v[c]) for c in range(0x7F)]
+    a = min(abs(y), 448.0)
+    best = min(pos, key=lambda cv: (abs(cv[1] - a), cv[0] & 1))
+    c = best[0]
+    return (c | 0x80) if (y < 0 and c != 0) else c
+
+
+def test_e4m3_encode_matches_exhaustive_search():
+    rng = np.random.default_rng(11)
+    v = O.e4m3_values()
+    mids = [(v[c] + v[c + 1]) / 2 for c in range(0x7E)]            # every tie
+    ys = list(rng.standard_normal(300) * 40) + list(rng.uniform(-0.02, 0.02, 200)) + mids
+    ys += [-m for m in mids] + [0.0, -0.0, 447.9, 448.0, 463.99, 464.0, 500.0, -511.0, 2.0 ** -10, 3 * 2.0 ** -11]
+    got = O.e4m3_encode(np.array(ys))
+    for y, c in zip(ys, got):
+        assert int(c) == brute_e4m3(y), (y, int(c), brute_e4m3(y))
+
+
+def test_mx_scale_brackets_the_block_maximum():
+    """X = 2^e with 256 X <= amax < 512 X (amax / X has exponent 8, E4M3's largest);
+    an all-zero block gets e = -127 and zero codes."""
+    rng = np.random.default_rng(12)
+    amax = np.abs(rng.standard_normal(1000) * np.exp(rng.uniform(-20, 20, 1000))).astype(np.float32)
+    e = O.mx_scale_exponent(amax)
+    for a, ee in zip(amax.astype(np.float64), e):
+        assert Fraction(256) * Fraction(2) ** int(ee) <= Fraction(a) < Fraction(512) * Fraction(2) ** int(ee)
+    codes, sc = O.mx_quantize_rows(np.zeros((1, 64), np.float32))
+    assert not codes.any() and np.all(sc == 0)
+
+
+def test_mxfp8_dequant_error_bound():
+    """Outside saturation an element is within half an E4M3 spacing of its value: 2^-4 of
+    its binade (2^-10 X in the subnormal range); the saturated block maximum is off by at
+    most 64 X."""
+    x = I.normal((50, 128), 13, 1) * np.float32(3.0)
+    x[:, 5] *= 30
+    codes, sc = O.mx_quantize_rows(x)
+    xh = O.mx_dequant_rows(codes, sc)
+    X = np.repeat(np.exp2(sc.astype(np.float64) - 127), 32, axis=1)
+    a = np.abs(x.astype(np.float64)) / X
+    err = np.abs(x - xh) / X
+    sat = a >= 448
+    binade = np.exp2(np.floor(np.log2(np.maximum(a, 2.0 ** -6))))
+    assert np.all(err[~sat] <= binade[~sat] * 2.0 ** -4 + 1e-12)
+    assert np.all(err[sat] <= 64)
+
+
+def test_kf8v4_footprint():
+    """fp8 key rows are D code bytes + D/32 exponent bytes; 4-bit value rows as in K8V4."""
+    for d in (64, 128):
+        per = (d + d // 32) + (d // 2 + 2 * d // 32)
+        assert O.layout_footprint_bytes(5, 2, 3, d, 300) == 2 * 3 * 512 * per
