@@ -7,7 +7,7 @@ generators.  Importing the package does not load the library; the first call doe
 from ._lib import (  # noqa: F401
     KVError, LIB_PATH, LAYOUT_IDS,
     KV_OK, KV_EINVAL, KV_ECAPACITY, KV_ENOMEM, KV_EUNSUPPORTED, KV_EEMPTY, KV_EHIP,
-    KV_FP16, KV_K8V8, KV_K8V4, KV_K4V8, KV_K4V4, KV_F32, KV_BF16, KV_F16,
+    KV_FP16, KV_K8V8, KV_K8V4, KV_K4V8, KV_K4V4, KV_KF8V4, KV_F32, KV_BF16, KV_F16,
     KV_PLANE_KC, KV_PLANE_KS, KV_PLANE_VC, KV_PLANE_VS,
     lib, kv_cache_create, kv_cache_create_layered, kv_cache_layout, kv_layered_footprint_bytes, kv_cache_destroy, kv_append_quant, kv_attend_decode,
     kv_decode_workspace_bytes, kv_decode_plan, kv_attend_decode_partial, kv_merge_partials,

@@ -12,10 +12,10 @@ from pathlib import Path
 LIB_PATH = Path(__file__).resolve().with_name("libkvq.so")
 
 KV_OK, KV_EINVAL, KV_ECAPACITY, KV_ENOMEM, KV_EUNSUPPORTED, KV_EEMPTY, KV_EHIP = 0, -1, -2, -3, -4, -5, -6
-KV_FP16, KV_K8V8, KV_K8V4, KV_K4V8, KV_K4V4 = 0, 1, 2, 3, 4
+KV_FP16, KV_K8V8, KV_K8V4, KV_K4V8, KV_K4V4, KV_KF8V4 = 0, 1, 2, 3, 4, 5
 KV_F32, KV_BF16, KV_F16 = 0, 1, 2
 KV_PLANE_KC, KV_PLANE_KS, KV_PLANE_VC, KV_PLANE_VS = 0, 1, 2, 3
-LAYOUT_IDS = {"FP16": 0, "K8V8": 1, "K8V4": 2, "K4V8": 3, "K4V4": 4}
+LAYOUT_IDS = {"FP16": 0, "K8V8": 1, "K8V4": 2, "K4V8": 3, "K4V4": 4, "KF8V4": 5}
 STATUS_NAMES = {0: "KV_OK", -1: "KV_EINVAL", -2: "KV_ECAPACITY", -3: "KV_ENOMEM",
                 -4: "KV_EUNSUPPORTED", -5: "KV_EEMPTY", -6: "KV_EHIP"}
 

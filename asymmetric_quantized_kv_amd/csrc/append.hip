@@ -7,6 +7,10 @@
 // are contiguous, the block's amax is reduced over the 8 lanes, and every lane encodes
 // its own 4 elements.  Rounding follows the format fixed in include/kvq.h: fp32 IEEE
 // division, fp16 round-to-nearest-even for the scale, round-half-away for the codes.
+// fp8 keys (OCP MX blocks: a power-of-two block scale and E4M3 codes, the FP8
+// alternative of "KV Cache Offloading for Context-Intensive Tasks", section
+// "2. Metodologia") take the exponent from the amax's fp32 bits; the division by a
+// power of two is exact and the E4M3 rounding is done in fp32 integer steps.
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -41,6 +45,25 @@ __device__ __forceinline__ uint16_t f16_bits(float x) {
   return b;
 }
 
+// E4M3 code of an exact fp32 value y: nearest, ties to even, saturated at +-448, +0 for 0.
+__device__ __forceinline__ uint32_t e4m3_code(float y) {
+  const float a = fabsf(y);
+  uint32_t c;
+  if (a >= 448.f) {
+    c = 0x7E;
+  } else if (a < 0.015625f) {                       // below 2^-6: multiples of 2^-9
+    c = (uint32_t)rintf(a * 512.f);                 // 8 lands on 2^-6, code 0x08
+  } else {
+    int ex = (int)((__float_as_uint(a) >> 23) & 255) - 127;             // -6 .. 8
+    const float up = __uint_as_float((uint32_t)(127 + 3 - ex) << 23);   // 2^(3 - ex)
+    uint32_t mm = (uint32_t)rintf(a * up);          // 8 .. 16, exact product
+    if (mm == 16) { ++ex; mm = 8; }
+    c = ((uint32_t)(ex + 7) << 3) | (mm - 8);
+    if (c == 0x7F) c = 0x7E;                        // 480 is not a number in E4M3
+  }
+  return (y < 0.f && c != 0) ? (c | 0x80u) : c;
+}
+
 template <int BITS, int DT, int D>
 __device__ __forceinline__ void encode_one(const void* src, uint8_t* region, const Geom& g,
                                            int64_t row, int64_t elem, int blk, int sub,
@@ -53,6 +76,21 @@ __device__ __forceinline__ void encode_one(const void* src, uint8_t* region, con
     uint32_t lo = f16_bits(x[0]) | ((uint32_t)f16_bits(x[1]) << 16);
     uint32_t hi = f16_bits(x[2]) | ((uint32_t)f16_bits(x[3]) << 16);
     *reinterpret_cast<uint2*>(codes + (blk * 32 + sub * 4) * 2) = make_uint2(lo, hi);
+  } else if constexpr (BITS == kF8) {
+    float amax = fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
+    amax = fmaxf(amax, __shfl_xor(amax, 1, 8));
+    amax = fmaxf(amax, __shfl_xor(amax, 2, 8));
+    amax = fmaxf(amax, __shfl_xor(amax, 4, 8));
+    // e = floor(log2 amax) - 8 (the exponent of E4M3's largest binade), in [-127, 127];
+    // a zero or subnormal amax gives -127
+    const int eb = (int)((__float_as_uint(amax) >> 23) & 255);
+    const int e = eb == 0 ? -127 : max(eb - 127 - 8, -127);
+    const float inv = __uint_as_float((uint32_t)(127 - e) << 23);       // 2^-e, normal
+    uint32_t w = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w |= e4m3_code(x[i] * inv) << (8 * i);
+    *reinterpret_cast<uint32_t*>(codes + blk * 32 + sub * 4) = w;
+    if (sub == 0) region[scale_off + row * scale_row + blk] = (uint8_t)(e + 127);
   } else {
     constexpr float qmax = BITS == 8 ? 127.f : 7.f;
     float amax = fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
@@ -139,6 +177,7 @@ hipError_t launch_append(const AppendArgs& a, int kbits, int vbits, int dtype, i
   if (kbits == 8 && vbits == 4) return launch_dt<8, 4>(a, dtype, d, s);
   if (kbits == 4 && vbits == 8) return launch_dt<4, 8>(a, dtype, d, s);
   if (kbits == 4 && vbits == 4) return launch_dt<4, 4>(a, dtype, d, s);
+  if (kbits == kF8 && vbits == 4) return launch_dt<kF8, 4>(a, dtype, d, s);
   return hipErrorInvalidValue;
 }
 

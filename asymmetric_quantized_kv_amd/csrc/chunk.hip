@@ -11,6 +11,8 @@
 // value with a 2^-9 relative error), while fp16 keeps 11 bits at the same MFMA rate.
 // Quantized keys are carried as fp16 hi + lo (code * scale = hi + lo exactly), so scores
 // are exact up to fp32 accumulation; fp32 queries are likewise carried as hi + lo.
+// fp8 (E4M3) keys with power-of-two block scales widen to fp16 exactly in one conversion
+// (v_cvt_scalef32_pk_f16_fp8), so they need no low part: one MFMA per k-step.
 //
 // A workgroup owns 256 rows of one KV head and one split of the context.
 // Per 64-key tile: the workgroup dequantizes K into LDS as [key][d] and V as [d][key]
@@ -105,14 +107,14 @@ __device__ __forceinline__ void k4_pairs(uint32_t w, half2_t (&c)[4]) {
 
 template <int KB, int VB, int D, bool QSPLIT, bool KSPLIT_>
 __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(ChunkArgs a) {
-  constexpr bool KSPLIT = KSPLIT_ && KB != 16;   // fp16 keys are exact already
+  constexpr bool KSPLIT = KSPLIT_ && KB != 16 && KB != kF8;   // fp16 and fp8 keys are exact already
   constexpr int NK = kChunkKeys;   // keys per tile
   constexpr int KSTR = D + 8;      // halves per LDS key row
   constexpr int VSTR = NK + 4;     // halves per LDS transposed-value row (34 dwords: no bank conflicts)
   constexpr int NDT = D / 32;      // 32-wide output blocks along d
   constexpr int NKS = D / 16;      // k-steps of Q.K^T
   constexpr int KE = D / 4;        // key elements one producer thread dequantizes (4 per key)
-  constexpr int KW = KE * KB / 32; // their dwords
+  constexpr int KW = KE * (KB == kF8 ? 8 : KB) / 32;  // their dwords
   constexpr int VW = VB / 4;       // dwords of 8 value elements of one key
   constexpr int VITEMS = (NK / 4) * (D / 8);  // (4 keys x 8 d) value items per tile
   constexpr int KBUF = NK * KSTR, VBUF = D * VSTR;
@@ -163,7 +165,7 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(ChunkArgs a) {
     const int v_kg = pt & 15, v_dg = pt >> 4;
     const bool v_on = pt < VITEMS;
     const uint32_t k_off = k_key * a.g.kc + k_part * (KW * 4);
-    const uint32_t ks_off = k_key * a.g.ks + 2 * ((k_part * KE) / kBlock);
+    const uint32_t ks_off = k_key * a.g.ks + (KB == kF8 ? 1 : 2) * ((k_part * KE) / kBlock);
     const uint32_t v_off = 4 * v_kg * a.g.vc + v_dg * VB;
     const uint32_t vs_off = 4 * v_kg * a.g.vs + 2 * (v_dg >> 2);
     uint32_t kraw[KW];
@@ -173,7 +175,8 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(ChunkArgs a) {
     auto fetch = [&](int t) {
       const int64_t kt0 = k_lo + (int64_t)t * NK;
       load_dw<KW>(kc + kt0 * a.g.kc + k_off, kraw);
-      if constexpr (KB != 16) kscale = *reinterpret_cast<const uint16_t*>(ks + kt0 * a.g.ks + ks_off);
+      if constexpr (KB == kF8) kscale = ks[kt0 * a.g.ks + ks_off];
+      else if constexpr (KB != 16) kscale = *reinterpret_cast<const uint16_t*>(ks + kt0 * a.g.ks + ks_off);
       if (v_on) {
         const uint8_t* vt = vc + kt0 * a.g.vc;
         const uint8_t* vst = vs + kt0 * a.g.vs;
@@ -193,6 +196,15 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(ChunkArgs a) {
         if constexpr (KB == 16) {
 #pragma unroll
           for (int i = 0; i < KE / 2; ++i) hi[i] = h2(kraw[i]);
+        } else if constexpr (KB == kF8) {
+          // E4M3 value * 2^(s - 127), rounded once to fp16: exact while |x| < 65536
+          // (s = 0 reads as 0: 2^-127 times any code is below every fp16)
+          const float x = __uint_as_float((uint32_t)kscale << 23);
+#pragma unroll
+          for (int w = 0; w < KW; ++w) {
+            hi[2 * w] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)kraw[w], x, false);
+            hi[2 * w + 1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)kraw[w], x, true);
+          }
         } else {
           const half2_t d2 = splat(kscale);
 #pragma unroll
@@ -473,11 +485,13 @@ hipError_t launch_chunk(const ChunkArgs& a, int kbits, int vbits, int d, hipStre
   if (kbits == 8 && vbits == 4) return launch_d<8, 4>(a, d, s);
   if (kbits == 4 && vbits == 8) return launch_d<4, 8>(a, d, s);
   if (kbits == 4 && vbits == 4) return launch_d<4, 4>(a, d, s);
+  if (kbits == kF8 && vbits == 4) return launch_d<kF8, 4>(a, d, s);
   return hipErrorInvalidValue;
 }
 
 const void* chunk_kernel_for(int kbits, int vbits, int d, bool q_fp32) {
   if (kbits == 16) return ptr_d<16, 16>(d, q_fp32);
+  if (kbits == kF8) return ptr_d<kF8, 4>(d, q_fp32);
   if (kbits == 8 && vbits == 8) return ptr_d<8, 8>(d, q_fp32);
   if (kbits == 8) return ptr_d<8, 4>(d, q_fp32);
   if (vbits == 8) return ptr_d<4, 8>(d, q_fp32);

@@ -14,7 +14,10 @@
 //   A  scores: integer dot products (v_dot4_i32_i8) of the 8/4-bit key codes with the
 //      query (one scale per head) split into two int8 digits, or fp16 dot2 for the fp16
 //      control; the lanes of one block add their integers, scale by the block's d, and
-//      the block sums are reduced over the LPT lanes with DPP;
+//      the block sums are reduced over the LPT lanes with DPP.  fp8 (E4M3) key codes are
+//      widened to fp16 with the block's power-of-two scale folded into the conversion
+//      (exact), then meet the query (scaled by a power of two into fp16's range, fp32
+//      queries as fp16 hi + lo) in fp16 dot2;
 //   B  one lane per token: the query's scale turns the raw score into a base-2 logit;
 //      exact running max of the chunk per query head, p = 2^(s-m),
 //      the accumulators rescaled only when the max moved;
@@ -74,6 +77,10 @@ __device__ __forceinline__ uint16_t buf_u16(__amdgpu_buffer_rsrc_t r, uint32_t v
   return __builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, (int)soff, 0);
 }
 
+__device__ __forceinline__ uint16_t buf_u8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b8(r, (int)voff, (int)soff, 0);
+}
+
 // a . b over four signed bytes, starting a new sum (the VOP3 form takes the zero as an
 // inline constant; the accumulating two-operand form would need a register cleared first)
 __device__ __forceinline__ int sdot4_start(int a, int b) {
@@ -108,7 +115,9 @@ __device__ __forceinline__ float load_q(const void* q, int dt, int64_t i) {
   return h2f(b);
 }
 
-template <int KB, int VB, int D, int GP, int E>
+// QLO: fp8 keys with fp32 queries, which carry an fp16 low part (16-bit queries are
+// exact in fp16 after the power-of-two prescale)
+template <int KB, int VB, int D, int GP, int E, bool QLO = false>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   constexpr int LPT = D / E;           // lanes per token
   constexpr int TPS = 64 / LPT;        // tokens per half step
@@ -116,9 +125,9 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   constexpr int CT = kDecodeChunk;     // tokens per chunk
   constexpr int NS = CT / STEP;        // steps per chunk
   constexpr int NB = D / kBlock;       // blocks per row
-  constexpr int KW = KB == 16 ? E / 2 : (KB == 8 ? E / 4 : E / 8);  // key dwords per token per lane
+  constexpr int KW = KB == 16 ? E / 2 : (KB == 4 ? E / 8 : E / 4);  // key dwords per token per lane
   constexpr int VW = VB == 16 ? E / 2 : (VB == 8 ? E / 4 : E / 8);  // value dwords per token per lane
-  constexpr int QW = KB == 16 ? E / 2 : E / 4;                       // query dwords per head
+  constexpr int QW = KB == 16 || KB == kF8 ? E / 2 : E / 4;         // query dwords per head
   constexpr int KC = code_row_bytes(KB, D), KS = scale_row_bytes(KB, D);  // row bytes per plane
   constexpr int VC = code_row_bytes(VB, D), VS = scale_row_bytes(VB, D);
   constexpr int LPB = kBlock / E;      // lanes per block (their key codes share one scale)
@@ -127,6 +136,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 
   __shared__ float s_q[GP][D];
   __shared__ float s_qs[GP];
+  __shared__ float s_qi[GP];                               // fp8 keys: power-of-two query prescale
   __shared__ __attribute__((aligned(16))) int8_t s_qa[GP][D];
   __shared__ __attribute__((aligned(16))) int8_t s_qb[GP][D];
   __shared__ float s_sc[4][CT][GP];                        // raw scores of a chunk
@@ -168,6 +178,17 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   for (int g = wave; g < GP; g += 4) {
     if constexpr (KB == 16) {
       if (lane == 0) s_qs[g] = a.qk_scale;
+    } else if constexpr (KB == kF8) {
+      // q' = q * 2^-k with max |q'| in [2^14, 2^15): fp16 holds q' without overflow and
+      // 16-bit queries exactly
+      float amax = 0.f;
+      for (int e = lane; e < D; e += 64) amax = fmaxf(amax, fabsf(s_q[g][e]));
+      amax = wave_max(amax);
+      const int sb = max((int)((__float_as_uint(amax) >> 23) & 255) - 14, 1);
+      if (lane == 0) {
+        s_qi[g] = __uint_as_float((uint32_t)(254 - sb) << 23);
+        s_qs[g] = __uint_as_float((uint32_t)sb << 23) * a.qk_scale;
+      }
     } else {
       float amax = 0.f;
       for (int e = lane; e < D; e += 64) amax = fmaxf(amax, fabsf(s_q[g][e]));
@@ -199,6 +220,15 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 #pragma unroll
       for (int j = 0; j < QW; ++j)
         qa_r[g][j] = __builtin_bit_cast(uint32_t, pack_rne(s_q[g][e0 + 2 * j], s_q[g][e0 + 2 * j + 1]));
+    } else if constexpr (KB == kF8) {
+      const float qi = s_qi[g];
+#pragma unroll
+      for (int j = 0; j < QW; ++j) {
+        const float x0 = s_q[g][e0 + 2 * j] * qi, x1 = s_q[g][e0 + 2 * j + 1] * qi;
+        const half2_t hi = pack_rne(x0, x1);
+        qa_r[g][j] = __builtin_bit_cast(uint32_t, hi);
+        qb_r[g][j] = __builtin_bit_cast(uint32_t, pack_rne(x0 - (float)hi.x, x1 - (float)hi.y));
+      }
     } else if constexpr (KB == 8) {
 #pragma unroll
       for (int j = 0; j < QW; ++j) {
@@ -239,7 +269,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     for (int e = 0; e < E; ++e) acc[g][e] = 0.f;
   }
 
-  const uint32_t koff = grp * KC + sub * (KW * 4), ksoff = grp * KS + blk * 2;
+  const uint32_t koff = grp * KC + sub * (KW * 4), ksoff = grp * KS + blk * (KB == kF8 ? 1 : 2);
   const uint32_t voff = grp * VC + sub * (VW * 4), vsoff = grp * VS + blk * 2;
   const int64_t n_chunks = te > ts ? (te - ts + CT - 1) / CT : 0;
   // Load pipeline: step s of a phase uses ring slot s % R, and the codes of the step
@@ -262,7 +292,10 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     const int slot = s % R;
     buf_dwords<KW>(r.kc, koff, s * STEP * KC, kbuf[slot][0]);
     buf_dwords<KW>(r.kc, koff + TPS * KC, s * STEP * KC, kbuf[slot][1]);
-    if constexpr (KB != 16) {
+    if constexpr (KB == kF8) {
+      kscl[slot][0] = buf_u8(r.ks, ksoff, s * STEP * KS);
+      kscl[slot][1] = buf_u8(r.ks, ksoff + TPS * KS, s * STEP * KS);
+    } else if constexpr (KB != 16) {
       kscl[slot][0] = buf_u16(r.ks, ksoff, s * STEP * KS);
       kscl[slot][1] = buf_u16(r.ks, ksoff + TPS * KS, s * STEP * KS);
     }
@@ -296,7 +329,19 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       const uint32_t* ka = kbuf[s % R][0];
       const uint32_t* kb = kbuf[s % R][1];
       float da = 1.f, db = 1.f;
-      if constexpr (KB != 16) {
+      half2_t fa[KB == kF8 ? 2 * KW : 1], fb[KB == kF8 ? 2 * KW : 1];
+      if constexpr (KB == kF8) {
+        // x_hat = E4M3 value * 2^(s - 127); s = 0 would be 2^-127, below every fp16
+        const float xa = __uint_as_float((uint32_t)kscl[s % R][0] << 23);
+        const float xb = __uint_as_float((uint32_t)kscl[s % R][1] << 23);
+#pragma unroll
+        for (int j = 0; j < KW; ++j) {
+          fa[2 * j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)ka[j], xa, false);
+          fa[2 * j + 1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)ka[j], xa, true);
+          fb[2 * j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)kb[j], xb, false);
+          fb[2 * j + 1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)kb[j], xb, true);
+        }
+      } else if constexpr (KB != 16) {
         da = h2f(kscl[s % R][0]);
         db = h2f(kscl[s % R][1]);
       }
@@ -309,6 +354,22 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
           for (int j = 0; j < KW; ++j) {
             xa = __builtin_amdgcn_fdot2(as_h2(qa_r[g][j]), as_h2(ka[j]), xa, false);
             xb = __builtin_amdgcn_fdot2(as_h2(qa_r[g][j]), as_h2(kb[j]), xb, false);
+          }
+          pa[g] = group_sum<LPT>(xa);
+          pb[g] = group_sum<LPT>(xb);
+        } else if constexpr (KB == kF8) {
+          float xa = 0.f, xb = 0.f;
+#pragma unroll
+          for (int j = 0; j < QW; ++j) {
+            xa = __builtin_amdgcn_fdot2(as_h2(qa_r[g][j]), fa[j], xa, false);
+            xb = __builtin_amdgcn_fdot2(as_h2(qa_r[g][j]), fb[j], xb, false);
+          }
+          if constexpr (QLO) {
+#pragma unroll
+            for (int j = 0; j < QW; ++j) {
+              xa = __builtin_amdgcn_fdot2(as_h2(qb_r[g][j]), fa[j], xa, false);
+              xb = __builtin_amdgcn_fdot2(as_h2(qb_r[g][j]), fb[j], xb, false);
+            }
           }
           pa[g] = group_sum<LPT>(xa);
           pb[g] = group_sum<LPT>(xb);
@@ -519,7 +580,10 @@ template <int KB, int VB, int D, int GP>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
   constexpr int E = lane_elems<GP>();
   dim3 grid(a.n_splits, a.hkv, a.n_sess);
-  hipLaunchKernelGGL((decode_kernel<KB, VB, D, GP, E>), grid, dim3(256), 0, s, a);
+  if (KB == kF8 && a.q_dtype == 0)
+    hipLaunchKernelGGL((decode_kernel<KB, VB, D, GP, E, KB == kF8>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((decode_kernel<KB, VB, D, GP, E>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -562,6 +626,7 @@ const void* ptr_d(int d, int gp) {
 
 const void* decode_kernel_for(int kbits, int vbits, int d, int gp) {
   if (kbits == 16) return ptr_d<16, 16>(d, gp);
+  if (kbits == kF8) return ptr_d<kF8, 4>(d, gp);
   if (kbits == 8 && vbits == 8) return ptr_d<8, 8>(d, gp);
   if (kbits == 8) return ptr_d<8, 4>(d, gp);
   if (vbits == 8) return ptr_d<4, 8>(d, gp);
@@ -574,6 +639,7 @@ hipError_t launch_decode(const DecodeArgs& a, int kbits, int vbits, int d, int g
   if (kbits == 8 && vbits == 4) return launch_d<8, 4>(a, d, gp, s);
   if (kbits == 4 && vbits == 8) return launch_d<4, 8>(a, d, gp, s);
   if (kbits == 4 && vbits == 4) return launch_d<4, 4>(a, d, gp, s);
+  if (kbits == kF8 && vbits == 4) return launch_d<kF8, 4>(a, d, gp, s);
   return hipErrorInvalidValue;
 }
 

@@ -56,8 +56,8 @@ void clear_err() {
 }
 
 bool layout_bits(int layout, int* kb, int* vb) {
-  static const int tab[5][2] = {{16, 16}, {8, 8}, {8, 4}, {4, 8}, {4, 4}};
-  if (layout < 0 || layout > 4) return false;
+  static const int tab[6][2] = {{16, 16}, {8, 8}, {8, 4}, {4, 8}, {4, 4}, {kF8, 4}};
+  if (layout < 0 || layout > 5) return false;
   *kb = tab[layout][0];
   *vb = tab[layout][1];
   return true;
@@ -70,7 +70,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // Shape check shared by kv_cache_create and kv_layout_footprint_bytes.
 int check_shape(int layout, int n_layers, int n_kv_heads, int head_dim, int64_t max_tokens) {
   int kb, vb;
-  if (!layout_bits(layout, &kb, &vb)) return fail(KV_EINVAL, "layout %d is not one of 0..4", layout);
+  if (!layout_bits(layout, &kb, &vb)) return fail(KV_EINVAL, "layout %d is not one of 0..5", layout);
   if (n_layers < 1) return fail(KV_EINVAL, "n_layers must be >= 1 (got %d)", n_layers);
   if (n_kv_heads < 1) return fail(KV_EINVAL, "n_kv_heads must be >= 1 (got %d)", n_kv_heads);
   if (head_dim < 32 || head_dim % 32) return fail(KV_EINVAL, "head_dim must be a positive multiple of 32 (got %d)", head_dim);

@@ -16,11 +16,13 @@ constexpr int kChunkRows = 256;     // query rows per chunk-prefill workgroup (3
 constexpr int kChunkKeys = 64;      // keys per chunk-prefill tile
 constexpr uint32_t kXcds = 8;       // accelerator dies of an MI355X; workgroups are dealt round-robin
 
+constexpr int kF8 = 9;              // "bits" marker of fp8 (E4M3) codes with power-of-two block scales
+
 __host__ __device__ constexpr int code_row_bytes(int bits, int d) {
-  return bits == 16 ? 2 * d : (bits == 8 ? d : d / 2);
+  return bits == 16 ? 2 * d : (bits == 8 || bits == kF8 ? d : d / 2);
 }
 __host__ __device__ constexpr int scale_row_bytes(int bits, int d) {
-  return bits == 16 ? 0 : 2 * (d / kBlock);
+  return bits == 16 ? 0 : (bits == kF8 ? d / kBlock : 2 * (d / kBlock));
 }
 
 // Planes of one (layer, KV head) region, token-major, in this order: KC, KS, VC, VS.

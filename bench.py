@@ -42,6 +42,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing on host cores")
     ap.add_argument("--no-k4v8", action="store_true", help="skip the K4V8 decode on the identical inputs")
+    ap.add_argument("--no-kf8v4", action="store_true", help="skip the fp8-key (KF8V4) decode and chunk")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (for HBM counter calibration)")
     return ap.parse_args()
@@ -93,7 +94,7 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(x)).to(dev).to(torch.bfloat16).contiguous()
 
     # ---- decode workload ---------------------------------------------------------
-    layouts = ["K8V4"] + ([] if args.no_k4v8 else ["K4V8"])
+    layouts = ["K8V4"] + ([] if args.no_k4v8 else ["K4V8"]) + ([] if args.no_kf8v4 else ["KF8V4"])
     t0 = time.time()
     caches = {L: [kvq.kv_cache_create(L, 1, DEC_HKV, D, DEC_T) for _ in range(DEC_S)] for L in layouts}
     keep = {}                                    # host copies of the sessions the CPU baseline uses
@@ -226,6 +227,54 @@ def main():
         t48 = e0.elapsed_time(e1) / args.steps
         extra["decode_k4v8_GBps"] = round(dec_bytes / (t48 * 1e-3) / 1e9, 1)
         extra["decode_k4v8_ms"] = round(t48, 4)
+
+    if "KF8V4" in layouts:
+        # fp8 keys (E4M3 codes, one exponent byte per 32-element block) with 4-bit values:
+        # the same decode inputs, and the same turn on its own 100,500-token session
+        f8_bytes = sum(kvq.kv_footprint_bytes(h) for h in caches["KF8V4"])
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for _ in range(args.warmup):
+            decode("KF8V4")
+        e0.record(stream)
+        for _ in range(args.steps):
+            decode("KF8V4")
+        e1.record(stream)
+        torch.cuda.synchronize()
+        tf8 = e0.elapsed_time(e1) / args.steps
+        hf = kvq.kv_cache_create("KF8V4", 1, TURN_HKV, D, TURN_CTX + TURN_NEW)
+        kvq.kv_append_quant(hf, 0, to_dev(c3["k"]), to_dev(c3["v"]))
+        f8_plan = kvq.kv_chunk_plan(hf, 0, TURN_HQ, TURN_NEW)
+        part_f8 = torch.empty((TURN_NEW, TURN_HQ, f8_plan[0], D + 2), dtype=torch.float32, device=dev)
+
+        def f8_pass1():
+            if f8_plan[0] == 1:
+                kvq.kv_attend_chunk(hf, 0, q_new, TURN_NEW, sm, out=out_turn, workspace=ws_turn)
+            else:
+                kvq.kv_attend_chunk_partial(hf, 0, q_new, TURN_NEW, sm, f8_plan[0], f8_plan[1], partials=part_f8)
+
+        for _ in range(args.warmup):
+            f8_pass1()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.steps):
+            f8_pass1()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        tcf8 = e0.elapsed_time(e1) / args.steps
+        kvq.kv_cache_destroy(hf)
+        del part_f8
+        f8_tflops = chunk_flop / (tcf8 * 1e-3) / 1e12
+        extra["kf8v4"] = {
+            "workload": "the decode and turn workloads above with fp8 (E4M3, MX block exponent) keys and "
+                        "4-bit values",
+            "decode_cache_bytes": f8_bytes, "decode_ms": round(tf8, 4),
+            "decode_GBps": round(f8_bytes / (tf8 * 1e-3) / 1e9, 1),
+            "decode_hbm_frac": round(f8_bytes / (tf8 * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "chunk_kernel_ms": round(tcf8, 4), "chunk_plan": {"n_splits": f8_plan[0], "keys_per_split": f8_plan[1]},
+            "chunk_TFLOPs": round(f8_tflops, 1), "chunk_mfma_frac": round(f8_tflops / MFMA_F16_PEAK_TFLOPS, 4),
+        }
+        log(f"KF8V4 decode {tf8:.4f} ms ({extra['kf8v4']['decode_GBps']} GB/s), chunk kernel {tcf8:.4f} ms "
+            f"({f8_tflops:.1f} TFLOP/s, plan {f8_plan})")
 
     # session offload / restore of the 100,500-token turn cache through pinned host memory
     # (host-link rate, PCIe included: context for a cache hit, not the metric)

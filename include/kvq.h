@@ -19,9 +19,19 @@
  *     -qmax, qmax), all zero when d == 0;
  *   - 8-bit codes are int8 (two's complement); 4-bit codes are nibbles u = q + 8, byte j
  *     of a block = u[2j] | u[2j+1] << 4; the FP16 layout stores fp16_rne(x), no scale;
- *   - planes per (layer, KV head), token-major: KC [cap][code bytes], KS [cap][2*D/32],
- *     VC, VS; cap = max_tokens rounded up to 256 tokens (the KVSplit page's remark on
- *     256-byte alignment, section "Otimizacao para Apple Silicon e limitacoes").
+ *   - fp8 keys (KV_KF8V4) are OCP "MX" blocks: the offloading page ("KV Cache
+ *     Offloading for Context-Intensive Tasks", section "2. Metodologia", its fourth item)
+ *     names FP8 KV storage without fixing a format, and gfx950 converts OCP E4M3 in
+ *     hardware.  Per 32-element block one exponent byte s = e + 127 with
+ *     e = clamp(floor(log2(amax)) - 8, -127, 127) (-127 for an all-zero block), and per
+ *     element the E4M3 code (bias 7, largest 448, no infinities) of x * 2^-e rounded to
+ *     nearest, ties to even, saturated at +-448; a result of zero is stored as +0.
+ *     x_hat = E4M3 value * 2^(s - 127).  The attention kernels widen these keys to fp16
+ *     (exactly while |x| < 65536: the fp16 control layout's range);
+ *   - planes per (layer, KV head), token-major: KC [cap][code bytes], KS [cap][scale
+ *     bytes] (2*D/32 for fp16 scales, D/32 for exponent bytes), VC, VS; cap = max_tokens
+ *     rounded up to 256 tokens (the KVSplit page's remark on 256-byte alignment, section
+ *     "Otimizacao para Apple Silicon e limitacoes").
  *
  * Conventions for every entry point:
  *   - status: 0 (KV_OK) or a negative KV_E* code; kv_last_error() then holds a message
@@ -54,12 +64,14 @@ extern "C" {
 #define KV_EEMPTY       -5   /* attention over a layer with no cached token              */
 #define KV_EHIP         -6   /* a HIP call failed; the cache is poisoned                 */
 
-/* layouts: key bits x value bits (the five configurations the KVSplit page compares) */
-#define KV_FP16 0
-#define KV_K8V8 1
-#define KV_K8V4 2
-#define KV_K4V8 3
-#define KV_K4V4 4
+/* layouts: key bits x value bits (0..4: the five configurations the KVSplit page
+ * compares; 5: fp8 keys, the FP8 alternative of the offloading page, with 4-bit values) */
+#define KV_FP16  0
+#define KV_K8V8  1
+#define KV_K8V4  2
+#define KV_K4V8  3
+#define KV_K4V4  4
+#define KV_KF8V4 5
 
 /* element types of k, v, q */
 #define KV_F32  0
@@ -75,7 +87,7 @@ extern "C" {
 typedef struct kv_cache kv_cache;
 
 /* Create an empty session cache on the current HIP device.
- * layout: KV_FP16..KV_K4V4.  n_layers >= 1, n_kv_heads >= 1, head_dim in {64, 128}
+ * layout: KV_FP16..KV_KF8V4.  n_layers >= 1, n_kv_heads >= 1, head_dim in {64, 128}
  * (other multiples of 32 -> KV_EUNSUPPORTED), 1 <= max_tokens <= 2^31 - 256.
  * Allocates n_layers * n_kv_heads * round_up(max_tokens, 256) token rows, zero-filled.
  * Returns NULL on error (kv_last_error() says why; KV_ENOMEM if hipMalloc failed). */

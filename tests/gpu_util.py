@@ -7,6 +7,7 @@ import sys
 import numpy as np
 
 import asymmetric_quantized_kv_amd as kvq
+from asymmetric_quantized_kv_amd import inputs as I
 
 TOL = 5e-3   # max abs error of attention outputs against the oracle
 
@@ -32,7 +33,9 @@ def host_inputs(x: np.ndarray, dtype: str) -> np.ndarray:
     """The values the oracle must see for a device tensor made by dev(x, dtype)."""
     if dtype == "f16":
         return x.astype(np.float16).astype(np.float32)
-    return np.asarray(x, np.float32)   # f32 as is; bf16 inputs are already bf16 values
+    if dtype == "bf16":   # torch's fp32 -> bf16 conversion rounds to nearest even
+        return I.bf16_round(x)
+    return np.asarray(x, np.float32)
 
 
 @contextlib.contextmanager

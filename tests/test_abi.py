@@ -43,14 +43,14 @@ def test_every_declared_symbol_is_exported(built_library):
     assert set(names) <= set(_lib._SIGS), "binding misses a declared entry point"
 
 
-@pytest.mark.parametrize("layout", range(5))
+@pytest.mark.parametrize("layout", range(6))
 def test_layout_footprint_matches_oracle(layout):
     for L, hkv, d, t in [(22, 4, 64, 8192), (22, 4, 64, 128), (1, 8, 128, 100_500), (3, 5, 96, 1), (2, 1, 32, 257)]:
         assert kvq.kv_layout_footprint_bytes(layout, L, hkv, d, t) == O.layout_footprint_bytes(layout, L, hkv, d, t)
 
 
 def test_layered_footprint_matches_oracle():
-    for layouts in ([2], [0, 1, 2, 3, 4], [1] * 11 + [4] * 11, [3, 0, 3]):
+    for layouts in ([2], [0, 1, 2, 3, 4, 5], [1] * 11 + [4] * 11, [3, 0, 3]):
         for hkv, d, t in ((4, 64, 8192), (8, 128, 100_500), (3, 96, 1)):
             want = O.OracleLayeredCache(layouts, hkv, d, t).footprint_bytes()
             assert kvq.kv_layered_footprint_bytes(layouts, hkv, d, t) == want

@@ -15,7 +15,7 @@ from test_gpu_session import PLANES, parse_saved
 
 pytestmark = pytest.mark.gpu
 
-LAYOUTS = ["FP16", "K8V8", "K8V4", "K4V8", "K4V4"]
+LAYOUTS = ["FP16", "K8V8", "K8V4", "K4V8", "K4V4", "KF8V4"]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -46,8 +46,8 @@ def test_layered_cache_matches_oracle():
     h, oc = layered_pair(LAYOUTS)
     try:
         assert kvq.kv_footprint_bytes(h) == oc.footprint_bytes()
-        assert [kvq.kv_cache_layout(h, l) for l in range(5)] == [O.LAYOUT_IDS[x] for x in LAYOUTS]
-        for l in range(5):
+        assert [kvq.kv_cache_layout(h, l) for l in range(len(LAYOUTS))] == [O.LAYOUT_IDS[x] for x in LAYOUTS]
+        for l in range(len(LAYOUTS)):
             n = oc.len[l]
             for hh in range(2):
                 for name, p in PLANES:

@@ -16,7 +16,7 @@ from gpu_util import TOL, assert_planes_equal, dev, gpu_cache, host_inputs, log,
 
 pytestmark = pytest.mark.gpu
 
-LAYOUTS = ["FP16", "K8V8", "K8V4", "K4V8", "K4V4"]
+LAYOUTS = ["FP16", "K8V8", "K8V4", "K4V8", "K4V4", "KF8V4"]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -74,6 +74,40 @@ def test_append_codec_edge_cases(layout):
         assert_planes_equal(h, oc, 0)
 
 
+def _mx_edge_rows():
+    """Rows of two 32-element blocks, values y * 2^e on E4M3's grid and its midpoints:
+    ties to even (normal and subnormal), the 448 saturation, -0, an all-zero block, and
+    block maxima at the ends of the exponent range (scale clamp at -127, large scales)."""
+    v = O.e4m3_values()
+    mids = [(v[c] + v[c + 1]) / 2 for c in range(0x7E)]
+    rows = []
+    for e, top in ((-3, 256.0), (5, 500.0), (-20, 464.0), (40, 300.0), (-133, 256.0), (92, 511.0)):
+        for start in range(0, len(mids), 31):
+            blk = [top] + mids[start:start + 31]
+            blk += [0.0] * (32 - len(blk))
+            b = np.array(blk) * 2.0 ** e
+            b[1::3] *= -1
+            rows.append(np.concatenate([b, -b[::-1]]))
+    z = np.zeros(64)
+    z[33] = -0.0
+    z[40] = 2.0 ** -100
+    rows.append(z)
+    return np.array(rows, dtype=np.float32)
+
+
+def test_append_fp8_key_edge_cases():
+    """fp8 key blocks of every rounding case are the oracle's bit for bit."""
+    rows = _mx_edge_rows()
+    assert np.all(np.isfinite(rows))
+    k = rows[:, None, :]
+    v = (rows[:, None, :] * np.float32(2.0 ** -60)).astype(np.float32)
+    oc = O.OracleCache(O.LAYOUT_IDS["KF8V4"], 1, 1, 64, len(rows))
+    oc.append(0, k, v)
+    with gpu_cache("KF8V4", 1, 1, 64, len(rows)) as h:
+        kvq.kv_append_quant(h, 0, dev(k, "f32"), dev(v, "f32"))
+        assert_planes_equal(h, oc, 0)
+
+
 # ---------------------------------------------------------------------------
 # decode
 # ---------------------------------------------------------------------------
@@ -94,6 +128,10 @@ DECODE_CASES = [
     ("K8V4", 64, 16, "f32", [600]),
     ("K4V8", 128, 16, "bf16", [257]),
     ("FP16", 64, 2, "f16", [64, 5000]),
+    ("KF8V4", 128, 8, "bf16", [1, 129, 3000]),
+    ("KF8V4", 64, 4, "f32", [700, 2049]),
+    ("KF8V4", 128, 3, "f16", [513]),
+    ("KF8V4", 128, 16, "f32", [1000]),
 ]
 
 
@@ -181,6 +219,9 @@ CHUNK_CASES = [
     ("FP16", 64, 8, "f32", 4000, 16),
     ("K8V4", 64, 2, "f32", 0, 700),
     ("K4V8", 128, 16, "bf16", 333, 3),
+    ("KF8V4", 128, 8, "bf16", 3000, 200),
+    ("KF8V4", 64, 2, "f32", 0, 700),
+    ("KF8V4", 128, 5, "f16", 1500, 64),
 ]
 
 

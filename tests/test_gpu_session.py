@@ -60,7 +60,7 @@ def filled_pair(layout, dtype="bf16"):
     return h, oc
 
 
-@pytest.mark.parametrize("layout", ["K8V4", "FP16", "K4V8"])
+@pytest.mark.parametrize("layout", ["K8V4", "FP16", "K4V8", "KF8V4"])
 @pytest.mark.parametrize("pinned", [True, False])
 def test_save_restore_round_trip(layout, pinned):
     log(f"session round trip {layout} pinned={pinned}")

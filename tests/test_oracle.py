@@ -107,7 +107,7 @@ def test_footprint_context_ratio():
 
 
 def test_cache_object_footprint_and_capacity_granule():
-    for layout in range(5):
+    for layout in range(6):
         c = O.OracleCache(layout, 2, 3, 64, 300)
         assert c.cap == 512
         assert c.footprint_bytes() == O.layout_footprint_bytes(layout, 2, 3, 64, 300)
@@ -227,7 +227,7 @@ def test_fp16_layout_roundtrip():
 
 def test_append_is_chunk_invariant():
     k, v, _ = I.workload_small(12, 700, 2, 64, 4, 1)
-    for layout in range(5):
+    for layout in range(6):
         one = O.OracleCache(layout, 1, 2, 64, 700)
         one.append(0, k, v)
         parts = O.OracleCache(layout, 1, 2, 64, 700)
