@@ -272,6 +272,7 @@ def main():
             "decode_hbm_frac": round(f8_bytes / (tf8 * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
             "chunk_kernel_ms": round(tcf8, 4), "chunk_plan": {"n_splits": f8_plan[0], "keys_per_split": f8_plan[1]},
             "chunk_TFLOPs": round(f8_tflops, 1), "chunk_mfma_frac": round(f8_tflops / MFMA_F16_PEAK_TFLOPS, 4),
+            "traffic_decode": load_traffic("decode_kf8v4"), "traffic_chunk": load_traffic("chunk_kf8v4"),
         }
         log(f"KF8V4 decode {tf8:.4f} ms ({extra['kf8v4']['decode_GBps']} GB/s), chunk kernel {tcf8:.4f} ms "
             f"({f8_tflops:.1f} TFLOP/s, plan {f8_plan})")

@@ -54,18 +54,20 @@ def test_config2_all_layouts_all_layers():
 
 
 @pytest.mark.timeout(900)
-def test_config3_turn_and_reuse_invariant():
-    """100,000 cached + 500 new tokens, Hq 64 / Hkv 8 / D 128, K8V4: every plane byte, every
-    output of the turn against the oracle, and the reuse invariant on the GPU (the turn
-    equals the last 500 rows of one chunk over all 100,500 positions)."""
+@pytest.mark.parametrize("layout", ["K8V4", "KF8V4"])
+def test_config3_turn_and_reuse_invariant(layout):
+    """100,000 cached + 500 new tokens, Hq 64 / Hkv 8 / D 128, K8V4 (and the fp8-key layout
+    on the same inputs): every plane byte, every output of the turn against the oracle, and
+    the reuse invariant on the GPU (the turn equals the last 500 rows of one chunk over all
+    100,500 positions)."""
     torch = torch_mod()
     t = time.time()
     c = I.config3()
     n_ctx, n_new = c["n_ctx"], c["n_new"]
-    oc = O.OracleCache(2, 1, 8, 128, n_ctx + n_new)
+    oc = O.OracleCache(O.LAYOUT_IDS[layout], 1, 8, 128, n_ctx + n_new)
     oc.append(0, c["k"], c["v"])
-    log(f"config 3 oracle cache built ({time.time() - t:.1f} s)")
-    with gpu_cache("K8V4", 1, 8, 128, n_ctx + n_new) as h:
+    log(f"config 3 {layout} oracle cache built ({time.time() - t:.1f} s)")
+    with gpu_cache(layout, 1, 8, 128, n_ctx + n_new) as h:
         kvq.kv_append_quant(h, 0, dev(c["k"][:n_ctx], "bf16"), dev(c["v"][:n_ctx], "bf16"))
         kvq.kv_append_quant(h, 0, dev(c["k"][n_ctx:], "bf16"), dev(c["v"][n_ctx:], "bf16"))
         assert_planes_equal(h, oc, 0)
@@ -74,28 +76,28 @@ def test_config3_turn_and_reuse_invariant():
         log(f"config 3 gpu turn done ({time.time() - t:.1f} s)")
         want = O.attend_chunk(oc, 0, c["q"], n_new, SM128, row_block=256)
         err = max_err(out, want)
-        log(f"config 3 turn: max err {err:.3e} ({time.time() - t:.1f} s)")
+        log(f"config 3 {layout} turn: max err {err:.3e} ({time.time() - t:.1f} s)")
         assert err <= TOL
         # reuse invariant: recompute the whole context as one chunk
         q_all = torch.zeros((n_ctx + n_new, 64, 128), dtype=torch.bfloat16, device="cuda")
         q_all[n_ctx:] = dev(c["q"], "bf16")
         full = kvq.kv_attend_chunk(h, 0, q_all, n_ctx + n_new, SM128)
         diff = float((full[n_ctx:] - out).abs().max())
-        log(f"config 3 reuse invariant: turn vs full recompute max diff {diff:.3e}")
+        log(f"config 3 {layout} reuse invariant: turn vs full recompute max diff {diff:.3e}")
         assert diff <= TOL
         del full, q_all
 
 
 @pytest.mark.timeout(1200)
 def test_config4_batched_decode_sampled_sessions():
-    """64 sessions x 32,768 tokens, Hq 32 / Hkv 8 / D 128, K8V4 and K4V8 on identical
-    inputs.  Oracle on sessions {0, 21, 63} (planes and outputs); every session's output
-    is finite and inside the hull of that session's values; the attention error against
-    unquantized fp64 attention is reported and K4V8's exceeds K8V4's."""
+    """64 sessions x 32,768 tokens, Hq 32 / Hkv 8 / D 128, K8V4, K4V8 and the fp8-key layout
+    on identical inputs.  Oracle on sessions {0, 21, 63} (planes and outputs); every
+    session's output is finite and inside the hull of that session's values; the attention
+    error against unquantized fp64 attention is reported and K4V8's exceeds K8V4's."""
     torch = torch_mod()
     sample = (0, 21, 63)
     t = time.time()
-    hs = {L: [kvq.kv_cache_create(L, 1, 8, 128, 32768) for _ in range(64)] for L in ("K8V4", "K4V8")}
+    hs = {L: [kvq.kv_cache_create(L, 1, 8, 128, 32768) for _ in range(64)] for L in ("K8V4", "K4V8", "KF8V4")}
     kept, vmax = {}, np.zeros(64)
     try:
         for s in range(64):

@@ -58,6 +58,7 @@ DECODE_CASES = [
     ("K4V8", 128, 4, [1300, 64], [(2, 1024), (4, 512)]),
     ("FP16", 64, 8, [513, 1024], [(2, 512), (5, 512)]),
     ("K4V4", 64, 1, [900], [(1, 1024), (2, 512)]),
+    ("KF8V4", 128, 8, [2000, 33], [(1, 2048), (4, 512)]),
 ]
 
 
@@ -107,6 +108,7 @@ def test_decode_partials_and_merge(case):
 @pytest.mark.parametrize("layout,d,g,n_ctx,n_new,plans", [
     ("K8V4", 128, 8, 1200, 300, [(1, 1536), (4, 384), (8, 192)]),
     ("K4V8", 64, 5, 100, 77, [(3, 64), (1, 192)]),
+    ("KF8V4", 128, 8, 900, 120, [(1, 1024), (5, 256)]),
 ])
 def test_chunk_partials_and_merge(layout, d, g, n_ctx, n_new, plans):
     log(f"chunk partials {layout} D={d} G={g} {n_ctx}+{n_new}")

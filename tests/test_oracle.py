@@ -603,3 +603,18 @@ def test_kf8v4_footprint():
     for d in (64, 128):
         per = (d + d // 32) + (d // 2 + 2 * d // 32)
         assert O.layout_footprint_bytes(5, 2, 3, d, 300) == 2 * 3 * 512 * per
+
+
+def test_fp8_queries_would_miss_the_attention_tolerance():
+    """Why the fp8-key layout's chunk path keeps fp16 MFMA: rounding the *queries* to MX
+    fp8 as well (what an fp8 x fp8 MFMA needs) moves attention outputs far past the 5e-3
+    tolerance on the turn's input recipe, while the fp8 keys alone are the cache's content."""
+    k, v, q = I.workload_small(5, 4000, 1, 128, 8, 64, bf16=True, n_outliers=4)
+    oc = O.OracleCache(5, 1, 1, 128, 4000)
+    oc.append(0, k, v)
+    sm = 128 ** -0.5
+    want = O.attend_chunk(oc, 0, q, 64, sm)
+    qc, qs = O.mx_quantize_rows(q.reshape(-1, 128))
+    q8 = O.mx_dequant_rows(qc, qs).reshape(q.shape).astype(np.float32)
+    err = float(np.abs(O.attend_chunk(oc, 0, q8, 64, sm) - want).max())
+    assert err > 10 * 5e-3, err
