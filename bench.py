@@ -43,6 +43,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing on host cores")
     ap.add_argument("--no-k4v8", action="store_true", help="skip the K4V8 decode on the identical inputs")
     ap.add_argument("--no-kf8v4", action="store_true", help="skip the fp8-key (KF8V4) decode and chunk")
+    ap.add_argument("--no-rebuild", action="store_true", help="skip the 131,072-token full rebuild")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (for HBM counter calibration)")
     return ap.parse_args()
@@ -383,6 +384,9 @@ def main():
     }
     log(f"ragged decode {t_rag:.4f} ms ({extra['ragged_decode']['GBps']} GB/s), plan {rag_plan}")
 
+    if not args.no_rebuild:
+        extra["full_rebuild"] = full_rebuild(args, kvq, I, torch, dev, stream, log_fn=log)
+
     if args.copy_calibration:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         b = torch.empty_like(a)
@@ -442,6 +446,59 @@ def main():
     }
     record.update(extra)
     print(json.dumps(record), flush=True)
+
+
+def full_rebuild(args, kvq, I, torch, dev, stream, log_fn):
+    """A full cache miss: reset, then 131,072 tokens as 32 chunks of 4,096, each appended and
+    attended causally (Hq 40 / Hkv 8 / D 128, bf16), K8V4 and the fp8-key layout on the same
+    inputs.  Inputs are resident on the device before the timed region; the chunk workspace
+    is sized for the largest split plan of the 32 calls."""
+    n_chunks, chunk, hq, hkv = 32, 4096, 40, 8
+    ks, vs, qs = [], [], []
+    for c in range(n_chunks):
+        k, v, q = I.config5_chunk(c)
+        ks.append(torch.from_numpy(k).to(dev).to(torch.bfloat16))
+        vs.append(torch.from_numpy(v).to(dev).to(torch.bfloat16))
+        qs.append(torch.from_numpy(q).to(dev).to(torch.bfloat16))
+        del k, v, q
+    out = torch.empty((chunk, hq, D), dtype=torch.float32, device=dev)
+    pairs = hq * sum(c * chunk * chunk + chunk * (chunk + 1) // 2 for c in range(n_chunks))
+    flop = 4.0 * D * pairs
+    res = {"workload": "reset + 32 x (append 4,096 tokens + causal chunk attention), 131,072 tokens, "
+                       "Hq 40 / Hkv 8 / D 128, bf16 inputs", "visible_pairs": pairs}
+    for L in ("K8V4",) + (() if args.no_kf8v4 else ("KF8V4",)):
+        h = kvq.kv_cache_create(L, 1, hkv, D, n_chunks * chunk)
+        ws_bytes = 16
+        kvq.kv_cache_reset(h)
+        for c in range(n_chunks):      # sizing pass (also the warm-up)
+            kvq.kv_append_quant(h, 0, ks[c], vs[c])
+            ws_bytes = max(ws_bytes, kvq.kv_chunk_workspace_bytes(h, 0, hq, chunk))
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+
+        def rebuild():
+            kvq.kv_cache_reset(h)
+            for c in range(n_chunks):
+                kvq.kv_append_quant(h, 0, ks[c], vs[c])
+                kvq.kv_attend_chunk(h, 0, qs[c], chunk, D ** -0.5, out=out, workspace=ws)
+
+        rebuild()
+        torch.cuda.synchronize()
+        reps = 3
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            rebuild()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / reps
+        kvq.kv_cache_destroy(h)
+        del ws
+        tf = flop / (t * 1e-3) / 1e12
+        res[L] = {"ms": round(t, 2), "tokens_per_s": round(n_chunks * chunk / (t * 1e-3), 1),
+                  "TFLOPs": round(tf, 1), "mfma_frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4)}
+        log_fn(f"full rebuild {L}: {t:.2f} ms ({tf:.1f} TFLOP/s, {res[L]['tokens_per_s']:.0f} tokens/s)")
+    del ks, vs, qs, out
+    return res
 
 
 def cpu_baseline(keep, sm):
