@@ -12,6 +12,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <functional>
 #include <string>
 #include <vector>
 
@@ -736,9 +737,71 @@ int chunk_prepare(const kv_cache* cache, int layer, int n_q_heads, int64_t n_new
   return KV_OK;
 }
 
-void chunk_plan(const ChunkPrep& p, int* n_splits, int64_t* tps) {
-  plan_splits(p.base, p.slots, split_cap(p.base, p.slots, kMaxSplitsChunk), p.len, kChunkKeys,
-              kChunkMinKeysPerSplit, n_splits, tps);
+// Splits considered for a chunk.  At least 2 even when the row tiles alone exceed the
+// resident workgroups: 640 tiles on 256 slots run 2.5 rounds (the last one half idle) at one
+// split, but 5 full rounds of half-length work at two.
+int64_t chunk_split_cap(const ChunkPrep& p) {
+  return std::max<int64_t>(2, split_cap(p.base, p.slots, kMaxSplitsChunk));
+}
+
+// Estimated duration of a chunk launch under the split (n, t), in units of one 64-key tile of
+// one workgroup.  Each workgroup costs its causal key-tile count plus a fixed start-up and
+// epilogue charge; the workgroups of each XCD are list-scheduled over that die's resident
+// slots in the order the kernel hands them out (die x takes t = x * per + i, i = 0, 1, ...,
+// as row tile t % mtiles of split t / (mtiles * hkv)).  More than one split adds the merge's
+// traffic (partials written and read back) at a nominal bandwidth.
+double chunk_cost(const ChunkPrep& p, int d, int n, int64_t t, std::vector<double>& heap) {
+  constexpr double kWgFixedTiles = 2.0;
+  constexpr double kMergeBytesPerSec = 5e12, kCuFlopsPerSec = 2.9e12;
+  const int64_t slots = p.slots > 0 ? p.slots : 1024;
+  const int64_t die_slots = std::max<int64_t>(1, slots / kXcds);
+  const int64_t hkv = p.base / p.mtiles, n_new = p.rows / p.group, base_pos = p.len - n_new;
+  const int64_t total = p.base * n, per = total / kXcds, rem = total % kXcds;
+  double makespan = 0;
+  for (int64_t x = 0; x < (int64_t)kXcds; ++x) {
+    const int64_t cnt = per + (x < rem ? 1 : 0), first = x * per + std::min(x, rem);
+    if (cnt == 0) continue;
+    heap.assign((size_t)std::min(die_slots, cnt), 0.0);
+    for (int64_t i = 0; i < cnt; ++i) {
+      const int64_t wg = first + i, mt = wg % p.mtiles, sp = wg / (p.mtiles * hkv);
+      const int64_t last_row = std::min((mt + 1) * kChunkRows, p.rows) - 1;
+      const int64_t k_lo = sp * t, k_hi = std::min({k_lo + t, p.len, base_pos + last_row / p.group + 1});
+      const double w = kWgFixedTiles + (k_hi > k_lo ? (double)ceil_div(k_hi - k_lo, kChunkKeys) : 0.0);
+      std::pop_heap(heap.begin(), heap.end(), std::greater<double>());
+      heap.back() += w;
+      std::push_heap(heap.begin(), heap.end(), std::greater<double>());
+    }
+    makespan = std::max(makespan, *std::max_element(heap.begin(), heap.end()));
+  }
+  if (n > 1) {
+    const double bytes = 2.0 * (double)(p.rows * hkv) * n * (d + 2) * sizeof(float);
+    const double tile_sec = (double)kChunkRows * kChunkKeys * 4.0 * d / kCuFlopsPerSec;
+    makespan += bytes / kMergeBytesPerSec / tile_sec;
+  }
+  return makespan;
+}
+
+void chunk_plan(const ChunkPrep& p, int d, int* n_splits, int64_t* tps) {
+  const int64_t cap = chunk_split_cap(p);
+  if (p.base * cap > (int64_t(1) << 20)) {   // very large launches: the round-count model
+    plan_splits(p.base, p.slots, cap, p.len, kChunkKeys, kChunkMinKeysPerSplit, n_splits, tps);
+    return;
+  }
+  std::vector<double> heap;
+  double best = 0;
+  *n_splits = 1;
+  *tps = round_up(std::max<int64_t>(p.len, 1), kChunkKeys);
+  for (int64_t s = 1; s <= cap; ++s) {
+    const int64_t t = std::max(round_up(kChunkMinKeysPerSplit, kChunkKeys), round_up(ceil_div(p.len, s), kChunkKeys));
+    const int64_t n = ceil_div(p.len, t);
+    if (n != s && s > 1) continue;
+    const double cost = chunk_cost(p, d, (int)n, s == 1 ? *tps : t, heap);
+    if (s == 1 || cost < best * 0.98) {
+      best = cost;
+      *n_splits = (int)n;
+      *tps = s == 1 ? *tps : t;
+    }
+  }
 }
 
 int chunk_launch(kv_cache* cache, int layer, const ChunkPrep& p, const void* q, int q_dtype, int n_q_heads,
@@ -856,9 +919,7 @@ int64_t kv_chunk_workspace_bytes(const kv_cache* cache, int layer, int n_q_heads
   ChunkPrep p;
   int rc = chunk_prepare(cache, layer, n_q_heads, n_new, false, &p);
   if (rc) return rc;
-  const int64_t cap = split_cap(p.base, p.slots, kMaxSplitsChunk);
-  if (cap <= 1) return 0;
-  return partial_bytes(n_new * n_q_heads, (int)cap, cache->d);
+  return partial_bytes(n_new * n_q_heads, (int)chunk_split_cap(p), cache->d);
 }
 
 int kv_chunk_plan(const kv_cache* cache, int layer, int n_q_heads, int64_t n_new, int* n_splits,
@@ -868,7 +929,7 @@ int kv_chunk_plan(const kv_cache* cache, int layer, int n_q_heads, int64_t n_new
   ChunkPrep p;
   int rc = chunk_prepare(cache, layer, n_q_heads, n_new, true, &p);
   if (rc) return rc;
-  chunk_plan(p, n_splits, keys_per_split);
+  chunk_plan(p, cache->d, n_splits, keys_per_split);
   return KV_OK;
 }
 
@@ -882,7 +943,7 @@ int kv_attend_chunk(kv_cache* cache, int layer, const void* q, int q_dtype, int 
   if ((rc = check_q_out(q, q_dtype, out, "out"))) return rc;
   int n_splits;
   int64_t tps;
-  chunk_plan(p, &n_splits, &tps);
+  chunk_plan(p, cache->d, &n_splits, &tps);
   const int64_t need = n_splits > 1 ? partial_bytes(n_new * n_q_heads, n_splits, cache->d) : 0;
   if ((rc = check_workspace(workspace, ws_bytes, need))) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
