@@ -19,8 +19,8 @@ import numpy as np
 
 __all__ = [
     "bf16_round", "bf16_bits", "normal", "outlier_channels", "workload_small",
-    "config1", "config2", "config3", "config4_session", "config4_queries",
-    "config5_chunk", "ragged_lengths", "CONFIGS",
+    "decode_128_tokens", "layers22_8192_tokens", "turn_100k_plus_500", "batch64x32k_session", "batch64x32k_queries",
+    "rebuild131k_chunk", "ragged_lengths", "WORKLOADS",
 ]
 
 
@@ -100,7 +100,7 @@ def workload_small(seed: int, n_tokens: int, n_kv_heads: int, head_dim: int,
 # ---------------------------------------------------------------------------
 # the five workloads
 # ---------------------------------------------------------------------------
-def config1(seed: int = 1):
+def decode_128_tokens(seed: int = 1):
     """1 layer, 128 cached tokens, Hq 32, Hkv 4, D 64, fp32 N(0,1); K8V4; one query."""
     k = normal((128, 4, 64), seed, 1)
     v = normal((128, 4, 64), seed, 2)
@@ -109,7 +109,7 @@ def config1(seed: int = 1):
                 n_q_heads=32, dtype="f32")
 
 
-def config2(seed: int = 2, n_layers: int = 22, n_tokens: int = 8192):
+def layers22_8192_tokens(seed: int = 2, n_layers: int = 22, n_tokens: int = 8192):
     """22 layers x 4 KV heads x 64, Hq 32, 8192 tokens, fp32; 4 of 64 key channels x8
     per (layer, KV head).  K, V [L, T, Hkv, D]; Q [L, 1, Hq, D]."""
     k = np.empty((n_layers, n_tokens, 4, 64), np.float32)
@@ -124,7 +124,7 @@ def config2(seed: int = 2, n_layers: int = 22, n_tokens: int = 8192):
                 n_q_heads=32, dtype="f32")
 
 
-def config3(seed: int = 3, n_ctx: int = 100_000, n_new: int = 500):
+def turn_100k_plus_500(seed: int = 3, n_ctx: int = 100_000, n_new: int = 500):
     """1 layer, Hq 64, Hkv 8, D 128, bf16.  K, V [n_ctx + n_new, 8, 128] with 8 of 128
     key channels x8 per KV head (before the bf16 cast); Q [n_new, 64, 128]."""
     n = n_ctx + n_new
@@ -137,7 +137,7 @@ def config3(seed: int = 3, n_ctx: int = 100_000, n_new: int = 500):
                 n_kv_heads=8, head_dim=128, n_q_heads=64, dtype="bf16")
 
 
-def config4_session(s: int, seed: int = 4, n_tokens: int = 32_768):
+def batch64x32k_session(s: int, seed: int = 4, n_tokens: int = 32_768):
     """Session ``s`` of the batched-decode workload (bf16): K = z * c with z ~ N(0,1) and a
     per-(session, KV head, channel) scale c = exp(N(0,1)); V ~ N(0,1).  [T, 8, 128] each."""
     z = normal((n_tokens, 8, 128), seed, 1, s)
@@ -147,12 +147,12 @@ def config4_session(s: int, seed: int = 4, n_tokens: int = 32_768):
     return k, v
 
 
-def config4_queries(seed: int = 4, n_sessions: int = 64):
+def batch64x32k_queries(seed: int = 4, n_sessions: int = 64):
     """One bf16 query per session: [S, 32, 128]."""
     return bf16_round(normal((n_sessions, 32, 128), seed, 3))
 
 
-def config5_chunk(c: int, seed: int = 5, chunk: int = 4096):
+def rebuild131k_chunk(c: int, seed: int = 5, chunk: int = 4096):
     """Tokens [chunk*c, chunk*(c+1)) of the 131,072-token rebuild (bf16):
     K, V [chunk, 8, 128], Q [chunk, 40, 128], all N(0,1)."""
     k = bf16_round(normal((chunk, 8, 128), seed, 1, c))
@@ -168,10 +168,10 @@ def ragged_lengths(n_sessions: int = 64, lo: int = 512, hi: int = 32_768, seed: 
     return np.floor(np.exp(np.log(lo) + u * (np.log(hi + 1) - np.log(lo)))).astype(np.int64).clip(lo, hi)
 
 
-CONFIGS = {
-    1: "1 layer, 128 tokens, Hq 32 / Hkv 4 / D 64, fp32, K8V4, decode",
-    2: "22 layers x 4 KV heads x 64, Hq 32, 8192 tokens, fp32, all layouts, decode",
-    3: "100,000 cached + 500 new tokens, Hq 64 / Hkv 8 / D 128, bf16, K8V4, chunk append",
-    4: "64 sessions x 32,768 tokens, Hq 32 / Hkv 8 / D 128, bf16, K8V4 and K4V8, decode",
-    5: "131,072 tokens as 32 chunks of 4096, Hq 40 / Hkv 8 / D 128, bf16, K8V4, rebuild",
+WORKLOADS = {
+    "decode_128_tokens": "1 layer, 128 tokens, Hq 32 / Hkv 4 / D 64, fp32, K8V4, decode",
+    "layers22_8192_tokens": "22 layers x 4 KV heads x 64, Hq 32, 8192 tokens, fp32, all layouts, decode",
+    "turn_100k_plus_500": "100,000 cached + 500 new tokens, Hq 64 / Hkv 8 / D 128, bf16, K8V4, chunk append",
+    "batch64x32k": "64 sessions x 32,768 tokens, Hq 32 / Hkv 8 / D 128, bf16, K8V4 and K4V8, decode",
+    "rebuild131k": "131,072 tokens as 32 chunks of 4096, Hq 40 / Hkv 8 / D 128, bf16, K8V4, rebuild",
 }

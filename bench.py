@@ -76,7 +76,7 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
         sys.exit(2)
 
@@ -101,14 +101,14 @@ def main():
     keep = {}                                    # host copies of the sessions the CPU baseline uses
     n_cpu_sessions = 0 if args.no_cpu_baseline else 8
     for s in range(DEC_S):
-        k, v = I.config4_session(s)
+        k, v = I.batch64x32k_session(s)
         kd, vd = to_dev(k), to_dev(v)
         for L in layouts:
             kvq.kv_append_quant(caches[L][s], 0, kd, vd)
         if s < n_cpu_sessions:
             keep[s] = (k, v)
         del kd, vd
-    q_dec = to_dev(I.config4_queries())
+    q_dec = to_dev(I.batch64x32k_queries())
     torch.cuda.synchronize()
     log(f"decode caches ready ({time.time() - t0:.1f} s)")
     dec_bytes = sum(kvq.kv_footprint_bytes(h) for h in caches["K8V4"])   # every row is cached
@@ -118,11 +118,11 @@ def main():
                          dtype=torch.uint8, device=dev)
 
     # ---- turn workload -------------------------------------------------------------
-    c3 = I.config3()
+    turn_in = I.turn_100k_plus_500()
     h3 = kvq.kv_cache_create("K8V4", 1, TURN_HKV, D, TURN_CTX + TURN_NEW)
-    kvq.kv_append_quant(h3, 0, to_dev(c3["k"][:TURN_CTX]), to_dev(c3["v"][:TURN_CTX]))
-    k_new, v_new = to_dev(c3["k"][TURN_CTX:]), to_dev(c3["v"][TURN_CTX:])
-    q_new = to_dev(c3["q"])
+    kvq.kv_append_quant(h3, 0, to_dev(turn_in["k"][:TURN_CTX]), to_dev(turn_in["v"][:TURN_CTX]))
+    k_new, v_new = to_dev(turn_in["k"][TURN_CTX:]), to_dev(turn_in["v"][TURN_CTX:])
+    q_new = to_dev(turn_in["q"])
     out_turn = torch.empty((TURN_NEW, TURN_HQ, D), dtype=torch.float32, device=dev)
     # the workspace is sized after the append, for the length the chunk call sees
     kvq.kv_append_quant(h3, 0, k_new, v_new)
@@ -243,7 +243,7 @@ def main():
         torch.cuda.synchronize()
         tf8 = e0.elapsed_time(e1) / args.steps
         hf = kvq.kv_cache_create("KF8V4", 1, TURN_HKV, D, TURN_CTX + TURN_NEW)
-        kvq.kv_append_quant(hf, 0, to_dev(c3["k"]), to_dev(c3["v"]))
+        kvq.kv_append_quant(hf, 0, to_dev(turn_in["k"]), to_dev(turn_in["v"]))
         f8_plan = kvq.kv_chunk_plan(hf, 0, TURN_HQ, TURN_NEW)
         part_f8 = torch.empty((TURN_NEW, TURN_HQ, f8_plan[0], D + 2), dtype=torch.float32, device=dev)
 
@@ -309,12 +309,12 @@ def main():
     # layer-specific layouts: the 22-layer x 4 KV-head x 64 cache of 8192 tokens with
     # K8V8 in its first 4 layers, K8V4 in the middle 14 and K4V4 in the last 4; one decode
     # step is a call per layer (cache-resident: the whole cache fits the 256 MB MALL)
-    c2 = I.config2()
+    lay22_in = I.layers22_8192_tokens()
     lay22 = ["K8V8"] * 4 + ["K8V4"] * 14 + ["K4V4"] * 4
     hl = kvq.kv_cache_create_layered(lay22, 4, 64, 8192)
     for l in range(22):
-        kvq.kv_append_quant(hl, l, torch.from_numpy(c2["k"][l]).to(dev), torch.from_numpy(c2["v"][l]).to(dev))
-    q22 = torch.from_numpy(c2["q"]).to(dev)
+        kvq.kv_append_quant(hl, l, torch.from_numpy(lay22_in["k"][l]).to(dev), torch.from_numpy(lay22_in["v"][l]).to(dev))
+    q22 = torch.from_numpy(lay22_in["q"]).to(dev)
     out22 = torch.empty((1, 32, 64), dtype=torch.float32, device=dev)
     ws22 = torch.empty(max(16, max(kvq.kv_decode_workspace_bytes([hl], l, 32) for l in range(22))),
                        dtype=torch.uint8, device=dev)
@@ -397,7 +397,7 @@ def main():
     cpu = None
     if n_cpu_sessions:
         cpu = cpu_baseline(keep, sm)
-        extra["cpu_baseline_chunk"] = cpu_baseline_chunk(c3, sm)
+        extra["cpu_baseline_chunk"] = cpu_baseline_chunk(turn_in, sm)
 
     record = {
         "metric": "K8V4 decode KV-read GB/s (% HBM peak) + chunk-append tokens/s at 100K ctx",
@@ -456,7 +456,7 @@ def full_rebuild(args, kvq, I, torch, dev, stream, log_fn):
     n_chunks, chunk, hq, hkv = 32, 4096, 40, 8
     ks, vs, qs = [], [], []
     for c in range(n_chunks):
-        k, v, q = I.config5_chunk(c)
+        k, v, q = I.rebuild131k_chunk(c)
         ks.append(torch.from_numpy(k).to(dev).to(torch.bfloat16))
         vs.append(torch.from_numpy(v).to(dev).to(torch.bfloat16))
         qs.append(torch.from_numpy(q).to(dev).to(torch.bfloat16))
@@ -508,7 +508,7 @@ def cpu_baseline(keep, sm):
     import oracle as O
     from asymmetric_quantized_kv_amd import inputs as I
 
-    q = I.config4_queries()
+    q = I.batch64x32k_queries()
     ocs = []
     for s in sorted(keep):
         k, v = keep[s]
@@ -531,17 +531,17 @@ def cpu_baseline(keep, sm):
             "affinity_cpus": len(os.sched_getaffinity(0))}
 
 
-def cpu_baseline_chunk(c3, sm):
+def cpu_baseline_chunk(turn_in, sm):
     """The oracle's chunk attention for 16 of the 500 new tokens (all 64 heads), on host cores."""
     import numpy as np
 
     import oracle as O
 
     c = O.OracleCache(2, 1, TURN_HKV, D, TURN_CTX + TURN_NEW)
-    c.append(0, c3["k"], c3["v"])
+    c.append(0, turn_in["k"], turn_in["v"])
     rows = np.linspace(0, TURN_NEW - 1, 16).astype(int)
     t, cpu0 = time.perf_counter(), time.process_time()
-    O.attend_chunk(c, 0, c3["q"], TURN_NEW, sm, rows=rows)
+    O.attend_chunk(c, 0, turn_in["q"], TURN_NEW, sm, rows=rows)
     spent = time.perf_counter() - t
     cpu_used = time.process_time() - cpu0
     return {"value": round(len(rows) / spent, 2), "unit": "tokens/s", "cores": max(1, round(cpu_used / spent)),

@@ -29,7 +29,7 @@ def header_functions():
     return sorted(set(re.findall(r"\b(kv_[a-z_]+)\s*\(", text)))
 
 
-def test_header_declares_the_north_star_calls():
+def test_header_declares_the_core_calls():
     names = header_functions()
     for n in ("kv_cache_create", "kv_append_quant", "kv_attend_decode", "kv_attend_chunk", "kv_footprint_bytes"):
         assert n in names

@@ -29,11 +29,11 @@ def _gpu():
 
 
 @pytest.mark.timeout(900)
-def test_config2_all_layouts_all_layers():
+def test_22_layers_8192_tokens_all_layouts():
     """22 layers x 4 KV heads x 64, 8,192 tokens, 5 layouts: footprint equals the printed
     table, every plane byte equals the oracle's, every output of the 22-layer decode step
     is within tolerance."""
-    c = I.config2()
+    c = I.layers22_8192_tokens()
     printed = {"FP16": 176.00, "K8V8": 93.50, "K8V4": 71.50, "K4V8": 71.50, "K4V4": 49.50}
     for name, mb in printed.items():
         t = time.time()
@@ -49,47 +49,47 @@ def test_config2_all_layouts_all_layers():
                 assert_planes_equal(h, oc, l)
                 out = kvq.kv_attend_decode([h], l, dev(c["q"][l], "f32"), 64 ** -0.5)
                 worst = max(worst, max_err(out, O.attend_decode([oc], l, c["q"][l], 64 ** -0.5)))
-            log(f"config 2 {name}: max err {worst:.3e} ({time.time() - t:.1f} s)")
+            log(f"22 layers {name}: max err {worst:.3e} ({time.time() - t:.1f} s)")
             assert worst <= TOL
 
 
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("layout", ["K8V4", "KF8V4"])
-def test_config3_turn_and_reuse_invariant(layout):
+def test_turn_100k_plus_500_and_reuse_invariant(layout):
     """100,000 cached + 500 new tokens, Hq 64 / Hkv 8 / D 128, K8V4 (and the fp8-key layout
     on the same inputs): every plane byte, every output of the turn against the oracle, and
     the reuse invariant on the GPU (the turn equals the last 500 rows of one chunk over all
     100,500 positions)."""
     torch = torch_mod()
     t = time.time()
-    c = I.config3()
+    c = I.turn_100k_plus_500()
     n_ctx, n_new = c["n_ctx"], c["n_new"]
     oc = O.OracleCache(O.LAYOUT_IDS[layout], 1, 8, 128, n_ctx + n_new)
     oc.append(0, c["k"], c["v"])
-    log(f"config 3 {layout} oracle cache built ({time.time() - t:.1f} s)")
+    log(f"turn 100k+500 {layout} oracle cache built ({time.time() - t:.1f} s)")
     with gpu_cache(layout, 1, 8, 128, n_ctx + n_new) as h:
         kvq.kv_append_quant(h, 0, dev(c["k"][:n_ctx], "bf16"), dev(c["v"][:n_ctx], "bf16"))
         kvq.kv_append_quant(h, 0, dev(c["k"][n_ctx:], "bf16"), dev(c["v"][n_ctx:], "bf16"))
         assert_planes_equal(h, oc, 0)
         out = kvq.kv_attend_chunk(h, 0, dev(c["q"], "bf16"), n_new, SM128)
         torch.cuda.synchronize()
-        log(f"config 3 gpu turn done ({time.time() - t:.1f} s)")
+        log(f"turn 100k+500 gpu turn done ({time.time() - t:.1f} s)")
         want = O.attend_chunk(oc, 0, c["q"], n_new, SM128, row_block=256)
         err = max_err(out, want)
-        log(f"config 3 {layout} turn: max err {err:.3e} ({time.time() - t:.1f} s)")
+        log(f"turn 100k+500 {layout} turn: max err {err:.3e} ({time.time() - t:.1f} s)")
         assert err <= TOL
         # reuse invariant: recompute the whole context as one chunk
         q_all = torch.zeros((n_ctx + n_new, 64, 128), dtype=torch.bfloat16, device="cuda")
         q_all[n_ctx:] = dev(c["q"], "bf16")
         full = kvq.kv_attend_chunk(h, 0, q_all, n_ctx + n_new, SM128)
         diff = float((full[n_ctx:] - out).abs().max())
-        log(f"config 3 {layout} reuse invariant: turn vs full recompute max diff {diff:.3e}")
+        log(f"turn 100k+500 {layout} reuse invariant: turn vs full recompute max diff {diff:.3e}")
         assert diff <= TOL
         del full, q_all
 
 
 @pytest.mark.timeout(1200)
-def test_config4_batched_decode_sampled_sessions():
+def test_batch_64x32k_decode_sampled_sessions():
     """64 sessions x 32,768 tokens, Hq 32 / Hkv 8 / D 128, K8V4, K4V8 and the fp8-key layout
     on identical inputs.  Oracle on sessions {0, 21, 63} (planes and outputs); every
     session's output is finite and inside the hull of that session's values; the attention
@@ -101,15 +101,15 @@ def test_config4_batched_decode_sampled_sessions():
     kept, vmax = {}, np.zeros(64)
     try:
         for s in range(64):
-            k, v = I.config4_session(s)
+            k, v = I.batch64x32k_session(s)
             kd, vd = dev(k, "bf16"), dev(v, "bf16")
             for L in hs:
                 kvq.kv_append_quant(hs[L][s], 0, kd, vd)
             vmax[s] = np.abs(v).max()
             if s in sample:
                 kept[s] = (k, v)
-        q = I.config4_queries()
-        log(f"config 4 caches built ({time.time() - t:.1f} s)")
+        q = I.batch64x32k_queries()
+        log(f"batch 64x32k caches built ({time.time() - t:.1f} s)")
         errs = {}
         for L in hs:
             out = kvq.kv_attend_decode(hs[L], 0, dev(q, "bf16"), SM128).cpu().numpy().astype(np.float64)
@@ -130,10 +130,10 @@ def test_config4_batched_decode_sampled_sessions():
                 qe.append(out[s] - exact)
             qe = np.concatenate(qe)
             errs[L] = (float(np.abs(qe).max()), float(np.sqrt(np.mean(qe ** 2))))
-            log(f"config 4 {L}: max err vs oracle {ex:.3e}; vs unquantized fp64: max {errs[L][0]:.3e} "
+            log(f"batch 64x32k {L}: max err vs oracle {ex:.3e}; vs unquantized fp64: max {errs[L][0]:.3e} "
                 f"rms {errs[L][1]:.3e} ({time.time() - t:.1f} s)")
             assert ex <= TOL
-        log(f"config 4 error asymmetry K4V8/K8V4: rms x{errs['K4V8'][1] / errs['K8V4'][1]:.1f}, "
+        log(f"batch 64x32k error asymmetry K4V8/K8V4: rms x{errs['K4V8'][1] / errs['K8V4'][1]:.1f}, "
             f"max x{errs['K4V8'][0] / errs['K8V4'][0]:.1f}")
         assert errs["K4V8"][1] > errs["K8V4"][1]
     finally:
@@ -144,7 +144,7 @@ def test_config4_batched_decode_sampled_sessions():
 
 
 @pytest.mark.timeout(1200)
-def test_config5_full_rebuild_sampled_rows():
+def test_rebuild_131k_sampled_rows():
     """131,072 tokens as 32 chunks of 4,096, Hq 40 / Hkv 8 / D 128, K8V4: reset, then per chunk
     append + causal chunk attention.  Every plane byte is checked at the end; the outputs of
     8 rows per chunk (first, last, 6 seeded) x 40 heads are checked against the oracle; every
@@ -159,7 +159,7 @@ def test_config5_full_rebuild_sampled_rows():
     with gpu_cache("K8V4", 1, 8, 128, n_chunks * chunk) as h:
         kvq.kv_cache_reset(h)
         for ci in range(n_chunks):
-            k, v, q = I.config5_chunk(ci)
+            k, v, q = I.rebuild131k_chunk(ci)
             kvq.kv_append_quant(h, 0, dev(k, "bf16"), dev(v, "bf16"))
             out = kvq.kv_attend_chunk(h, 0, dev(q, "bf16"), chunk, SM128)
             assert bool(torch.isfinite(out).all())
@@ -167,9 +167,9 @@ def test_config5_full_rebuild_sampled_rows():
             qs.append(q[picks[ci]])
             oc.append(0, k, v)
             if ci % 8 == 7:
-                log(f"config 5: {ci + 1} chunks ({time.time() - t:.1f} s)")
+                log(f"rebuild 131k: {ci + 1} chunks ({time.time() - t:.1f} s)")
         assert_planes_equal(h, oc, 0)
-    log(f"config 5 planes equal ({time.time() - t:.1f} s)")
+    log(f"rebuild 131k planes equal ({time.time() - t:.1f} s)")
     worst = 0.0
     for h in range(8):
         kh, vh = oc.keys(0, h), oc.values(0, h)
@@ -178,5 +178,5 @@ def test_config5_full_rebuild_sampled_rows():
                 pos = ci * chunk + r
                 want = O.attention_exact(qs[ci][r_i, 5 * h:5 * h + 5], kh[:pos + 1], vh[:pos + 1], SM128)
                 worst = max(worst, float(np.max(np.abs(got[ci][r_i, 5 * h:5 * h + 5] - want))))
-        log(f"config 5 oracle kv head {h} done, max err so far {worst:.3e} ({time.time() - t:.1f} s)")
+        log(f"rebuild 131k oracle kv head {h} done, max err so far {worst:.3e} ({time.time() - t:.1f} s)")
     assert worst <= TOL

@@ -190,9 +190,9 @@ def test_decode_more_sessions_than_one_launch():
             kvq.kv_cache_destroy(h)
 
 
-def test_config1_exact_workload():
-    log("config 1")
-    c = I.config1()
+def test_decode_128_tokens_exact_workload():
+    log("decode 128 tokens")
+    c = I.decode_128_tokens()
     oc = O.OracleCache(2, 1, 4, 64, 128)
     oc.append(0, c["k"], c["v"])
     with gpu_cache("K8V4", 1, 4, 64, 128) as h:
@@ -200,7 +200,7 @@ def test_config1_exact_workload():
         assert_planes_equal(h, oc, 0)
         out = kvq.kv_attend_decode([h], 0, dev(c["q"], "f32"), 64 ** -0.5)
         err = max_err(out, O.attend_decode([oc], 0, c["q"], 64 ** -0.5))
-        log(f"  config 1 max err {err:.3e}")
+        log(f"  decode 128 tokens max err {err:.3e}")
         assert tuple(out.shape) == (1, 32, 64) and err <= TOL
 
 
