@@ -8,7 +8,11 @@
 // codes are dequantized in registers, never materialized.
 //
 // Work split: one workgroup (4 waves) per (split of the context, KV head, session);
-// each wave takes 128-token chunks of the split in turn.  Within a wave, E = D / LPT
+// each wave takes 128-token chunks of the split in turn.  The grid runs KV head fastest,
+// then session, then split: the runtime deals workgroups to the 8 XCDs round-robin by
+// linear id, so each die gets the same heads of every session (equal work), and the splits
+// that are empty for short sessions come last.  (Split fastest would put every workgroup
+// of split s on die s whenever the split count is a multiple of 8.)  Within a wave, E = D / LPT
 // elements of a token belong to one lane (LPT lanes per token), and each lane holds
 // two tokens per step, t and t + 64 / LPT.  A chunk is processed in three phases:
 //   A  scores: integer dot products (v_dot4_i32_i8) of the 8/4-bit key codes with the
@@ -145,7 +149,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   __shared__ float s_ml[4][2][GP];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int split = blockIdx.x, head = blockIdx.y, sl = blockIdx.z;
+  const int head = blockIdx.x, sl = blockIdx.y, split = blockIdx.z;
   const SessionRef S = a.sess[sl];
   const int64_t srow = S.row * a.hq + (int64_t)head * a.group;  // first q row
   const int64_t ts = (int64_t)split * a.tps;
@@ -579,7 +583,7 @@ constexpr int lane_elems() { return GP <= 2 ? 32 : (GP == 4 ? 16 : 8); }
 template <int KB, int VB, int D, int GP>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
   constexpr int E = lane_elems<GP>();
-  dim3 grid(a.n_splits, a.hkv, a.n_sess);
+  dim3 grid(a.hkv, a.n_sess, a.n_splits);
   if (KB == kF8 && a.q_dtype == 0)
     hipLaunchKernelGGL((decode_kernel<KB, VB, D, GP, E, KB == kF8>), grid, dim3(256), 0, s, a);
   else

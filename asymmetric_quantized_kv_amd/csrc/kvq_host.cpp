@@ -570,7 +570,7 @@ int check_workspace(const void* ws, size_t ws_bytes, int64_t need) {
 // A caller-chosen split: n_splits ranges of `per` tokens (a multiple of `gran`) that
 // together cover `len` tokens.
 int check_split(int n_splits, int64_t per, int64_t gran, int64_t len, const char* what) {
-  if (n_splits < 1) return fail(KV_EINVAL, "n_splits must be >= 1 (got %d)", n_splits);
+  if (n_splits < 1 || n_splits > 65535) return fail(KV_EINVAL, "n_splits must be in [1, 65535] (got %d)", n_splits);
   if (per < 1 || per % gran || per > (int64_t(1) << 40))
     return fail(KV_EINVAL, "%s must be a positive multiple of %lld (got %lld)", what, (long long)gran, (long long)per);
   if ((int64_t)n_splits * per < len)

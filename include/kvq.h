@@ -146,7 +146,7 @@ int64_t kv_decode_workspace_bytes(kv_cache* const* sessions, int n_sessions, int
  * longest session.  Errors as kv_attend_decode (KV_EEMPTY for an empty session).
  *
  * kv_attend_decode_partial: the first pass alone, with a split of the caller's choice
- * (n_splits >= 1; tokens_per_split a positive multiple of 512 with n_splits *
+ * (1 <= n_splits <= 65535; tokens_per_split a positive multiple of 512 with n_splits *
  * tokens_per_split >= the longest session).  Split s of session b covers tokens
  * [s * tokens_per_split, min((s + 1) * tokens_per_split, len_b)).  Writes, per row
  * r = b * n_q_heads + h and split s, partials[(r * n_splits + s) * (head_dim + 2) + i]:

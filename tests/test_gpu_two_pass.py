@@ -178,7 +178,7 @@ def test_partial_entry_points_reject_bad_splits():
         k, v, q = I.workload_small(970, 1500, 2, 64, 4, 1, bf16=True)
         kvq.kv_append_quant(h, 0, dev(k, "bf16"), dev(v, "bf16"))
         qd = dev(q, "bf16")
-        for n_splits, per in [(2, 500), (2, 512), (0, 2048), (1, 0)]:   # not a multiple / too short / bad count
+        for n_splits, per in [(2, 500), (2, 512), (0, 2048), (1, 0), (70000, 512)]:   # not a multiple / too short / bad count
             with pytest.raises(kvq.KVError) as e:
                 kvq.kv_attend_decode_partial([h], 0, qd, 0.125, n_splits, per)
             assert e.value.code == kvq.KV_EINVAL
