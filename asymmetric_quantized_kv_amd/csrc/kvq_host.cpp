@@ -74,9 +74,15 @@ int check_shape(int layout, int n_layers, int n_kv_heads, int head_dim, int64_t 
   if (!layout_bits(layout, &kb, &vb)) return fail(KV_EINVAL, "layout %d is not one of 0..5", layout);
   if (n_layers < 1) return fail(KV_EINVAL, "n_layers must be >= 1 (got %d)", n_layers);
   if (n_kv_heads < 1) return fail(KV_EINVAL, "n_kv_heads must be >= 1 (got %d)", n_kv_heads);
-  if (head_dim < 32 || head_dim % 32) return fail(KV_EINVAL, "head_dim must be a positive multiple of 32 (got %d)", head_dim);
+  if (head_dim < 32 || head_dim % 32 || head_dim > (1 << 16))
+    return fail(KV_EINVAL, "head_dim must be a multiple of 32 in [32, 65536] (got %d)", head_dim);
   if (max_tokens < 1 || max_tokens > (int64_t(1) << 31) - kGranule)
     return fail(KV_EINVAL, "max_tokens out of range (got %lld)", (long long)max_tokens);
+  // the arena size must not overflow: layers x heads x cap x (at most 4 D bytes per token)
+  const __int128 worst = (__int128)n_layers * n_kv_heads * round_up(max_tokens, kGranule) * (4 * (__int128)head_dim);
+  if (worst > ((__int128)1 << 50))
+    return fail(KV_EINVAL, "a cache of %d layers x %d KV heads x %lld tokens x head_dim %d is too large", n_layers,
+                n_kv_heads, (long long)max_tokens, head_dim);
   return KV_OK;
 }
 
@@ -224,6 +230,8 @@ int64_t kv_layered_footprint_bytes(const int* layouts, int n_layers, int n_kv_he
   clear_err();
   if (!layouts) return fail(KV_EINVAL, "layouts is NULL");
   if (n_layers < 1) return fail(KV_EINVAL, "n_layers must be >= 1 (got %d)", n_layers);
+  for (int l = 0; l < n_layers; ++l)   // the bound on the whole arena, per layout
+    if (int rc = check_shape(layouts[l], n_layers, n_kv_heads, head_dim, max_tokens)) return rc;
   int64_t total = 0;
   for (int l = 0; l < n_layers; ++l) {
     const int64_t b = kv_layout_footprint_bytes(layouts[l], 1, n_kv_heads, head_dim, max_tokens);
@@ -245,7 +253,7 @@ kv_cache* kv_cache_create_layered(const int* layouts, int n_layers, int n_kv_hea
     return nullptr;
   }
   for (int l = 0; l < n_layers; ++l)
-    if (check_shape(layouts[l], 1, n_kv_heads, head_dim, max_tokens)) return nullptr;
+    if (check_shape(layouts[l], n_layers, n_kv_heads, head_dim, max_tokens)) return nullptr;
   if (head_dim != 64 && head_dim != 128) {
     fail(KV_EUNSUPPORTED, "head_dim %d is valid but only 64 and 128 are built", head_dim);
     return nullptr;
@@ -504,7 +512,7 @@ int kv_cache_copy_plane(const kv_cache* cache, int layer, int kv_head, int plane
   int rc = kv_cache_plane(cache, layer, kv_head, plane, &p, &rb);
   if (rc) return rc;
   if (!dst) return fail(KV_EINVAL, "dst is NULL");
-  if (row0 < 0 || n_rows < 0 || row0 + n_rows > cache->lg[layer].g.cap)
+  if (row0 < 0 || n_rows < 0 || row0 > cache->lg[layer].g.cap || n_rows > cache->lg[layer].g.cap - row0)
     return fail(KV_EINVAL, "rows [%lld, %lld) outside the plane", (long long)row0, (long long)(row0 + n_rows));
   if (cache->poisoned) return fail(KV_EHIP, "cache is poisoned by an earlier HIP error");
   if (rb == 0 || n_rows == 0) return KV_OK;
@@ -522,7 +530,7 @@ int kv_append_quant(kv_cache* cache, int layer, const void* k, const void* v, in
   if (layer < 0 || layer >= cache->n_layers) return fail(KV_EINVAL, "layer %d out of range [0, %d)", layer, cache->n_layers);
   if (n_new < 0) return fail(KV_EINVAL, "n_new must be >= 0 (got %lld)", (long long)n_new);
   if (!dtype_ok(dtype)) return fail(KV_EINVAL, "dtype %d is not one of KV_F32/KV_BF16/KV_F16", dtype);
-  if (cache->len[layer] + n_new > cache->max_tokens)
+  if (n_new > cache->max_tokens - cache->len[layer])
     return fail(KV_ECAPACITY, "append of %lld tokens to layer %d (len %lld) exceeds max_tokens %lld",
                 (long long)n_new, layer, (long long)cache->len[layer], (long long)cache->max_tokens);
   if (n_new == 0) return KV_OK;
@@ -547,7 +555,7 @@ int kv_append_quant(kv_cache* cache, int layer, const void* k, const void* v, in
 
 namespace {
 
-constexpr int64_t kMaxSplitsDecode = 1 << 20;
+constexpr int64_t kMaxSplitsDecode = 65535;   // the split is the decode grid's z dimension
 
 int64_t partial_bytes(int64_t rows, int n_splits, int d) {
   return rows * n_splits * (int64_t)(d + 2) * (int64_t)sizeof(float);

@@ -88,7 +88,9 @@ typedef struct kv_cache kv_cache;
 
 /* Create an empty session cache on the current HIP device.
  * layout: KV_FP16..KV_KF8V4.  n_layers >= 1, n_kv_heads >= 1, head_dim in {64, 128}
- * (other multiples of 32 -> KV_EUNSUPPORTED), 1 <= max_tokens <= 2^31 - 256.
+ * (other multiples of 32 up to 65536 -> KV_EUNSUPPORTED), 1 <= max_tokens <= 2^31 - 256,
+ * and n_layers * n_kv_heads * round_up(max_tokens, 256) * 4 * head_dim <= 2^50 (KV_EINVAL
+ * beyond: the arena size stays far from int64 overflow).
  * Allocates n_layers * n_kv_heads * round_up(max_tokens, 256) token rows, zero-filled.
  * Returns NULL on error (kv_last_error() says why; KV_ENOMEM if hipMalloc failed). */
 kv_cache* kv_cache_create(int layout, int n_layers, int n_kv_heads, int head_dim,
@@ -215,7 +217,9 @@ int kv_attend_chunk_partial(kv_cache* cache, int layer, const void* q, int q_dty
  * < 0 for a NULL cache. */
 int64_t kv_footprint_bytes(const kv_cache* cache);
 
-/* The same footprint for a shape, without allocating (pure host arithmetic). < 0 if invalid. */
+/* The same footprint for a shape, without allocating (pure host arithmetic). < 0 if invalid
+ * (the shape rules of kv_cache_create, except that any multiple of 32 up to 65536 is a
+ * valid head_dim here). */
 int64_t kv_layout_footprint_bytes(int layout, int n_layers, int n_kv_heads, int head_dim,
                                   int64_t max_tokens);
 

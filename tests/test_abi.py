@@ -128,3 +128,16 @@ def test_status_is_cleared_by_a_good_call():
         kvq.kv_cache_create(9, 1, 1, 64, 1)
     assert kvq.kv_layout_footprint_bytes(2, 1, 1, 64, 1) > 0
     assert kvq.kv_last_status() == kvq.KV_OK and kvq.kv_last_error() == ""
+
+
+def test_shapes_too_large_for_an_arena_are_rejected():
+    """The footprint of an absurd shape is an error, never a wrapped-around int64."""
+    for args in ((0, 1 << 20, 1 << 20, 128, 1 << 20), (0, 1, 1, 1 << 17, 100), (2, 1 << 30, 1 << 30, 64, 1 << 30)):
+        with pytest.raises(kvq.KVError) as e:
+            kvq.kv_layout_footprint_bytes(*args)
+        assert e.value.code == kvq.KV_EINVAL
+    with pytest.raises(kvq.KVError):
+        kvq.kv_layered_footprint_bytes([2] * 4096, 1 << 16, 128, 1 << 20)
+    # the largest accepted head_dim still gives the exact formula (K8V4: D + D/16, D/2 + D/16)
+    d = 65536
+    assert kvq.kv_layout_footprint_bytes(2, 1, 1, d, 256) == 256 * (d + d // 16 + d // 2 + d // 16)

@@ -305,3 +305,10 @@ def test_device_error_paths():
         assert kvq.kv_cache_len(h, 0) == 4
         kvq.kv_cache_reset(h)
         assert kvq.kv_cache_len(h, 0) == 0
+        # sizes that would overflow the host's range arithmetic are refused, not wrapped
+        big = (1 << 63) - 1
+        assert kvq.lib().kv_append_quant(h, 0, x.data_ptr(), x.data_ptr(), kvq.KV_F32, big, None) == kvq.KV_ECAPACITY
+        assert kvq.kv_cache_len(h, 0) == 0
+        buf = torch.empty(64, dtype=torch.uint8, device="cuda")
+        assert kvq.lib().kv_cache_copy_plane(h, 0, 0, kvq.KV_PLANE_KC, 1 << 62, 1 << 62, buf.data_ptr(),
+                                             None) == kvq.KV_EINVAL
