@@ -3,9 +3,8 @@
 //   M = max_s m_s,  o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
 // One wave per output row.  Lane s loads split s's (m, l), so the statistics of up to 64
 // splits take one round trip; the weights w_s = 2^(m_s - M) / L then go to every lane
-// through readlane, and each lane sums the splits for its elements of head_dim with the
-// loads of several splits in flight.  Splits that saw no token carry m = -inf, l = 0 and
-// weigh nothing.
+// through readlane, and each lane sums the splits for its elements of head_dim.  Splits
+// that saw no token carry m = -inf, l = 0 and weigh nothing.
 #include "kvq_internal.h"
 #include "wave_ops.h"
 
@@ -46,7 +45,6 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
         if (ms != -INFINITY) w = __builtin_amdgcn_exp2f(ms - M) * inv;
       }
       const int n = min(64, a.n_splits - s0);
-#pragma unroll 8
       for (int j = 0; j < n; ++j) {
         const float wj = readlane(w, j);
         if (e < a.d) o = fmaf(wj, p[(s0 + j) * stride + e], o);
