@@ -36,6 +36,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   const float inv = 1.f / L;
   for (int e0 = 0; e0 < a.d; e0 += 64) {
     const int e = e0 + lane;
+    const bool on = e < a.d;
     float o = 0.f;
     for (int s0 = 0; s0 < a.n_splits; s0 += 64) {
       const int s = s0 + lane;
@@ -45,12 +46,16 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
         if (ms != -INFINITY) w = __builtin_amdgcn_exp2f(ms - M) * inv;
       }
       const int n = min(64, a.n_splits - s0);
-      for (int j = 0; j < n; ++j) {
-        const float wj = readlane(w, j);
-        if (e < a.d) o = fmaf(wj, p[(s0 + j) * stride + e], o);
+      // four splits' loads are issued before their products are summed
+      for (int j = 0; j < n; j += 4) {
+        float x[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = on && j + i < n ? p[(s0 + j + i) * stride + e] : 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o = fmaf(readlane(w, min(j + i, 63)), x[i], o);
       }
     }
-    if (e < a.d) a.out[row * a.d + e] = o;
+    if (on) a.out[row * a.d + e] = o;
   }
 }
 
