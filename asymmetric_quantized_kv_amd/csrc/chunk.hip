@@ -59,13 +59,6 @@ __device__ __forceinline__ half2_t splat(uint16_t b) {
   return r;
 }
 
-__device__ __forceinline__ float q_at(const void* q, int dt, int64_t i) {
-  if (dt == 0) return static_cast<const float*>(q)[i];
-  const uint16_t b = static_cast<const uint16_t*>(q)[i];
-  if (dt == 1) return __uint_as_float((uint32_t)b << 16);
-  return h2f(b);
-}
-
 template <int W>
 __device__ __forceinline__ void load_dw(const uint8_t* p, uint32_t* o) {
   if constexpr (W % 4 == 0) {
@@ -314,14 +307,41 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(ChunkArgs a) {
   half8_t qv[NKS];
   half8_t ql[QSPLIT ? NKS : 1];
   {
-    const int64_t qoff = (tok * a.hq + qh) * (int64_t)D;
+    // 8 consecutive elements per k-step: one 16-byte load each (two for fp32), all issued
+    // before the first conversion
+    const int64_t qoff = (tok * a.hq + qh) * (int64_t)D + 8 * hl;
+    if constexpr (QSPLIT) {   // fp32 queries
+      const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(a.q) + qoff);
+      float4 raw[2 * NKS];
 #pragma unroll
-    for (int k = 0; k < NKS; ++k) {
+      for (int k = 0; k < NKS; ++k) {
+        raw[2 * k] = valid ? src[4 * k] : make_float4(0.f, 0.f, 0.f, 0.f);
+        raw[2 * k + 1] = valid ? src[4 * k + 1] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float x = valid ? q_at(a.q, a.q_dtype, qoff + 16 * k + 8 * hl + i) : 0.f;
-        qv[k][i] = (_Float16)x;
-        if constexpr (QSPLIT) ql[k][i] = (_Float16)(x - (float)qv[k][i]);
+      for (int k = 0; k < NKS; ++k) {
+        const float x[8] = {raw[2 * k].x, raw[2 * k].y, raw[2 * k].z, raw[2 * k].w,
+                            raw[2 * k + 1].x, raw[2 * k + 1].y, raw[2 * k + 1].z, raw[2 * k + 1].w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          qv[k][i] = (_Float16)x[i];
+          ql[k][i] = (_Float16)(x[i] - (float)qv[k][i]);
+        }
+      }
+    } else {                  // bf16 or fp16 queries
+      const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + qoff);
+      uint4 raw[NKS];
+#pragma unroll
+      for (int k = 0; k < NKS; ++k) raw[k] = valid ? src[2 * k] : make_uint4(0u, 0u, 0u, 0u);
+      const bool bf = a.q_dtype == 1;
+#pragma unroll
+      for (int k = 0; k < NKS; ++k) {
+        const uint32_t w[4] = {raw[k].x, raw[k].y, raw[k].z, raw[k].w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint16_t b = (uint16_t)(w[i / 2] >> (16 * (i & 1)));
+          qv[k][i] = bf ? (_Float16)__uint_as_float((uint32_t)b << 16) : __builtin_bit_cast(_Float16, b);
+        }
       }
     }
   }
