@@ -141,3 +141,20 @@ def test_shapes_too_large_for_an_arena_are_rejected():
     # the largest accepted head_dim still gives the exact formula (K8V4: D + D/16, D/2 + D/16)
     d = 65536
     assert kvq.kv_layout_footprint_bytes(2, 1, 1, d, 256) == 256 * (d + d // 16 + d // 2 + d // 16)
+
+
+def test_header_compiles_as_c99_and_links(tmp_path, built_library):
+    """include/kvq.h is a plain C interface: a C99 program that includes it builds with gcc,
+    links against libkvq.so and runs its host-side calls."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    exe = tmp_path / "abi_from_c"
+    lib_dir = _lib.LIB_PATH.parent
+    subprocess.run([cc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-I", str(ROOT / "include"),
+                    str(ROOT / "tests" / "c" / "abi_from_c.c"), "-o", str(exe), "-L", str(lib_dir), "-lkvq",
+                    f"-Wl,-rpath,{lib_dir}"], check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0 and r.stdout.strip() == "ok", (r.returncode, r.stdout, r.stderr)
