@@ -36,6 +36,9 @@
 #ifndef KVQ_DECODE_DEPTH
 #define KVQ_DECODE_DEPTH 4   // steps of key/value codes requested ahead of the one computing
 #endif
+#ifndef KVQ_DECODE_MFMA_QK
+#define KVQ_DECODE_MFMA_QK 1 // 8-bit keys: Q.K on the matrix cores (int8 MFMA per 32-element block)
+#endif
 
 namespace kvq {
 namespace {
@@ -53,6 +56,8 @@ __device__ __forceinline__ half2_t pack_rne(float a, float b) {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
 
 // Buffer resource over `bytes` bytes at p (raw, byte-addressed); loads through it take a
 // per-lane 32-bit offset and a wave-uniform offset, so addresses cost no vector ALU.
@@ -262,6 +267,25 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     }
   }
 
+  // 8-bit keys on the matrix cores: v_mfma_i32_32x32x32_i8 multiplies the query's digit
+  // rows (row 2 g + i = digit i of head g, zero above 2 GP) by one 32-element block of 32
+  // tokens' key codes.  Lane (r, h) of a wave holds A row r = lane % 32 and B column
+  // (token) r, elements 16 h .. 16 h + 15 of the block (h = lane / 32).
+  constexpr bool MQK = KB == 8 && KVQ_DECODE_MFMA_QK;
+  i32x4 qA[MQK ? NB : 1];
+  if constexpr (MQK) {
+    const int r = lane & 31, hl = lane >> 5;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      i32x4 x = {0, 0, 0, 0};
+      if (r < 2 * GP) {
+        const int8_t* src = (r & 1) ? &s_qb[r >> 1][0] : &s_qa[r >> 1][0];
+        x = *reinterpret_cast<const i32x4*>(src + 32 * b + 16 * hl);
+      }
+      qA[b] = x;
+    }
+  }
+
   float acc[GP][E];
   float wsum[GP], lsum[GP], m[GP];
 #pragma unroll
@@ -304,6 +328,29 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       kscl[slot][1] = buf_u16(r.ks, ksoff + TPS * KS, s * STEP * KS);
     }
   };
+  // MFMA key groups: 32 tokens each; lane (r, h) loads token r's bytes 32 b + 16 h .. + 16 of
+  // every block b, and its fp16 scales (a ring of RK groups, PDK groups ahead)
+  constexpr int NG = CT / 32, PDK = 2, RK = PDK + 1;
+  i32x4 kq[MQK ? RK : 1][MQK ? NB : 1];
+  uint32_t kqs[MQK ? RK : 1][MQK ? (NB + 1) / 2 : 1];
+  const uint32_t kqoff = (lane & 31) * KC + 16 * (lane >> 5), kqsoff = (lane & 31) * KS;
+  auto load_kg = [&](const Rsrc& r, int j) {
+    if constexpr (MQK) {
+      const int slot = j % RK;
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+        kq[slot][b] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(r.kc, (int)(kqoff + 32 * b),
+                                                                                      (int)(j * 32 * KC), 0));
+      if constexpr (NB == 4) {
+        const u32x2 t = __builtin_amdgcn_raw_buffer_load_b64(r.ks, (int)kqsoff, (int)(j * 32 * KS), 0);
+        kqs[slot][0] = t.x;
+        kqs[slot][1] = t.y;
+      } else {
+        static_assert(NB == 2, "head_dim 64 or 128");
+        kqs[slot][0] = __builtin_amdgcn_raw_buffer_load_b32(r.ks, (int)kqsoff, (int)(j * 32 * KS), 0);
+      }
+    }
+  };
   auto load_v = [&](const Rsrc& r, int s) {
     const int slot = s % R;
     buf_dwords<VW>(r.vc, voff, s * STEP * VC, vbuf[slot][0]);
@@ -316,8 +363,13 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   int64_t c = __builtin_amdgcn_readfirstlane(wave);
   Rsrc rc = chunk_rsrc(c, CT);
   if (c < n_chunks) {
+    if constexpr (MQK) {
 #pragma unroll
-    for (int s = 0; s < PD; ++s) load_k(rc, s);
+      for (int j = 0; j < PDK; ++j) load_kg(rc, j);
+    } else {
+#pragma unroll
+      for (int s = 0; s < PD; ++s) load_k(rc, s);
+    }
   }
   for (; c < n_chunks; c += 4) {
     const int64_t c0 = ts + c * CT;
@@ -325,120 +377,162 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     const bool more = c + 4 < n_chunks;
     const Rsrc rn = chunk_rsrc(c + 4, more ? CT : 0);
     // ---- phase A: scores ----------------------------------------------------------
+    if constexpr (MQK) {
+      // late iterations request the chunk's first value steps instead of key groups
+      constexpr int VPER = (PD + PDK - 1) / PDK;
+      constexpr int NQ = (2 * GP + 7) / 8;   // quads of D rows that hold query rows
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const int la = s * STEP + grp, lb = la + TPS;
-      if (s + PD < NS) load_k(rc, s + PD);
-      else load_v(rc, s + PD - NS);
-      const uint32_t* ka = kbuf[s % R][0];
-      const uint32_t* kb = kbuf[s % R][1];
-      float da = 1.f, db = 1.f;
-      half2_t fa[KB == kF8 ? 2 * KW : 1], fb[KB == kF8 ? 2 * KW : 1];
-      if constexpr (KB == kF8) {
-        // x_hat = E4M3 value * 2^(s - 127); s = 0 would be 2^-127, below every fp16
-        const float xa = __uint_as_float((uint32_t)kscl[s % R][0] << 23);
-        const float xb = __uint_as_float((uint32_t)kscl[s % R][1] << 23);
+      for (int j = 0; j < NG; ++j) {
+        if (j + PDK < NG) {
+          load_kg(rc, j + PDK);
+        } else {
 #pragma unroll
-        for (int j = 0; j < KW; ++j) {
-          fa[2 * j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)ka[j], xa, false);
-          fa[2 * j + 1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)ka[j], xa, true);
-          fb[2 * j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)kb[j], xb, false);
-          fb[2 * j + 1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)kb[j], xb, true);
+          for (int i = 0; i < VPER; ++i)
+            if ((j + PDK - NG) * VPER + i < PD) load_v(rc, (j + PDK - NG) * VPER + i);
         }
-      } else if constexpr (KB != 16) {
-        da = h2f(kscl[s % R][0]);
-        db = h2f(kscl[s % R][1]);
-      }
-      float pa[GP], pb[GP];
+        const int slot = j % RK;
+        // lane (token, h) gets D rows 8 q + 4 h + {0..3}: heads 4 q + 2 h + {0, 1}, both digits
+        float sc[NQ][2];
 #pragma unroll
-      for (int g = 0; g < GP; ++g) {
-        if constexpr (KB == 16) {
-          float xa = 0.f, xb = 0.f;
+        for (int q = 0; q < NQ; ++q) sc[q][0] = sc[q][1] = 0.f;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          const i32x16 zero = {};
+          const i32x16 dq = __builtin_amdgcn_mfma_i32_32x32x32_i8(qA[b], kq[slot][b], zero, 0, 0, 0);
+          const float d = h2f((uint16_t)(kqs[slot][b >> 1] >> (16 * (b & 1))));
+#pragma unroll
+          for (int q = 0; q < NQ; ++q) {
+            sc[q][0] = fmaf((float)((dq[4 * q] << 8) + dq[4 * q + 1]), d, sc[q][0]);
+            sc[q][1] = fmaf((float)((dq[4 * q + 2] << 8) + dq[4 * q + 3]), d, sc[q][1]);
+          }
+        }
+        const int t = 32 * j + (lane & 31);
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+          const int g0 = 4 * q + 2 * (lane >> 5);
+          if (g0 + 1 < GP) {
+            *reinterpret_cast<float2*>(&s_sc[wave][t][g0]) = make_float2(sc[q][0], sc[q][1]);
+          } else if (g0 < GP) {
+            s_sc[wave][t][g0] = sc[q][0];
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const int la = s * STEP + grp, lb = la + TPS;
+        if (s + PD < NS) load_k(rc, s + PD);
+        else load_v(rc, s + PD - NS);
+        const uint32_t* ka = kbuf[s % R][0];
+        const uint32_t* kb = kbuf[s % R][1];
+        float da = 1.f, db = 1.f;
+        half2_t fa[KB == kF8 ? 2 * KW : 1], fb[KB == kF8 ? 2 * KW : 1];
+        if constexpr (KB == kF8) {
+          // x_hat = E4M3 value * 2^(s - 127); s = 0 would be 2^-127, below every fp16
+          const float xa = __uint_as_float((uint32_t)kscl[s % R][0] << 23);
+          const float xb = __uint_as_float((uint32_t)kscl[s % R][1] << 23);
 #pragma unroll
           for (int j = 0; j < KW; ++j) {
-            xa = __builtin_amdgcn_fdot2(as_h2(qa_r[g][j]), as_h2(ka[j]), xa, false);
-            xb = __builtin_amdgcn_fdot2(as_h2(qa_r[g][j]), as_h2(kb[j]), xb, false);
+            fa[2 * j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)ka[j], xa, false);
+            fa[2 * j + 1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)ka[j], xa, true);
+            fb[2 * j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)kb[j], xb, false);
+            fb[2 * j + 1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)kb[j], xb, true);
           }
-          pa[g] = group_sum<LPT>(xa);
-          pb[g] = group_sum<LPT>(xb);
-        } else if constexpr (KB == kF8) {
-          float xa = 0.f, xb = 0.f;
-#pragma unroll
-          for (int j = 0; j < QW; ++j) {
-            xa = __builtin_amdgcn_fdot2(as_h2(qa_r[g][j]), fa[j], xa, false);
-            xb = __builtin_amdgcn_fdot2(as_h2(qa_r[g][j]), fb[j], xb, false);
-          }
-          if constexpr (QLO) {
-#pragma unroll
-            for (int j = 0; j < QW; ++j) {
-              xa = __builtin_amdgcn_fdot2(as_h2(qb_r[g][j]), fa[j], xa, false);
-              xb = __builtin_amdgcn_fdot2(as_h2(qb_r[g][j]), fb[j], xb, false);
-            }
-          }
-          pa[g] = group_sum<LPT>(xa);
-          pb[g] = group_sum<LPT>(xb);
-        } else {
-          // one chain per token: high digit, times 256, then the low digit
-          int ha = corr_a[g], hb = corr_a[g];
-          if constexpr (KB == 8) {
-            // the first product starts the chain (8-bit keys need no offset correction)
-            ha = sdot4_start((int)ka[0], (int)qa_r[g][0]);
-            hb = sdot4_start((int)kb[0], (int)qa_r[g][0]);
-#pragma unroll
-            for (int j = 1; j < KW; ++j) {
-              ha = __builtin_amdgcn_sdot4((int)ka[j], (int)qa_r[g][j], ha, false);
-              hb = __builtin_amdgcn_sdot4((int)kb[j], (int)qa_r[g][j], hb, false);
-            }
-            ha = (ha << 8) + corr_b[g];
-            hb = (hb << 8) + corr_b[g];
-#pragma unroll
-            for (int j = 0; j < KW; ++j) {
-              ha = __builtin_amdgcn_sdot4((int)ka[j], (int)qb_r[g][j], ha, false);
-              hb = __builtin_amdgcn_sdot4((int)kb[j], (int)qb_r[g][j], hb, false);
-            }
-          } else {
-            uint32_t ae[KW], ao[KW], be[KW], bo[KW];
-#pragma unroll
-            for (int j = 0; j < KW; ++j) {
-              ae[j] = ka[j] & 0x0F0F0F0Fu; ao[j] = (ka[j] >> 4) & 0x0F0F0F0Fu;
-              be[j] = kb[j] & 0x0F0F0F0Fu; bo[j] = (kb[j] >> 4) & 0x0F0F0F0Fu;
-            }
-#pragma unroll
-            for (int j = 0; j < KW; ++j) {
-              ha = __builtin_amdgcn_sdot4((int)ae[j], (int)qa_r[g][2 * j], ha, false);
-              ha = __builtin_amdgcn_sdot4((int)ao[j], (int)qa_r[g][2 * j + 1], ha, false);
-              hb = __builtin_amdgcn_sdot4((int)be[j], (int)qa_r[g][2 * j], hb, false);
-              hb = __builtin_amdgcn_sdot4((int)bo[j], (int)qa_r[g][2 * j + 1], hb, false);
-            }
-            ha = (ha << 8) + corr_b[g];
-            hb = (hb << 8) + corr_b[g];
-#pragma unroll
-            for (int j = 0; j < KW; ++j) {
-              ha = __builtin_amdgcn_sdot4((int)ae[j], (int)qb_r[g][2 * j], ha, false);
-              ha = __builtin_amdgcn_sdot4((int)ao[j], (int)qb_r[g][2 * j + 1], ha, false);
-              hb = __builtin_amdgcn_sdot4((int)be[j], (int)qb_r[g][2 * j], hb, false);
-              hb = __builtin_amdgcn_sdot4((int)bo[j], (int)qb_r[g][2 * j + 1], hb, false);
-            }
-          }
-          // lanes of one block add their integers, then one scale per block
-          ha = group_sum_i<LPB>(ha);
-          hb = group_sum_i<LPB>(hb);
-          float xa = (float)ha * da, xb = (float)hb * db;
-          asm volatile("" : "+v"(xa), "+v"(xb));   // no multiply-add re-fusion across the DPP
-          pa[g] = group_sum_rest<LPT, LPB>(xa);
-          pb[g] = group_sum_rest<LPT, LPB>(xb);
+        } else if constexpr (KB != 16) {
+          da = h2f(kscl[s % R][0]);
+          db = h2f(kscl[s % R][1]);
         }
-        // keep the last reduction step out of the store's branch (so it fuses with DPP)
-        asm volatile("" : "+v"(pa[g]), "+v"(pb[g]));
-      }
-      if (sub == 0) {
+        float pa[GP], pb[GP];
 #pragma unroll
         for (int g = 0; g < GP; ++g) {
-          s_sc[wave][la][g] = pa[g];
-          s_sc[wave][lb][g] = pb[g];
+          if constexpr (KB == 16) {
+            float xa = 0.f, xb = 0.f;
+#pragma unroll
+            for (int j = 0; j < KW; ++j) {
+              xa = __builtin_amdgcn_fdot2(as_h2(qa_r[g][j]), as_h2(ka[j]), xa, false);
+              xb = __builtin_amdgcn_fdot2(as_h2(qa_r[g][j]), as_h2(kb[j]), xb, false);
+            }
+            pa[g] = group_sum<LPT>(xa);
+            pb[g] = group_sum<LPT>(xb);
+          } else if constexpr (KB == kF8) {
+            float xa = 0.f, xb = 0.f;
+#pragma unroll
+            for (int j = 0; j < QW; ++j) {
+              xa = __builtin_amdgcn_fdot2(as_h2(qa_r[g][j]), fa[j], xa, false);
+              xb = __builtin_amdgcn_fdot2(as_h2(qa_r[g][j]), fb[j], xb, false);
+            }
+            if constexpr (QLO) {
+#pragma unroll
+              for (int j = 0; j < QW; ++j) {
+                xa = __builtin_amdgcn_fdot2(as_h2(qb_r[g][j]), fa[j], xa, false);
+                xb = __builtin_amdgcn_fdot2(as_h2(qb_r[g][j]), fb[j], xb, false);
+              }
+            }
+            pa[g] = group_sum<LPT>(xa);
+            pb[g] = group_sum<LPT>(xb);
+          } else {
+            // one chain per token: high digit, times 256, then the low digit
+            int ha = corr_a[g], hb = corr_a[g];
+            if constexpr (KB == 8) {
+              // the first product starts the chain (8-bit keys need no offset correction)
+              ha = sdot4_start((int)ka[0], (int)qa_r[g][0]);
+              hb = sdot4_start((int)kb[0], (int)qa_r[g][0]);
+#pragma unroll
+              for (int j = 1; j < KW; ++j) {
+                ha = __builtin_amdgcn_sdot4((int)ka[j], (int)qa_r[g][j], ha, false);
+                hb = __builtin_amdgcn_sdot4((int)kb[j], (int)qa_r[g][j], hb, false);
+              }
+              ha = (ha << 8) + corr_b[g];
+              hb = (hb << 8) + corr_b[g];
+#pragma unroll
+              for (int j = 0; j < KW; ++j) {
+                ha = __builtin_amdgcn_sdot4((int)ka[j], (int)qb_r[g][j], ha, false);
+                hb = __builtin_amdgcn_sdot4((int)kb[j], (int)qb_r[g][j], hb, false);
+              }
+            } else {
+              uint32_t ae[KW], ao[KW], be[KW], bo[KW];
+#pragma unroll
+              for (int j = 0; j < KW; ++j) {
+                ae[j] = ka[j] & 0x0F0F0F0Fu; ao[j] = (ka[j] >> 4) & 0x0F0F0F0Fu;
+                be[j] = kb[j] & 0x0F0F0F0Fu; bo[j] = (kb[j] >> 4) & 0x0F0F0F0Fu;
+              }
+#pragma unroll
+              for (int j = 0; j < KW; ++j) {
+                ha = __builtin_amdgcn_sdot4((int)ae[j], (int)qa_r[g][2 * j], ha, false);
+                ha = __builtin_amdgcn_sdot4((int)ao[j], (int)qa_r[g][2 * j + 1], ha, false);
+                hb = __builtin_amdgcn_sdot4((int)be[j], (int)qa_r[g][2 * j], hb, false);
+                hb = __builtin_amdgcn_sdot4((int)bo[j], (int)qa_r[g][2 * j + 1], hb, false);
+              }
+              ha = (ha << 8) + corr_b[g];
+              hb = (hb << 8) + corr_b[g];
+#pragma unroll
+              for (int j = 0; j < KW; ++j) {
+                ha = __builtin_amdgcn_sdot4((int)ae[j], (int)qb_r[g][2 * j], ha, false);
+                ha = __builtin_amdgcn_sdot4((int)ao[j], (int)qb_r[g][2 * j + 1], ha, false);
+                hb = __builtin_amdgcn_sdot4((int)be[j], (int)qb_r[g][2 * j], hb, false);
+                hb = __builtin_amdgcn_sdot4((int)bo[j], (int)qb_r[g][2 * j + 1], hb, false);
+              }
+            }
+            // lanes of one block add their integers, then one scale per block
+            ha = group_sum_i<LPB>(ha);
+            hb = group_sum_i<LPB>(hb);
+            float xa = (float)ha * da, xb = (float)hb * db;
+            asm volatile("" : "+v"(xa), "+v"(xb));   // no multiply-add re-fusion across the DPP
+            pa[g] = group_sum_rest<LPT, LPB>(xa);
+            pb[g] = group_sum_rest<LPT, LPB>(xb);
+          }
+          // keep the last reduction step out of the store's branch (so it fuses with DPP)
+          asm volatile("" : "+v"(pa[g]), "+v"(pb[g]));
         }
+        if (sub == 0) {
+#pragma unroll
+          for (int g = 0; g < GP; ++g) {
+            s_sc[wave][la][g] = pa[g];
+            s_sc[wave][lb][g] = pb[g];
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
     }
     // (the first value codes of the chunk fly during the softmax statistics)
     wave_lds_sync();
@@ -474,7 +568,11 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       if (s + PD < NS) load_v(rc, s + PD);
-      else load_k(rn, s + PD - NS);   // the next chunk (none: an empty range, no traffic)
+      else if constexpr (MQK) {   // the next chunk's first key groups (none: an empty range)
+        if (s + PD - NS < PDK) load_kg(rn, s + PD - NS);
+      } else {
+        load_k(rn, s + PD - NS);   // the next chunk (none: an empty range, no traffic)
+      }
       const uint32_t* va = vbuf[s % R][0];
       const uint32_t* vb = vbuf[s % R][1];
       // weights of the token pair: fp16 p times the tokens' value scales (packed fp16)
