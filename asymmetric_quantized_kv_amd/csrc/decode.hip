@@ -37,7 +37,7 @@
 #define KVQ_DECODE_DEPTH 4   // steps of key/value codes requested ahead of the one computing
 #endif
 #ifndef KVQ_DECODE_MFMA_QK
-#define KVQ_DECODE_MFMA_QK 1 // 8-bit keys: Q.K on the matrix cores (int8 MFMA per 32-element block)
+#define KVQ_DECODE_MFMA_QK 1 // 8/4-bit keys: Q.K on the matrix cores (int8 MFMA per 32-element block)
 #endif
 
 namespace kvq {
@@ -267,22 +267,55 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     }
   }
 
-  // 8-bit keys on the matrix cores: v_mfma_i32_32x32x32_i8 multiplies the query's digit
+  // 8/4-bit keys on the matrix cores: v_mfma_i32_32x32x32_i8 multiplies the query's digit
   // rows (row 2 g + i = digit i of head g, zero above 2 GP) by one 32-element block of 32
   // tokens' key codes.  Lane (r, h) of a wave holds A row r = lane % 32 and B column
-  // (token) r, elements 16 h .. 16 h + 15 of the block (h = lane / 32).
-  constexpr bool MQK = KB == 8 && KVQ_DECODE_MFMA_QK;
+  // (token) r, elements 16 h .. 16 h + 15 of the block (h = lane / 32).  4-bit codes enter as
+  // their nibbles u = q + 8 in the order even elements, then odd ones (k = 4 i + j is element
+  // 2 j + (i & 1) + 8 (i >> 1)); the query rows follow the same order, and 8 times the
+  // block's digit sums is subtracted from each result.
+  // (4-bit keys at group 16 keep the VALU path: the corrections do not fit beside 16 heads'
+  // accumulators)
+  constexpr bool MQK = (KB == 8 || (KB == 4 && GP <= 8)) && KVQ_DECODE_MFMA_QK;
+  constexpr int NQ = (2 * GP + 7) / 8;   // quads of result rows that hold query rows
   i32x4 qA[MQK ? NB : 1];
+  int qcorr[MQK && KB == 4 ? NQ : 1][2][MQK && KB == 4 ? NB : 1];   // 8 (256 S_hi + S_lo) per head, block
   if constexpr (MQK) {
     const int r = lane & 31, hl = lane >> 5;
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       i32x4 x = {0, 0, 0, 0};
       if (r < 2 * GP) {
-        const int8_t* src = (r & 1) ? &s_qb[r >> 1][0] : &s_qa[r >> 1][0];
-        x = *reinterpret_cast<const i32x4*>(src + 32 * b + 16 * hl);
+        const int8_t* src = ((r & 1) ? &s_qb[r >> 1][0] : &s_qa[r >> 1][0]) + 32 * b + 16 * hl;
+        if constexpr (KB == 8) {
+          x = *reinterpret_cast<const i32x4*>(src);
+        } else {
+          int8_t t[16];
+#pragma unroll
+          for (int k = 0; k < 16; ++k) t[k] = src[2 * (k & 3) + ((k >> 2) & 1) + 8 * (k >> 3)];
+          __builtin_memcpy(&x, t, 16);
+        }
       }
       qA[b] = x;
+    }
+    if constexpr (KB == 4) {
+#pragma unroll
+      for (int q = 0; q < NQ; ++q)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int g = 4 * q + 2 * hl + h;
+#pragma unroll
+          for (int b = 0; b < NB; ++b) {
+            int sa = 0, sb = 0;
+            if (g < GP) {
+              for (int e = 0; e < kBlock; ++e) {
+                sa += s_qa[g][32 * b + e];
+                sb += s_qb[g][32 * b + e];
+              }
+            }
+            qcorr[q][h][b] = 8 * (256 * sa + sb);
+          }
+        }
     }
   }
 
@@ -331,16 +364,15 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   // MFMA key groups: 32 tokens each; lane (r, h) loads token r's bytes 32 b + 16 h .. + 16 of
   // every block b, and its fp16 scales (a ring of RK groups, PDK groups ahead)
   constexpr int NG = CT / 32, PDK = 2, RK = PDK + 1;
-  i32x4 kq[MQK ? RK : 1][MQK ? NB : 1];
+  constexpr int KQW = KB == 8 ? 4 : 2;   // code dwords per lane and block
+  uint32_t kq[MQK ? RK : 1][MQK ? NB : 1][KQW];
   uint32_t kqs[MQK ? RK : 1][MQK ? (NB + 1) / 2 : 1];
-  const uint32_t kqoff = (lane & 31) * KC + 16 * (lane >> 5), kqsoff = (lane & 31) * KS;
+  const uint32_t kqoff = (lane & 31) * KC + (KB == 8 ? 16 : 8) * (lane >> 5), kqsoff = (lane & 31) * KS;
   auto load_kg = [&](const Rsrc& r, int j) {
     if constexpr (MQK) {
       const int slot = j % RK;
 #pragma unroll
-      for (int b = 0; b < NB; ++b)
-        kq[slot][b] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(r.kc, (int)(kqoff + 32 * b),
-                                                                                      (int)(j * 32 * KC), 0));
+      for (int b = 0; b < NB; ++b) buf_dwords<KQW>(r.kc, kqoff + (KB == 8 ? 32 : 16) * b, j * 32 * KC, kq[slot][b]);
       if constexpr (NB == 4) {
         const u32x2 t = __builtin_amdgcn_raw_buffer_load_b64(r.ks, (int)kqsoff, (int)(j * 32 * KS), 0);
         kqs[slot][0] = t.x;
@@ -380,7 +412,6 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     if constexpr (MQK) {
       // late iterations request the chunk's first value steps instead of key groups
       constexpr int VPER = (PD + PDK - 1) / PDK;
-      constexpr int NQ = (2 * GP + 7) / 8;   // quads of D rows that hold query rows
 #pragma unroll
       for (int j = 0; j < NG; ++j) {
         if (j + PDK < NG) {
@@ -397,13 +428,26 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         for (int q = 0; q < NQ; ++q) sc[q][0] = sc[q][1] = 0.f;
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
+          i32x4 kb;
+          if constexpr (KB == 8) {
+            kb = i32x4{(int)kq[slot][b][0], (int)kq[slot][b][1], (int)kq[slot][b][2], (int)kq[slot][b][3]};
+          } else {   // nibbles -> bytes: even elements, then odd ones
+            const uint32_t w0 = kq[slot][b][0], w1 = kq[slot][b][1];
+            kb = i32x4{(int)(w0 & 0x0F0F0F0Fu), (int)((w0 >> 4) & 0x0F0F0F0Fu), (int)(w1 & 0x0F0F0F0Fu),
+                       (int)((w1 >> 4) & 0x0F0F0F0Fu)};
+          }
           const i32x16 zero = {};
-          const i32x16 dq = __builtin_amdgcn_mfma_i32_32x32x32_i8(qA[b], kq[slot][b], zero, 0, 0, 0);
+          const i32x16 dq = __builtin_amdgcn_mfma_i32_32x32x32_i8(qA[b], kb, zero, 0, 0, 0);
           const float d = h2f((uint16_t)(kqs[slot][b >> 1] >> (16 * (b & 1))));
 #pragma unroll
           for (int q = 0; q < NQ; ++q) {
-            sc[q][0] = fmaf((float)((dq[4 * q] << 8) + dq[4 * q + 1]), d, sc[q][0]);
-            sc[q][1] = fmaf((float)((dq[4 * q + 2] << 8) + dq[4 * q + 3]), d, sc[q][1]);
+            int x0 = (dq[4 * q] << 8) + dq[4 * q + 1], x1 = (dq[4 * q + 2] << 8) + dq[4 * q + 3];
+            if constexpr (KB == 4) {
+              x0 -= qcorr[q][0][b];
+              x1 -= qcorr[q][1][b];
+            }
+            sc[q][0] = fmaf((float)x0, d, sc[q][0]);
+            sc[q][1] = fmaf((float)x1, d, sc[q][1]);
           }
         }
         const int t = 32 * j + (lane & 31);
@@ -568,8 +612,12 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       if (s + PD < NS) load_v(rc, s + PD);
-      else if constexpr (MQK) {   // the next chunk's first key groups (none: an empty range)
+      else if constexpr (MQK) {   // the next chunk's first PDK key groups (none: an empty range)
         if (s + PD - NS < PDK) load_kg(rn, s + PD - NS);
+        if (s == NS - 1) {        // chunks of fewer value steps than PDK + 1: the rest at the end
+#pragma unroll
+          for (int g = PD; g < PDK; ++g) load_kg(rn, g);
+        }
       } else {
         load_k(rn, s + PD - NS);   // the next chunk (none: an empty range, no traffic)
       }

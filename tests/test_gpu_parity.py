@@ -128,6 +128,8 @@ DECODE_CASES = [
     ("K8V4", 64, 16, "f32", [600]),
     ("K4V8", 128, 16, "bf16", [257]),
     ("FP16", 64, 2, "f16", [64, 5000]),
+    ("K8V4", 64, 2, "bf16", [700, 2049]),     # two value steps per chunk: short prefetch
+    ("K4V4", 64, 1, "f32", [900]),
     ("KF8V4", 128, 8, "bf16", [1, 129, 3000]),
     ("KF8V4", 64, 4, "f32", [700, 2049]),
     ("KF8V4", 128, 3, "f16", [513]),
