@@ -58,6 +58,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // Buffer resource over `bytes` bytes at p (raw, byte-addressed); loads through it take a
 // per-lane 32-bit offset and a wave-uniform offset, so addresses cost no vector ALU.
@@ -319,6 +321,32 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     }
   }
 
+  // fp8 keys on the matrix cores: v_mfma_f32_32x32x16_f16 with the query rows (row g = head g,
+  // or rows 2 g + i = its fp16 hi and lo parts for fp32 queries) against 32 tokens' keys
+  // widened to fp16 (exactly; the block's power-of-two scale folds into the conversion).
+  // Lane (r, h) loads token r's bytes [h D / 2, (h + 1) D / 2); k-step k takes its bytes
+  // 8 k .. 8 k + 7 (block (h D / 2 + 8 k) / 32), and the query rows follow that order.
+  constexpr bool MQF = KB == kF8 && KVQ_DECODE_MFMA_QK;
+  constexpr int NK8 = D / 16;                       // k-steps of one 32-token group
+  constexpr int QROWS = QLO ? 2 * GP : GP;
+  half8_t qF[MQF ? NK8 : 1];
+  if constexpr (MQF) {
+    const int r = lane & 31, hl = lane >> 5;
+    const int g = QLO ? r >> 1 : r;
+    const bool on = r < QROWS;
+    const float qi = on ? s_qi[g] : 0.f;
+#pragma unroll
+    for (int k = 0; k < NK8; ++k) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float x = on ? s_q[g][(D / 2) * hl + 8 * k + i] * qi : 0.f;
+        const _Float16 hi = (_Float16)x;
+        qF[k][i] = (QLO && (r & 1)) ? (_Float16)(x - (float)hi) : hi;
+      }
+    }
+  }
+  constexpr bool MQ = MQK || MQF;
+
   float acc[GP][E];
   float wsum[GP], lsum[GP], m[GP];
 #pragma unroll
@@ -368,7 +396,17 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   uint32_t kq[MQK ? RK : 1][MQK ? NB : 1][KQW];
   uint32_t kqs[MQK ? RK : 1][MQK ? (NB + 1) / 2 : 1];
   const uint32_t kqoff = (lane & 31) * KC + (KB == 8 ? 16 : 8) * (lane >> 5), kqsoff = (lane & 31) * KS;
+  constexpr int KFW = MQF ? D / 8 : 1;   // fp8 code dwords per lane and group
+  uint32_t kf[MQF ? RK : 1][KFW];
+  uint32_t kfs[MQF ? RK : 1];
+  const uint32_t kfoff = (lane & 31) * KC + (D / 2) * (lane >> 5), kfsoff = (lane & 31) * KS;
   auto load_kg = [&](const Rsrc& r, int j) {
+    if constexpr (MQF) {
+      const int slot = j % RK;
+      buf_dwords<KFW>(r.kc, kfoff, j * 32 * KC, kf[slot]);
+      if constexpr (KS == 4) kfs[slot] = __builtin_amdgcn_raw_buffer_load_b32(r.ks, (int)kfsoff, (int)(j * 32 * KS), 0);
+      else kfs[slot] = buf_u16(r.ks, kfsoff, j * 32 * KS);
+    }
     if constexpr (MQK) {
       const int slot = j % RK;
 #pragma unroll
@@ -395,7 +433,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   int64_t c = __builtin_amdgcn_readfirstlane(wave);
   Rsrc rc = chunk_rsrc(c, CT);
   if (c < n_chunks) {
-    if constexpr (MQK) {
+    if constexpr (MQ) {
 #pragma unroll
       for (int j = 0; j < PDK; ++j) load_kg(rc, j);
     } else {
@@ -409,7 +447,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     const bool more = c + 4 < n_chunks;
     const Rsrc rn = chunk_rsrc(c + 4, more ? CT : 0);
     // ---- phase A: scores ----------------------------------------------------------
-    if constexpr (MQK) {
+    if constexpr (MQ) {
       // late iterations request the chunk's first value steps instead of key groups
       constexpr int VPER = (PD + PDK - 1) / PDK;
 #pragma unroll
@@ -423,11 +461,49 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         }
         const int slot = j % RK;
         // lane (token, h) gets D rows 8 q + 4 h + {0..3}: heads 4 q + 2 h + {0, 1}, both digits
+        // (or hi and lo parts); with one row per head (fp8 keys, 16-bit queries) heads 8 q + 4 h + {0..3}
         float sc[NQ][2];
 #pragma unroll
         for (int q = 0; q < NQ; ++q) sc[q][0] = sc[q][1] = 0.f;
+        if constexpr (MQF) {
+          const int hl = lane >> 5;
+          f32x16 fa = {};
 #pragma unroll
-        for (int b = 0; b < NB; ++b) {
+          for (int k = 0; k < NK8; ++k) {
+            const int blk = ((D / 2) * hl + 8 * k) / kBlock;
+            const float x = __uint_as_float(((kfs[slot] >> (8 * blk)) & 255u) << 23);
+            const half2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)kf[slot][2 * k], x, false);
+            const half2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)kf[slot][2 * k], x, true);
+            const half2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)kf[slot][2 * k + 1], x, false);
+            const half2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)kf[slot][2 * k + 1], x, true);
+            const half8_t kb8 = {p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+            fa = __builtin_amdgcn_mfma_f32_32x32x16_f16(qF[k], kb8, fa, 0, 0, 0);
+          }
+          const int t = 32 * j + (lane & 31);
+          if constexpr (QLO) {
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) {
+              sc[q][0] = fa[4 * q] + fa[4 * q + 1];
+              sc[q][1] = fa[4 * q + 2] + fa[4 * q + 3];
+            }
+          } else {
+#pragma unroll
+            for (int q = 0; q < (GP + 7) / 8; ++q) {
+              const int g0 = 8 * q + 4 * hl;
+              if (g0 + 3 < GP) {
+                *reinterpret_cast<float4*>(&s_sc[wave][t][g0]) =
+                    make_float4(fa[4 * q], fa[4 * q + 1], fa[4 * q + 2], fa[4 * q + 3]);
+              } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                  if (g0 + i < GP) s_sc[wave][t][g0 + i] = fa[4 * q + i];
+              }
+            }
+            continue;   // scores stored
+          }
+        }
+#pragma unroll
+        for (int b = 0; b < (MQK ? NB : 0); ++b) {
           i32x4 kb;
           if constexpr (KB == 8) {
             kb = i32x4{(int)kq[slot][b][0], (int)kq[slot][b][1], (int)kq[slot][b][2], (int)kq[slot][b][3]};
@@ -612,7 +688,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       if (s + PD < NS) load_v(rc, s + PD);
-      else if constexpr (MQK) {   // the next chunk's first PDK key groups (none: an empty range)
+      else if constexpr (MQ) {   // the next chunk's first PDK key groups (none: an empty range)
         if (s + PD - NS < PDK) load_kg(rn, s + PD - NS);
         if (s == NS - 1) {        // chunks of fewer value steps than PDK + 1: the rest at the end
 #pragma unroll
