@@ -15,13 +15,14 @@
 // of split s on die s whenever the split count is a multiple of 8.)  Within a wave, E = D / LPT
 // elements of a token belong to one lane (LPT lanes per token), and each lane holds
 // two tokens per step, t and t + 64 / LPT.  A chunk is processed in three phases:
-//   A  scores: integer dot products (v_dot4_i32_i8) of the 8/4-bit key codes with the
-//      query (one scale per head) split into two int8 digits, or fp16 dot2 for the fp16
-//      control; the lanes of one block add their integers, scale by the block's d, and
-//      the block sums are reduced over the LPT lanes with DPP.  fp8 (E4M3) key codes are
-//      widened to fp16 with the block's power-of-two scale folded into the conversion
-//      (exact), then meet the query (scaled by a power of two into fp16's range, fp32
-//      queries as fp16 hi + lo) in fp16 dot2;
+//   A  scores, on the matrix cores for quantized keys: the query (one scale per head)
+//      split into two int8 digits meets 32 tokens' 8/4-bit key codes of one 32-element
+//      block in v_mfma_i32_32x32x32_i8 (exact integer block sums, then the block's d);
+//      fp8 (E4M3) key codes are widened to fp16 with the block's power-of-two scale folded
+//      into the conversion (exact) and meet the query (scaled by a power of two into
+//      fp16's range, fp32 queries as fp16 hi + lo) in v_mfma_f32_32x32x16_f16.  The fp16
+//      control, and 4-bit keys at group 16, use VALU dot products (fp16 dot2, v_dot4) with
+//      the lanes of a token reduced by DPP;
 //   B  one lane per token: the query's scale turns the raw score into a base-2 logit;
 //      exact running max of the chunk per query head, p = 2^(s-m),
 //      the accumulators rescaled only when the max moved;
