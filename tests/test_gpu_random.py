@@ -1,7 +1,8 @@
-"""Seeded random sweep of the GPU path against the oracle: layouts, head_dims, group sizes,
+"""Seeded random sweep of the GPU path against the oracle (48 cases): layouts, head_dims, group sizes,
 input dtypes, session lengths and turn sizes drawn at random (fixed seed), each case small
 enough for the oracle to finish in well under a second.  Planes bit-exact; decode and chunk
-outputs within 5e-3."""
+outputs within 5e-3, through the one-call entry points and through the two passes with a
+random split."""
 from __future__ import annotations
 
 import numpy as np
@@ -34,7 +35,7 @@ def draw_cases(n: int, seed: int = 20261203):
     return cases
 
 
-CASES = draw_cases(24)
+CASES = draw_cases(48)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -79,8 +80,17 @@ def test_random_case_matches_oracle(case):
             qc = I.bf16_round(qc)
         outc = kvq.kv_attend_chunk(sessions[0], 0, dev(qc, dtype), n_new, scale)
         err_c = max_err(outc, O.attend_chunk(ocs[0], 0, host_inputs(qc, dtype), n_new, scale))
-        log(f"  decode err {err_d:.3e}, chunk err {err_c:.3e}")
-        assert err_d <= TOL and err_c <= TOL
+        # the two passes with a split of the test's choosing
+        rng = np.random.default_rng(4000 + i)
+        longest = max(lens)
+        per = 512 * int(rng.integers(1, max(1, -(-longest // 512)) + 1))
+        parts = kvq.kv_attend_decode_partial(sessions, 0, dev(q, dtype), scale, -(-longest // per), per)
+        err_p = max_err(kvq.kv_merge_partials(parts), O.attend_decode(ocs, 0, host_inputs(q, dtype), scale))
+        kper = 64 * int(rng.integers(1, max(1, -(-lens[0] // 64)) + 1))
+        cparts = kvq.kv_attend_chunk_partial(sessions[0], 0, dev(qc, dtype), n_new, scale, -(-lens[0] // kper), kper)
+        err_cp = max_err(kvq.kv_merge_partials(cparts), O.attend_chunk(ocs[0], 0, host_inputs(qc, dtype), n_new, scale))
+        log(f"  decode err {err_d:.3e}, chunk err {err_c:.3e}; two-pass {per}: {err_p:.3e}, {kper}: {err_cp:.3e}")
+        assert err_d <= TOL and err_c <= TOL and err_p <= TOL and err_cp <= TOL
     finally:
         torch.cuda.synchronize()
         for h in sessions:
