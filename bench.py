@@ -483,6 +483,20 @@ def full_rebuild(args, kvq, I, torch, dev, stream, log_fn):
 
         rebuild()
         torch.cuda.synchronize()
+        if L == "K8V4":   # the 32 appends alone: quantize-on-append at 4,096 tokens per call
+            ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            kvq.kv_cache_reset(h)
+            ea.record(stream)
+            for c in range(n_chunks):
+                kvq.kv_append_quant(h, 0, ks[c], vs[c])
+            eb.record(stream)
+            torch.cuda.synchronize()
+            t_app = ea.elapsed_time(eb) / n_chunks
+            io = chunk * hkv * (2 * D * 2 + kvq.kv_layout_footprint_bytes(L, 1, 1, D, 256) // 256)
+            res["append_4096"] = {"layout": L, "us_per_call": round(t_app * 1e3, 2), "bytes_per_call": io,
+                                  "GBps": round(io / (t_app * 1e-3) / 1e9, 1),
+                                  "hbm_frac": round(io / (t_app * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+            log_fn(f"append of 4,096 tokens: {t_app * 1e3:.2f} us ({res['append_4096']['GBps']} GB/s in + out)")
         reps = 3
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
