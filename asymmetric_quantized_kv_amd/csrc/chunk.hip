@@ -9,8 +9,13 @@
 // (v_mfma_f32_32x32x16_f16).  Operands are fp16 rather than bf16: a code times an fp16
 // scale needs more than bf16's 8 significant bits (a 1-key attention would return the
 // value with a 2^-9 relative error), while fp16 keeps 11 bits at the same MFMA rate.
-// Quantized keys are carried as fp16 hi + lo (code * scale = hi + lo exactly), so scores
-// are exact up to fp32 accumulation; fp32 queries are likewise carried as hi + lo.
+// A quantized key (code * scale: up to 18 significant bits) is carried as its fp16 rounding
+// hi plus the rest lo = code * scale - hi, which fp16 holds exactly.  hi meets the query on
+// the fp16 MFMA.  lo, at most 2^-11 of the key, goes to LDS as fp8 (E4M3) with a power-of-two
+// scale per 32-element block and meets an fp8 copy of the query (also block-scaled) on the
+// block-scaled fp8 MFMA (v_mfma_scale_f32_32x32x64_f8f6f4) at twice the fp16 rate: keys then
+// carry about 2^-15 relative error instead of fp16's 2^-12.  fp32 queries are carried as
+// fp16 hi + lo.
 // fp8 (E4M3) keys with power-of-two block scales widen to fp16 exactly in one conversion
 // (v_cvt_scalef32_pk_f16_fp8), so they need no low part: one MFMA per k-step.
 //
@@ -28,11 +33,12 @@
 
 #include <type_traits>
 
-// 1: quantized keys as the exact fp16 hi + lo split (the built form).  0 drops the lo part:
-// keys then carry fp16 rounding (2^-12 relative), which measured up to 4.9e-3 of attention
-// error against the 5e-3 tolerance, so it is kept only to reproduce that measurement.
-#ifndef KVQ_CHUNK_KSPLIT
-#define KVQ_CHUNK_KSPLIT 1
+// The low part of 8/4-bit keys: 2 = fp8 with block scales on the fp8 MFMA (the built form);
+// 1 = exact fp16 on the fp16 MFMA (one more fp16 MFMA per k-step); 0 = none: keys then carry
+// fp16 rounding (2^-12 relative), which measured up to 4.9e-3 of attention error against the
+// 5e-3 tolerance, so 0 is kept only to reproduce that measurement.
+#ifndef KVQ_CHUNK_KLO
+#define KVQ_CHUNK_KLO 2
 #endif
 
 namespace kvq {
@@ -42,6 +48,8 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float float16_t __attribute__((ext_vector_type(16)));
+typedef int int8v_t __attribute__((ext_vector_type(8)));
+typedef short short2_t __attribute__((ext_vector_type(2)));
 
 constexpr float kLazyMax = 8.f;   // log2 headroom before the running max is moved
 
@@ -60,6 +68,24 @@ __device__ __forceinline__ half2_t splat(uint16_t b) {
   r.x = h;
   r.y = h;
   return r;
+}
+
+// max and sum of lanes i and i ^ 32 (v_permlane32_swap: no LDS round trip)
+__device__ __forceinline__ float swap32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float swap32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// four fp16 values / 2^t as four E4M3 bytes (the conversion divides by its scale operand)
+__device__ __forceinline__ uint32_t fp8x4(half2_t a, half2_t b, float scale) {
+  short2_t r = {0, 0};
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(r, a, scale, false);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(r, b, scale, true);
+  return __builtin_bit_cast(uint32_t, r);
 }
 
 template <int W>
@@ -101,9 +127,10 @@ __device__ __forceinline__ void k4_pairs(uint32_t w, half2_t (&c)[4]) {
   }
 }
 
-template <int KB, int VB, int D, bool QSPLIT, bool KSPLIT_>
+template <int KB, int VB, int D, bool QSPLIT, int KLO_>
 __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(ChunkArgs a) {
-  constexpr bool KSPLIT = KSPLIT_ && KB != 16 && KB != kF8;   // fp16 and fp8 keys are exact already
+  constexpr int KLO = KB == 16 || KB == kF8 ? 0 : KLO_;   // fp16 and fp8 keys are exact already
+  constexpr bool KSPLIT = KLO != 0;
   constexpr int NK = kChunkKeys;   // keys per tile
   constexpr int KSTR = D + 8;      // halves per LDS key row
   constexpr int VSTR = NK + 4;     // halves per LDS transposed-value row (34 dwords: no bank conflicts)
@@ -114,10 +141,17 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(ChunkArgs a) {
   constexpr int VW = VB / 4;       // dwords of 8 value elements of one key
   constexpr int VITEMS = (NK / 4) * (D / 8);  // (4 keys x 8 d) value items per tile
   constexpr int KBUF = NK * KSTR, VBUF = D * VSTR;
+  // fp8 low parts: LDS rows of D bytes (+16: conflict-free 16-byte reads down a column), and
+  // per key and block the E8M0 exponent of its scale, ordered [h][m] for block 2 m + h (the
+  // scaled MFMA takes block 2 m + h of its m-th product from lane half h)
+  constexpr int NB = D / kBlock, NBH = NB / 2, LSTR = D + 16;
   static_assert(kChunkThreads == 768 && kChunkRows == 256, "8 consumer + 4 producer waves");
   // two tile buffers: the producers fill one while the consumers read the other
   __shared__ __attribute__((aligned(16))) _Float16 s_k[2 * KBUF];
-  __shared__ __attribute__((aligned(16))) _Float16 s_kl[KSPLIT ? 2 * KBUF : 8];
+  __shared__ __attribute__((aligned(16))) _Float16 s_kl[KLO == 1 ? 2 * KBUF : 8];
+  __shared__ __attribute__((aligned(16))) uint8_t s_kl8[KLO == 2 ? 2 * NK * LSTR : 16];
+  __shared__ __attribute__((aligned(4))) uint8_t s_kls[KLO == 2 ? 2 * NK * NB : 4];
+  __shared__ __attribute__((aligned(16))) uint8_t s_q8[KLO == 2 ? kChunkRows * LSTR : 16];  // fp8 queries
   __shared__ __attribute__((aligned(16))) _Float16 s_vt[2 * VBUF];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -185,7 +219,7 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(ChunkArgs a) {
     };
     auto produce = [&](int buf) {
       _Float16* bk = s_k + buf * KBUF;
-      _Float16* bkl = s_kl + (KSPLIT ? buf * KBUF : 0);
+      _Float16* bkl = s_kl + (KLO == 1 ? buf * KBUF : 0);
       _Float16* bv = s_vt + buf * VBUF;
       {
         half2_t hi[KE / 2], lo[KE / 2];
@@ -229,9 +263,25 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(ChunkArgs a) {
           const int off = k_key * KSTR + k_part * KE + 8 * i;
           *reinterpret_cast<uint4*>(&bk[off]) =
               make_uint4(u32(hi[4 * i]), u32(hi[4 * i + 1]), u32(hi[4 * i + 2]), u32(hi[4 * i + 3]));
-          if constexpr (KSPLIT)
+          if constexpr (KLO == 1)
             *reinterpret_cast<uint4*>(&bkl[off]) =
                 make_uint4(u32(lo[4 * i]), u32(lo[4 * i + 1]), u32(lo[4 * i + 2]), u32(lo[4 * i + 3]));
+        }
+        if constexpr (KLO == 2) {
+          // lo / 2^t as E4M3 with t = max(e, 1) - 26 for the fp16 exponent field e of the scale:
+          // |code * scale| < 2^(e - 7) bounds |lo| by 2^(e - 19), so |lo| / 2^t <= 128 (and a
+          // subnormal product's lo, below 2^-25, stays below 1)
+          const int e = max((int)((kscale >> 10) & 31), 1);
+          const float sc = __uint_as_float((uint32_t)(e + 101) << 23);
+          uint8_t* bl = s_kl8 + buf * NK * LSTR + k_key * LSTR + k_part * KE;
+#pragma unroll
+          for (int i = 0; i < KE / 16; ++i)
+            *reinterpret_cast<uint4*>(bl + 16 * i) =
+                make_uint4(fp8x4(lo[8 * i], lo[8 * i + 1], sc), fp8x4(lo[8 * i + 2], lo[8 * i + 3], sc),
+                           fp8x4(lo[8 * i + 4], lo[8 * i + 5], sc), fp8x4(lo[8 * i + 6], lo[8 * i + 7], sc));
+          const int b = (k_part * KE) / kBlock;
+          if ((k_part * KE) % kBlock == 0)
+            s_kls[buf * NK * NB + k_key * NB + (b & 1) * NBH + (b >> 1)] = (uint8_t)(e + 101);
         }
       }
       if (v_on) {
@@ -349,6 +399,33 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(ChunkArgs a) {
     }
   }
 
+  // fp8 copy of this wave's query rows for the low parts of the keys: one power-of-two scale
+  // 2^t per (row, block), t = floor(log2 amax) - 7 so that |q| / 2^t < 256 (2^-126 for a zero
+  // block); qs8[m] holds the E8M0 exponent of block 2 m + hl, which this lane feeds the
+  // scaled MFMA
+  uint32_t qs8[KLO == 2 ? NBH : 1];
+  if constexpr (KLO == 2) {
+    uint8_t* q8 = s_q8 + (wave * 32 + col) * LSTR;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      float am = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf((float)qv[2 * b + kk][i]));
+      am = swap32_max(am);
+      const int t = max((int)((__float_as_uint(am) >> 23) & 255) - 134, -126);
+      const float sc = __uint_as_float((uint32_t)(t + 127) << 23);
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const half8_t x = qv[2 * b + kk];
+        const half2_t p0 = {x[0], x[1]}, p1 = {x[2], x[3]}, p2 = {x[4], x[5]}, p3 = {x[6], x[7]};
+        *reinterpret_cast<uint2*>(q8 + 16 * (2 * b + kk) + 8 * hl) = make_uint2(fp8x4(p0, p1, sc), fp8x4(p2, p3, sc));
+      }
+      if ((b & 1) == hl) qs8[b >> 1] = (uint32_t)(t + 127);
+    }
+  }
+
   float m = -INFINITY, l = 0.f;
   float16_t o[NDT];
 #pragma unroll
@@ -357,7 +434,8 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(ChunkArgs a) {
     for (int v = 0; v < 16; ++v) o[t][v] = 0.f;
 
   // one 32-key half of a tile: S^T = K Q^T, online softmax, O^T += V^T P^T
-  auto half = [&](auto masked, const _Float16* bk, const _Float16* bkl, const _Float16* bv, int64_t kt0, int st) {
+  auto half = [&](auto masked, const _Float16* bk, const _Float16* bkl, const uint8_t* bkl8, const uint8_t* bks,
+                  const _Float16* bv, int64_t kt0, int st) {
     float16_t sv;
 #pragma unroll
     for (int v = 0; v < 16; ++v) sv[v] = 0.f;
@@ -366,11 +444,30 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(ChunkArgs a) {
       const int off = (32 * st + col) * KSTR + 16 * k + 8 * hl;
       const half8_t ak = *reinterpret_cast<const half8_t*>(&bk[off]);
       sv = __builtin_amdgcn_mfma_f32_32x32x16_f16(ak, qv[k], sv, 0, 0, 0);
-      if constexpr (KSPLIT) {
+      if constexpr (KLO == 1) {
         const half8_t al = *reinterpret_cast<const half8_t*>(&bkl[off]);
         sv = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, qv[k], sv, 0, 0, 0);
       }
       if constexpr (QSPLIT) sv = __builtin_amdgcn_mfma_f32_32x32x16_f16(ak, ql[k], sv, 0, 0, 0);
+    }
+    if constexpr (KLO == 2) {
+      // m-th product: lane half hl brings bytes 16 hl .. + 15 of blocks 2 m and 2 m + 1, and the
+      // scale of block 2 m + hl (16-byte group g of both halves is block 2 m + g)
+      const uint8_t* kl = bkl8 + (32 * st + col) * LSTR + 16 * hl;
+      const uint8_t* ql8 = s_q8 + (wave * 32 + col) * LSTR + 16 * hl;
+      const uint8_t* ksp = bks + (32 * st + col) * NB + hl * NBH;
+      const uint32_t asc = NBH == 2 ? (uint32_t)*reinterpret_cast<const uint16_t*>(ksp) : (uint32_t)*ksp;
+#pragma unroll
+      for (int mm = 0; mm < NBH; ++mm) {
+        const uint4 a0 = *reinterpret_cast<const uint4*>(kl + 64 * mm);
+        const uint4 a1 = *reinterpret_cast<const uint4*>(kl + 64 * mm + 32);
+        const uint4 b0 = *reinterpret_cast<const uint4*>(ql8 + 64 * mm);
+        const uint4 b1 = *reinterpret_cast<const uint4*>(ql8 + 64 * mm + 32);
+        const int8v_t av8 = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+        const int8v_t bv8 = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+        sv = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av8, bv8, sv, 0, 0, 0, (int)((asc >> (8 * mm)) & 255u), 0,
+                                                              (int)qs8[mm]);
+      }
     }
     if constexpr (decltype(masked)::value) {
       // keys kt0 + 32 st + [0, 32): offsets >= lim are past the range or in the future
@@ -384,7 +481,7 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(ChunkArgs a) {
     float mx = sv[0];
 #pragma unroll
     for (int v = 1; v < 16; ++v) mx = fmaxf(mx, sv[v]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.qk_scale;
+    mx = swap32_max(mx) * a.qk_scale;
     const bool move = mx > m + kLazyMax;
     if (__any(move)) {
       const float mn = move ? mx : m;
@@ -425,11 +522,13 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(ChunkArgs a) {
     if (wave_active) {
       const int buf = t & 1;
       const _Float16* bk = s_k + buf * KBUF;
-      const _Float16* bkl = s_kl + (KSPLIT ? buf * KBUF : 0);
+      const _Float16* bkl = s_kl + (KLO == 1 ? buf * KBUF : 0);
+      const uint8_t* bkl8 = s_kl8 + (KLO == 2 ? buf * NK * LSTR : 0);
+      const uint8_t* bks = s_kls + (KLO == 2 ? buf * NK * NB : 0);
       const _Float16* bv = s_vt + buf * VBUF;
       const int64_t kt0 = k_lo + (int64_t)t * NK;
-      half(masked, bk, bkl, bv, kt0, 0);
-      half(masked, bk, bkl, bv, kt0, 1);
+      half(masked, bk, bkl, bkl8, bks, bv, kt0, 0);
+      half(masked, bk, bkl, bkl8, bks, bv, kt0, 1);
     }
     __syncthreads();
   };
@@ -439,7 +538,7 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(ChunkArgs a) {
   for (; t < n_tiles; ++t) consume(std::true_type{}, t);
 
   // ---- output -----------------------------------------------------------------------
-  const float lt = l + __shfl_xor(l, 32);
+  const float lt = swap32_sum(l);
   if (!valid) return;
   const int64_t orow = tok * a.hq + qh;
   if (!a.partial) {
@@ -472,7 +571,7 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(ChunkArgs a) {
 
 template <int KB, int VB, int D, bool QSPLIT>
 const void* kernel_ptr() {
-  return reinterpret_cast<const void*>(&chunk_kernel<KB, VB, D, QSPLIT, KVQ_CHUNK_KSPLIT != 0>);
+  return reinterpret_cast<const void*>(&chunk_kernel<KB, VB, D, QSPLIT, KVQ_CHUNK_KLO>);
 }
 
 template <int KB, int VB, int D>
@@ -481,9 +580,9 @@ hipError_t launch_t(const ChunkArgs& a, hipStream_t s) {
   const int64_t mt = (rows + kChunkRows - 1) / kChunkRows;
   dim3 grid((unsigned)mt, a.hkv, a.n_splits);
   if (a.q_dtype == 0)
-    hipLaunchKernelGGL((chunk_kernel<KB, VB, D, true, KVQ_CHUNK_KSPLIT != 0>), grid, dim3(kChunkThreads), 0, s, a);
+    hipLaunchKernelGGL((chunk_kernel<KB, VB, D, true, KVQ_CHUNK_KLO>), grid, dim3(kChunkThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((chunk_kernel<KB, VB, D, false, KVQ_CHUNK_KSPLIT != 0>), grid, dim3(kChunkThreads), 0, s, a);
+    hipLaunchKernelGGL((chunk_kernel<KB, VB, D, false, KVQ_CHUNK_KLO>), grid, dim3(kChunkThreads), 0, s, a);
   return hipGetLastError();
 }
 
