@@ -33,12 +33,13 @@
 
 #include <type_traits>
 
-// The low part of 8/4-bit keys: 2 = fp8 with block scales on the fp8 MFMA (the built form);
-// 1 = exact fp16 on the fp16 MFMA (one more fp16 MFMA per k-step); 0 = none: keys then carry
-// fp16 rounding (2^-12 relative), which measured up to 4.9e-3 of attention error against the
-// 5e-3 tolerance, so 0 is kept only to reproduce that measurement.
+// The low part of 8/4-bit keys: 3 = fp6 (E2M3) with block scales on the block-scaled MFMA
+// at the fp6 rate (the built form for head_dim 128 and 16-bit queries; the others take 2); 2 = fp8 (E4M3)
+// likewise at the fp8 rate; 1 = exact fp16 on the fp16 MFMA (one more fp16 MFMA per k-step);
+// 0 = none: keys then carry fp16 rounding (2^-12 relative), which measured up to 4.9e-3 of
+// attention error against the 5e-3 tolerance, so 0 is kept only to reproduce that measurement.
 #ifndef KVQ_CHUNK_KLO
-#define KVQ_CHUNK_KLO 2
+#define KVQ_CHUNK_KLO 3
 #endif
 
 namespace kvq {
@@ -50,6 +51,8 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float float16_t __attribute__((ext_vector_type(16)));
 typedef int int8v_t __attribute__((ext_vector_type(8)));
 typedef short short2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half32_t __attribute__((ext_vector_type(32)));
+typedef unsigned int uint6v_t __attribute__((ext_vector_type(6)));
 
 constexpr float kLazyMax = 8.f;   // log2 headroom before the running max is moved
 
@@ -129,7 +132,10 @@ __device__ __forceinline__ void k4_pairs(uint32_t w, half2_t (&c)[4]) {
 
 template <int KB, int VB, int D, bool QSPLIT, int KLO_>
 __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(ChunkArgs a) {
-  constexpr int KLO = KB == 16 || KB == kF8 ? 0 : KLO_;   // fp16 and fp8 keys are exact already
+  // fp16 and fp8 keys are exact already; an fp6 low part needs a whole block per producer
+  // thread, and fp32 queries keep the fp8 one (the fp6 query exchange would spill their
+  // registers in the tile loop)
+  constexpr int KLO = KB == 16 || KB == kF8 ? 0 : (KLO_ == 3 && (D != 128 || QSPLIT) ? 2 : KLO_);
   constexpr bool KSPLIT = KLO != 0;
   constexpr int NK = kChunkKeys;   // keys per tile
   constexpr int KSTR = D + 8;      // halves per LDS key row
@@ -141,17 +147,18 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(ChunkArgs a) {
   constexpr int VW = VB / 4;       // dwords of 8 value elements of one key
   constexpr int VITEMS = (NK / 4) * (D / 8);  // (4 keys x 8 d) value items per tile
   constexpr int KBUF = NK * KSTR, VBUF = D * VSTR;
-  // fp8 low parts: LDS rows of D bytes (+16: conflict-free 16-byte reads down a column), and
-  // per key and block the E8M0 exponent of its scale, ordered [h][m] for block 2 m + h (the
-  // scaled MFMA takes block 2 m + h of its m-th product from lane half h)
+  // fp8 / fp6 low parts: LDS rows of D bytes (+16: conflict-free 16-byte reads down a column;
+  // an fp6 block takes 24 of its 32 bytes), and per key and block the E8M0 exponent of its
+  // scale, ordered [h][m] for block 2 m + h (the scaled MFMA takes the scale of block 2 m + h
+  // of its m-th product from lane half h)
   constexpr int NB = D / kBlock, NBH = NB / 2, LSTR = D + 16;
   static_assert(kChunkThreads == 768 && kChunkRows == 256, "8 consumer + 4 producer waves");
   // two tile buffers: the producers fill one while the consumers read the other
   __shared__ __attribute__((aligned(16))) _Float16 s_k[2 * KBUF];
   __shared__ __attribute__((aligned(16))) _Float16 s_kl[KLO == 1 ? 2 * KBUF : 8];
-  __shared__ __attribute__((aligned(16))) uint8_t s_kl8[KLO == 2 ? 2 * NK * LSTR : 16];
-  __shared__ __attribute__((aligned(4))) uint8_t s_kls[KLO == 2 ? 2 * NK * NB : 4];
-  __shared__ __attribute__((aligned(16))) uint8_t s_q8[KLO == 2 ? kChunkRows * LSTR : 16];  // fp8 queries
+  __shared__ __attribute__((aligned(16))) uint8_t s_kl8[KLO >= 2 ? 2 * NK * LSTR : 16];
+  __shared__ __attribute__((aligned(4))) uint8_t s_kls[KLO >= 2 ? 2 * NK * NB : 4];
+  __shared__ __attribute__((aligned(16))) uint8_t s_q8[KLO >= 2 ? kChunkRows * LSTR : 16];  // fp8 / fp6 queries
   __shared__ __attribute__((aligned(16))) _Float16 s_vt[2 * VBUF];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -282,6 +289,24 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(ChunkArgs a) {
           const int b = (k_part * KE) / kBlock;
           if ((k_part * KE) % kBlock == 0)
             s_kls[buf * NK * NB + k_key * NB + (b & 1) * NBH + (b >> 1)] = (uint8_t)(e + 101);
+        } else if constexpr (KLO == 3) {
+          // the thread's block (KE = 32) as E2M3 / 2^t, t = max(e, 1) + bits - 29: with
+          // |code| <= 2^(bits - 1), |lo| <= 2^(e + bits - 27), so |lo| / 2^t <= 4 (E2M3 tops out
+          // at 7.5 and saturates); 24 bytes at byte 32 b of the key's row
+          const int e = max((int)((kscale >> 10) & 31), 1);
+          const int t = e + KB - 29;
+          const float sc = __uint_as_float((uint32_t)(t + 127) << 23);
+          half32_t lv;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            lv[2 * i] = lo[i].x;
+            lv[2 * i + 1] = lo[i].y;
+          }
+          const uint6v_t f = __builtin_amdgcn_cvt_scalef32_pk32_fp6_f16(lv, sc);
+          uint8_t* bl = s_kl8 + buf * NK * LSTR + k_key * LSTR + k_part * kBlock;
+          *reinterpret_cast<uint4*>(bl) = make_uint4(f[0], f[1], f[2], f[3]);
+          *reinterpret_cast<uint2*>(bl + 16) = make_uint2(f[4], f[5]);
+          s_kls[buf * NK * NB + k_key * NB + (k_part & 1) * NBH + (k_part >> 1)] = (uint8_t)(t + 127);
         }
       }
       if (v_on) {
@@ -403,7 +428,7 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(ChunkArgs a) {
   // 2^t per (row, block), t = floor(log2 amax) - 7 so that |q| / 2^t < 256 (2^-126 for a zero
   // block); qs8[m] holds the E8M0 exponent of block 2 m + hl, which this lane feeds the
   // scaled MFMA
-  uint32_t qs8[KLO == 2 ? NBH : 1];
+  uint32_t qs8[KLO >= 2 ? NBH : 1];
   if constexpr (KLO == 2) {
     uint8_t* q8 = s_q8 + (wave * 32 + col) * LSTR;
 #pragma unroll
@@ -423,6 +448,48 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(ChunkArgs a) {
         *reinterpret_cast<uint2*>(q8 + 16 * (2 * b + kk) + 8 * hl) = make_uint2(fp8x4(p0, p1, sc), fp8x4(p2, p3, sc));
       }
       if ((b & 1) == hl) qs8[b >> 1] = (uint32_t)(t + 127);
+    }
+  } else if constexpr (KLO == 3) {
+    // the fp6 product takes a whole block from each lane: lane half hl converts block 2 m + hl,
+    // half of which its partner (lane ^ 32) holds; scale 2^t, t = floor(log2 amax) - 1, so
+    // |q| / 2^t < 4 (E2M3 tops out at 7.5); 24 bytes at byte 32 (2 m + hl) of the row
+    uint8_t* q6 = s_q8 + (wave * 32 + col) * LSTR;
+#pragma unroll
+    for (int mm = 0; mm < NBH; ++mm) {
+      // elements 8 hl + i (run 0) and 16 + 8 hl + i (run 1) of blocks 2 mm and 2 mm + 1 are here;
+      // send the partner those of the block it converts, receive those of ours
+      const half8_t mine0 = qv[2 * (2 * mm + hl)], mine1 = qv[2 * (2 * mm + hl) + 1];
+      const half8_t send0 = qv[2 * (2 * mm + 1 - hl)], send1 = qv[2 * (2 * mm + 1 - hl) + 1];
+      half8_t got0, got1;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t x0 = __builtin_bit_cast(uint32_t, half2_t{send0[2 * w], send0[2 * w + 1]});
+        const uint32_t x1 = __builtin_bit_cast(uint32_t, half2_t{send1[2 * w], send1[2 * w + 1]});
+        const auto r0 = __builtin_amdgcn_permlane32_swap(x0, x0, false, false);
+        const auto r1 = __builtin_amdgcn_permlane32_swap(x1, x1, false, false);
+        const half2_t g0 = __builtin_bit_cast(half2_t, hl ? r0[0] : r0[1]);
+        const half2_t g1 = __builtin_bit_cast(half2_t, hl ? r1[0] : r1[1]);
+        got0[2 * w] = g0.x; got0[2 * w + 1] = g0.y;
+        got1[2 * w] = g1.x; got1[2 * w + 1] = g1.y;
+      }
+      // the block in element order: 8-element runs r = 0..3 hold elements 8 r .. 8 r + 7
+      half32_t blk;
+      float am = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const _Float16 r0 = hl ? got0[i] : mine0[i];    // elements 0..7
+        const _Float16 r1 = hl ? mine0[i] : got0[i];    // 8..15
+        const _Float16 r2 = hl ? got1[i] : mine1[i];    // 16..23
+        const _Float16 r3 = hl ? mine1[i] : got1[i];    // 24..31
+        blk[i] = r0; blk[8 + i] = r1; blk[16 + i] = r2; blk[24 + i] = r3;
+        am = fmaxf(am, fmaxf(fmaxf(fabsf((float)r0), fabsf((float)r1)), fmaxf(fabsf((float)r2), fabsf((float)r3))));
+      }
+      const int t = max((int)((__float_as_uint(am) >> 23) & 255) - 128, -126);
+      const uint6v_t f = __builtin_amdgcn_cvt_scalef32_pk32_fp6_f16(blk, __uint_as_float((uint32_t)(t + 127) << 23));
+      uint8_t* dst = q6 + 32 * (2 * mm + hl);
+      *reinterpret_cast<uint4*>(dst) = make_uint4(f[0], f[1], f[2], f[3]);
+      *reinterpret_cast<uint2*>(dst + 16) = make_uint2(f[4], f[5]);
+      qs8[mm] = (uint32_t)(t + 127);
     }
   }
 
@@ -466,6 +533,24 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(ChunkArgs a) {
         const int8v_t av8 = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
         const int8v_t bv8 = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
         sv = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av8, bv8, sv, 0, 0, 0, (int)((asc >> (8 * mm)) & 255u), 0,
+                                                              (int)qs8[mm]);
+      }
+    } else if constexpr (KLO == 3) {
+      // m-th product at the fp6 rate: lane half hl brings all 32 elements of block 2 m + hl (24
+      // bytes) and that block's scale
+      const uint8_t* kl = bkl8 + (32 * st + col) * LSTR + 32 * hl;
+      const uint8_t* ql6 = s_q8 + (wave * 32 + col) * LSTR + 32 * hl;
+      const uint8_t* ksp = bks + (32 * st + col) * NB + hl * NBH;
+      const uint32_t asc = (uint32_t)*reinterpret_cast<const uint16_t*>(ksp);
+#pragma unroll
+      for (int mm = 0; mm < NBH; ++mm) {
+        const uint4 a0 = *reinterpret_cast<const uint4*>(kl + 64 * mm);
+        const uint2 a1 = *reinterpret_cast<const uint2*>(kl + 64 * mm + 16);
+        const uint4 b0 = *reinterpret_cast<const uint4*>(ql6 + 64 * mm);
+        const uint2 b1 = *reinterpret_cast<const uint2*>(ql6 + 64 * mm + 16);
+        const int8v_t av6 = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, 0, 0};
+        const int8v_t bv6 = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, 0, 0};
+        sv = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av6, bv6, sv, 2, 2, 0, (int)((asc >> (8 * mm)) & 255u), 0,
                                                               (int)qs8[mm]);
       }
     }
@@ -523,8 +608,8 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(ChunkArgs a) {
       const int buf = t & 1;
       const _Float16* bk = s_k + buf * KBUF;
       const _Float16* bkl = s_kl + (KLO == 1 ? buf * KBUF : 0);
-      const uint8_t* bkl8 = s_kl8 + (KLO == 2 ? buf * NK * LSTR : 0);
-      const uint8_t* bks = s_kls + (KLO == 2 ? buf * NK * NB : 0);
+      const uint8_t* bkl8 = s_kl8 + (KLO >= 2 ? buf * NK * LSTR : 0);
+      const uint8_t* bks = s_kls + (KLO >= 2 ? buf * NK * NB : 0);
       const _Float16* bv = s_vt + buf * VBUF;
       const int64_t kt0 = k_lo + (int64_t)t * NK;
       half(masked, bk, bkl, bkl8, bks, bv, kt0, 0);
