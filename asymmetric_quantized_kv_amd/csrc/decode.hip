@@ -157,7 +157,13 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   __shared__ float s_ml[4][2][GP];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int head = blockIdx.x, sl = blockIdx.y, split = blockIdx.z;
+  const int head = blockIdx.x;
+  int sl = blockIdx.y, split = blockIdx.z;
+  if (a.compact) {   // blockIdx.y enumerates the busy (split, session) pairs, split-major
+    split = 0;
+    while (split + 1 < a.n_splits && a.split0[split + 1] <= sl) ++split;
+    sl -= a.split0[split];
+  }
   const SessionRef S = a.sess[sl];
   const int64_t srow = S.row * a.hq + (int64_t)head * a.group;  // first q row
   const int64_t ts = (int64_t)split * a.tps;
@@ -806,7 +812,7 @@ constexpr int lane_elems() { return GP <= 2 ? 32 : (GP == 4 ? 16 : 8); }
 template <int KB, int VB, int D, int GP>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
   constexpr int E = lane_elems<GP>();
-  dim3 grid(a.hkv, a.n_sess, a.n_splits);
+  const dim3 grid(a.hkv, a.compact ? a.split0[a.n_splits] : a.n_sess, a.compact ? 1 : a.n_splits);
   if (KB == kF8 && a.q_dtype == 0)
     hipLaunchKernelGGL((decode_kernel<KB, VB, D, GP, E, KB == kF8>), grid, dim3(256), 0, s, a);
   else

@@ -662,9 +662,17 @@ void decode_plan(const DecodePrep& p, int* n_splits, int64_t* tps) {
   }
 }
 
+// Whether a split decode call launches only its busy workgroups (see DecodeArgs::compact):
+// then the splits past a session's end write nothing, and the merge reads each session's
+// first ceil(len / tps) splits.  The library's own calls do it when one launch holds every
+// session; kv_attend_decode_partial always writes every split.
+bool decode_compact(int n_sessions, int n_splits) {
+  return n_splits > 1 && n_splits <= kMaxCompactSplits && n_sessions <= kMaxSessions;
+}
+
 int decode_launch(kv_cache* const* sessions, int n_sessions, int layer, const DecodePrep& p, const void* q,
                   int q_dtype, int n_q_heads, float sm_scale, int n_splits, int64_t tps, bool partial, float* ws,
-                  float* out, hipStream_t st) {
+                  float* out, hipStream_t st, bool compact = false) {
   DecodeArgs a;
   memset(&a, 0, sizeof(a));
   a.hkv = p.hkv;
@@ -694,6 +702,15 @@ int decode_launch(kv_cache* const* sessions, int n_sessions, int layer, const De
       a.sess[i].len = c->len[layer];
       a.sess[i].row = r;
     }
+    a.compact = compact ? 1 : 0;
+    if (compact) {   // sessions are listed longest first, so split j's busy sessions are a prefix
+      a.split0[0] = 0;
+      for (int j = 0; j < n_splits; ++j) {
+        int cnt = 0;
+        while (cnt < nb && ceil_div(std::max<int64_t>(a.sess[cnt].len, 1), tps) > j) ++cnt;
+        a.split0[j + 1] = a.split0[j] + cnt;
+      }
+    }
     hipError_t e = launch_decode(a, p.kbits, p.vbits, p.d, p.gp, st);
     if (e != hipSuccess) {
       for (int i = 0; i < n_sessions; ++i) sessions[i]->poisoned = true;
@@ -703,13 +720,20 @@ int decode_launch(kv_cache* const* sessions, int n_sessions, int layer, const De
   return KV_OK;
 }
 
-hipError_t merge_launch(const float* ws, int64_t rows, int n_splits, int d, float* out, hipStream_t st) {
+// n_valid (optional): per session of rows_per_sess rows, how many of its splits hold partials
+hipError_t merge_launch(const float* ws, int64_t rows, int n_splits, int d, float* out, hipStream_t st,
+                        int rows_per_sess = 0, const int32_t* n_valid = nullptr) {
   MergeArgs m;
+  memset(&m, 0, sizeof(m));
   m.ws = ws;
   m.out = out;
   m.rows = rows;
   m.n_splits = n_splits;
   m.d = d;
+  if (rows_per_sess > 0 && n_valid) {
+    m.rows_per_sess = rows_per_sess;
+    for (int64_t i = 0; i < rows / rows_per_sess && i < kMaxSessions; ++i) m.n_valid[i] = n_valid[i];
+  }
   return launch_merge(m, st);
 }
 
@@ -877,11 +901,16 @@ int kv_attend_decode(kv_cache* const* sessions, int n_sessions, int layer, const
   if ((rc = check_workspace(workspace, ws_bytes, need))) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
   float* ws = static_cast<float*>(workspace);
+  const bool compact = decode_compact(n_sessions, n_splits);
   if ((rc = decode_launch(sessions, n_sessions, layer, p, q, q_dtype, n_q_heads, sm_scale, n_splits, tps,
-                          n_splits > 1, ws, out, st)))
+                          n_splits > 1, ws, out, st, compact)))
     return rc;
   if (n_splits > 1) {
-    hipError_t e = merge_launch(ws, (int64_t)n_sessions * n_q_heads, n_splits, p.d, out, st);
+    int32_t n_valid[kMaxSessions];
+    if (compact)
+      for (int i = 0; i < n_sessions; ++i) n_valid[i] = (int32_t)ceil_div(std::max<int64_t>(p.lens[i], 1), tps);
+    hipError_t e = merge_launch(ws, (int64_t)n_sessions * n_q_heads, n_splits, p.d, out, st,
+                                compact ? n_q_heads : 0, compact ? n_valid : nullptr);
     if (e != hipSuccess) {
       for (int i = 0; i < n_sessions; ++i) sessions[i]->poisoned = true;
       return fail(KV_EHIP, "merge launch: %s", hipGetErrorString(e));

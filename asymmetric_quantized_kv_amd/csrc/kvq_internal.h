@@ -9,6 +9,7 @@ namespace kvq {
 constexpr int kBlock = 32;          // elements per quantization block
 constexpr int kGranule = 256;       // capacity granule (tokens)
 constexpr int kMaxSessions = 64;    // sessions per decode launch (kernel-argument table)
+constexpr int kMaxCompactSplits = 256;  // splits of a decode launch that lists only busy workgroups
 constexpr int kDecodeChunk = 128;   // tokens one wave scores before its softmax update
 constexpr int kDecodeWaveTokens = 4 * kDecodeChunk;  // split granularity of decode
 constexpr int kChunkThreads = 768;  // threads per chunk-prefill workgroup: 8 consumer + 4 producer waves
@@ -57,6 +58,11 @@ struct DecodeArgs {
   int n_sess;             // sessions in this launch
   int hkv, hq, group;
   int n_splits;
+  // compact != 0: the grid holds only the workgroups with tokens, split-major: split j has
+  // the first split0[j + 1] - split0[j] sessions (those longer than j * tps, listed longest
+  // first); a split past a session's end then has no workgroup and no partial
+  int compact;
+  int32_t split0[kMaxCompactSplits + 1];
   int partial;            // 1: write (o, m, l) partials to ws; 0: normalized out (n_splits == 1)
   int64_t tps;            // tokens per split, multiple of kDecodeWaveTokens
   const void* q;
@@ -88,6 +94,10 @@ struct MergeArgs {
   int64_t rows;
   int n_splits;
   int d;
+  // rows_per_sess > 0: row r belongs to session r / rows_per_sess, whose partials are its first
+  // n_valid[session] splits only (the others were never written)
+  int rows_per_sess;
+  int32_t n_valid[kMaxSessions];
 };
 
 // Launchers (one per translation unit).  They return hipErrorInvalidValue for a

@@ -4,7 +4,8 @@
 // One wave per output row.  Lane s loads split s's (m, l), so the statistics of up to 64
 // splits take one round trip; the weights w_s = 2^(m_s - M) / L then go to every lane
 // through readlane, and each lane sums the splits for its elements of head_dim.  Splits
-// that saw no token carry m = -inf, l = 0 and weigh nothing.
+// that saw no token carry m = -inf, l = 0 and weigh nothing; a decode batch launched with
+// its busy workgroups only names, per session, how many leading splits to read.
 #include "kvq_internal.h"
 #include "wave_ops.h"
 
@@ -17,17 +18,18 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   if (row >= a.rows) return;   // wave-uniform
   const int stride = a.d + 2;
   const float* p = a.ws + row * a.n_splits * stride;
+  const int ns = a.rows_per_sess > 0 ? a.n_valid[row / a.rows_per_sess] : a.n_splits;   // splits to read
   // statistics, 64 splits at a time
   float M = -INFINITY;
-  for (int s0 = 0; s0 < a.n_splits; s0 += 64) {
-    const float ms = s0 + lane < a.n_splits ? p[(s0 + lane) * stride + a.d] : -INFINITY;
+  for (int s0 = 0; s0 < ns; s0 += 64) {
+    const float ms = s0 + lane < ns ? p[(s0 + lane) * stride + a.d] : -INFINITY;
     M = fmaxf(M, wave_max(ms));
   }
   float L = 0.f;
-  for (int s0 = 0; s0 < a.n_splits; s0 += 64) {
+  for (int s0 = 0; s0 < ns; s0 += 64) {
     const int s = s0 + lane;
     float w = 0.f;
-    if (s < a.n_splits) {
+    if (s < ns) {
       const float ms = p[s * stride + a.d];
       if (ms != -INFINITY) w = __builtin_amdgcn_exp2f(ms - M) * p[s * stride + a.d + 1];
     }
@@ -38,14 +40,14 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
     const int e = e0 + lane;
     const bool on = e < a.d;
     float o = 0.f;
-    for (int s0 = 0; s0 < a.n_splits; s0 += 64) {
+    for (int s0 = 0; s0 < ns; s0 += 64) {
       const int s = s0 + lane;
       float w = 0.f;   // this lane's split weight, handed to every lane below
-      if (s < a.n_splits) {
+      if (s < ns) {
         const float ms = p[s * stride + a.d];
         if (ms != -INFINITY) w = __builtin_amdgcn_exp2f(ms - M) * inv;
       }
-      const int n = min(64, a.n_splits - s0);
+      const int n = min(64, ns - s0);
       // four splits' loads are issued before their products are summed
       for (int j = 0; j < n; j += 4) {
         float x[4];

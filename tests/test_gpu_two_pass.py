@@ -199,8 +199,10 @@ def test_partial_entry_points_reject_bad_splits():
 
 def test_ragged_batch_spreads_the_long_session():
     """Lengths that differ by four orders of magnitude: the plan cuts the long session into
-    many splits (the short ones keep one busy split each, the rest exit empty), and the
-    result still matches the oracle, pass by pass."""
+    many splits (the short ones keep one busy split each), and the result still matches the
+    oracle, pass by pass.  The one-call path launches only the busy splits and its merge
+    reads no other partial: a workspace full of NaN gives the same output.  The partial
+    pass writes every split, the empty ones as (-inf, 0, 0)."""
     log("ragged batch plan")
     torch = torch_mod()
     lens = [20000, 300, 50, 4096, 1, 700]
@@ -225,6 +227,11 @@ def test_ragged_batch_spreads_the_long_session():
         want = O.attend_decode(ocs, 0, q, scale)
         err = max_err(kvq.kv_attend_decode(sessions, 0, qd, scale), want)
         log(f"  one call err {err:.3e}")
+        assert err <= TOL
+        nb = kvq.kv_decode_workspace_bytes(sessions, 0, hq)
+        ws = torch.full((nb,), 0xFF, dtype=torch.uint8, device=qd.device)   # every float NaN
+        err = max_err(kvq.kv_attend_decode(sessions, 0, qd, scale, workspace=ws), want)
+        log(f"  one call over a NaN-filled workspace err {err:.3e}")
         assert err <= TOL
         p = kvq.kv_attend_decode_partial(sessions, 0, qd, scale, n_splits, per)
         o, m, l = O.decode_partials(ocs, 0, q, scale, n_splits, per)
