@@ -159,12 +159,20 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int head = blockIdx.x;
   int sl = blockIdx.y, split = blockIdx.z;
-  if (a.compact) {   // blockIdx.y enumerates the busy (split, session) pairs, split-major
-    split = 0;
-    while (split + 1 < a.n_splits && a.split0[split + 1] <= sl) ++split;
-    sl -= a.split0[split];
+  // the full grid's session, read before the launch kind is known (no wait on a.compact
+  // first: the empty asm keeps the compiler from sinking these loads past the branch)
+  SessionRef S = a.sess[min(sl, kMaxSessions - 1)];
+  asm volatile("" : "+s"(S.base), "+s"(S.cap), "+s"(S.len));
+  if (a.compact) {   // blockIdx.y enumerates the busy (session, split) pairs: the last session
+    int lo = 0, hi = a.n_sess - 1;   // whose first piece is at or before it
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (a.sess[mid].piece0 <= sl) lo = mid; else hi = mid - 1;
+    }
+    split = sl - a.sess[lo].piece0;
+    sl = lo;
+    S = a.sess[sl];
   }
-  const SessionRef S = a.sess[sl];
   const int64_t srow = S.row * a.hq + (int64_t)head * a.group;  // first q row
   const int64_t ts = (int64_t)split * a.tps;
   const int64_t te = min(ts + a.tps, S.len);
@@ -812,7 +820,7 @@ constexpr int lane_elems() { return GP <= 2 ? 32 : (GP == 4 ? 16 : 8); }
 template <int KB, int VB, int D, int GP>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
   constexpr int E = lane_elems<GP>();
-  const dim3 grid(a.hkv, a.compact ? a.split0[a.n_splits] : a.n_sess, a.compact ? 1 : a.n_splits);
+  const dim3 grid(a.hkv, a.compact ? a.n_pieces : a.n_sess, a.compact ? 1 : a.n_splits);
   if (KB == kF8 && a.q_dtype == 0)
     hipLaunchKernelGGL((decode_kernel<KB, VB, D, GP, E, KB == kF8>), grid, dim3(256), 0, s, a);
   else

@@ -664,10 +664,19 @@ void decode_plan(const DecodePrep& p, int* n_splits, int64_t* tps) {
 
 // Whether a split decode call launches only its busy workgroups (see DecodeArgs::compact):
 // then the splits past a session's end write nothing, and the merge reads each session's
-// first ceil(len / tps) splits.  The library's own calls do it when one launch holds every
-// session; kv_attend_decode_partial always writes every split.
-bool decode_compact(int n_sessions, int n_splits) {
-  return n_splits > 1 && n_splits <= kMaxCompactSplits && n_sessions <= kMaxSessions;
+// first n_valid = ceil(len / tps) splits.  The library's own calls do it when one launch
+// holds every session and some session is shorter than the split range (otherwise there is
+// no empty workgroup to drop, and the workgroups' split lookup would only add latency);
+// kv_attend_decode_partial always writes every split.
+bool decode_compact(int n_sessions, int n_splits, const int32_t* n_valid) {
+  if (n_splits <= 1 || n_sessions > kMaxSessions) return false;
+  int64_t pieces = 0;   // the grid's second dimension
+  bool empty = false;
+  for (int i = 0; i < n_sessions; ++i) {
+    pieces += n_valid[i];
+    empty |= n_valid[i] < n_splits;
+  }
+  return empty && pieces <= 65535;
 }
 
 int decode_launch(kv_cache* const* sessions, int n_sessions, int layer, const DecodePrep& p, const void* q,
@@ -700,16 +709,13 @@ int decode_launch(kv_cache* const* sessions, int n_sessions, int layer, const De
       a.sess[i].base = layer_base(c, layer);
       a.sess[i].cap = c->lg[layer].g.cap;
       a.sess[i].len = c->len[layer];
-      a.sess[i].row = r;
+      a.sess[i].row = (int32_t)r;
     }
     a.compact = compact ? 1 : 0;
-    if (compact) {   // sessions are listed longest first, so split j's busy sessions are a prefix
-      a.split0[0] = 0;
-      for (int j = 0; j < n_splits; ++j) {
-        int cnt = 0;
-        while (cnt < nb && ceil_div(std::max<int64_t>(a.sess[cnt].len, 1), tps) > j) ++cnt;
-        a.split0[j + 1] = a.split0[j] + cnt;
-      }
+    a.n_pieces = 0;
+    for (int i = 0; i < nb; ++i) {   // each session's busy splits, one after the other
+      a.sess[i].piece0 = a.n_pieces;
+      a.n_pieces += (int32_t)ceil_div(std::max<int64_t>(a.sess[i].len, 1), tps);
     }
     hipError_t e = launch_decode(a, p.kbits, p.vbits, p.d, p.gp, st);
     if (e != hipSuccess) {
@@ -901,14 +907,13 @@ int kv_attend_decode(kv_cache* const* sessions, int n_sessions, int layer, const
   if ((rc = check_workspace(workspace, ws_bytes, need))) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
   float* ws = static_cast<float*>(workspace);
-  const bool compact = decode_compact(n_sessions, n_splits);
+  int32_t n_valid[kMaxSessions];
+  for (int i = 0; i < n_sessions && i < kMaxSessions; ++i) n_valid[i] = (int32_t)ceil_div(std::max<int64_t>(p.lens[i], 1), tps);
+  const bool compact = decode_compact(n_sessions, n_splits, n_valid);
   if ((rc = decode_launch(sessions, n_sessions, layer, p, q, q_dtype, n_q_heads, sm_scale, n_splits, tps,
                           n_splits > 1, ws, out, st, compact)))
     return rc;
   if (n_splits > 1) {
-    int32_t n_valid[kMaxSessions];
-    if (compact)
-      for (int i = 0; i < n_sessions; ++i) n_valid[i] = (int32_t)ceil_div(std::max<int64_t>(p.lens[i], 1), tps);
     hipError_t e = merge_launch(ws, (int64_t)n_sessions * n_q_heads, n_splits, p.d, out, st,
                                 compact ? n_q_heads : 0, compact ? n_valid : nullptr);
     if (e != hipSuccess) {

@@ -9,7 +9,6 @@ namespace kvq {
 constexpr int kBlock = 32;          // elements per quantization block
 constexpr int kGranule = 256;       // capacity granule (tokens)
 constexpr int kMaxSessions = 64;    // sessions per decode launch (kernel-argument table)
-constexpr int kMaxCompactSplits = 256;  // splits of a decode launch that lists only busy workgroups
 constexpr int kDecodeChunk = 128;   // tokens one wave scores before its softmax update
 constexpr int kDecodeWaveTokens = 4 * kDecodeChunk;  // split granularity of decode
 constexpr int kChunkThreads = 768;  // threads per chunk-prefill workgroup: 8 consumer + 4 producer waves
@@ -50,26 +49,27 @@ struct SessionRef {
   const uint8_t* base;    // arena + layer * Hkv * region of this session
   int64_t cap;
   int64_t len;
-  int64_t row;            // index of the session in the call (rows of q / out / workspace)
+  int32_t row;            // index of the session in the call (rows of q / out / workspace)
+  int32_t piece0;         // compact launches: index of its first busy split among all sessions
 };
 
 struct DecodeArgs {
-  SessionRef sess[kMaxSessions];
+  // the scalars first: a workgroup's first kernel-argument loads then share one cache line
   int n_sess;             // sessions in this launch
   int hkv, hq, group;
   int n_splits;
-  // compact != 0: the grid holds only the workgroups with tokens, split-major: split j has
-  // the first split0[j + 1] - split0[j] sessions (those longer than j * tps, listed longest
-  // first); a split past a session's end then has no workgroup and no partial
-  int compact;
-  int32_t split0[kMaxCompactSplits + 1];
   int partial;            // 1: write (o, m, l) partials to ws; 0: normalized out (n_splits == 1)
+  // compact != 0: the grid holds only the workgroups with tokens, session by session: session
+  // i's busy splits are pieces sess[i].piece0 .. + ceil(len / tps) - 1 of n_pieces; a split
+  // past a session's end then has no workgroup and no partial
+  int compact, n_pieces;
+  int q_dtype;
   int64_t tps;            // tokens per split, multiple of kDecodeWaveTokens
   const void* q;
-  int q_dtype;
   float qk_scale;         // sm_scale * log2(e)
   float* ws;              // [S][Hq][n_splits][D + 2] partials when partial
   float* out;             // [S][Hq][D] otherwise
+  SessionRef sess[kMaxSessions];
 };
 
 struct ChunkArgs {
