@@ -82,6 +82,12 @@ def outlier_channels(n_kv_heads: int, head_dim: int, n_out: int, *key) -> np.nda
     return mask
 
 
+def log10_uniform(shape, lo: float, hi: float, *key) -> np.ndarray:
+    """float32 10^u with u uniform in [lo, hi), from the stream named by ``key``."""
+    u = _rng(*key, 0x10C).uniform(lo, hi, size=tuple(int(s) for s in shape))
+    return np.power(10.0, u).astype(np.float32)
+
+
 def workload_small(seed: int, n_tokens: int, n_kv_heads: int, head_dim: int,
                    n_q_heads: int, n_q_rows: int, bf16: bool = False,
                    n_outliers: int = 0, outlier_factor: float = 8.0):

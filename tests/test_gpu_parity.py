@@ -250,6 +250,33 @@ def test_chunk_matches_oracle(case):
         assert err <= TOL
 
 
+@pytest.mark.parametrize("layout,d,dtype", [("K8V4", 128, "bf16"), ("K4V4", 128, "f16"), ("K8V8", 64, "bf16"),
+                                            ("K4V8", 128, "f32")])
+def test_chunk_keys_spanning_five_decades(layout, d, dtype):
+    """Key rows scaled by 10^u, u uniform in [-4, 1) per (token, KV head): the fp16 scales of
+    the key blocks take exponents over most of fp16's range, and the low part of every block
+    (fp6 at head_dim 128 with 16-bit queries, fp8 otherwise) is scaled from its own."""
+    log(f"chunk wide key range {layout} D{d} {dtype}")
+    hkv, g, n_ctx, n_new = 2, 4, 1200, 130
+    hq = hkv * g
+    n = n_ctx + n_new
+    k, v, q = I.workload_small(960 + d, n, hkv, d, hq, n_new, n_outliers=4)
+    k = k * I.log10_uniform((n, hkv, 1), -4.0, 1.0, 961 + d)
+    if dtype == "bf16":
+        k, v, q = I.bf16_round(k), I.bf16_round(v), I.bf16_round(q)
+    oc = O.OracleCache(O.LAYOUT_IDS[layout], 1, hkv, d, n)
+    with gpu_cache(layout, 1, hkv, d, n) as h:
+        kvq.kv_append_quant(h, 0, dev(k, dtype), dev(v, dtype))
+        oc.append(0, host_inputs(k, dtype), host_inputs(v, dtype))
+        assert_planes_equal(h, oc, 0)
+        scale = d ** -0.5
+        out = kvq.kv_attend_chunk(h, 0, dev(q, dtype), n_new, scale)
+        want = O.attend_chunk(oc, 0, host_inputs(q, dtype), n_new, scale)
+        err = max_err(out, want)
+        log(f"  max err {err:.3e}")
+        assert err <= TOL
+
+
 # ---------------------------------------------------------------------------
 # determinism and device-side error paths
 # ---------------------------------------------------------------------------
