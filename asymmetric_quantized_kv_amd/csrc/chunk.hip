@@ -11,11 +11,12 @@
 // value with a 2^-9 relative error), while fp16 keeps 11 bits at the same MFMA rate.
 // A quantized key (code * scale: up to 18 significant bits) is carried as its fp16 rounding
 // hi plus the rest lo = code * scale - hi, which fp16 holds exactly.  hi meets the query on
-// the fp16 MFMA.  lo, at most 2^-11 of the key, goes to LDS as fp8 (E4M3) with a power-of-two
-// scale per 32-element block and meets an fp8 copy of the query (also block-scaled) on the
-// block-scaled fp8 MFMA (v_mfma_scale_f32_32x32x64_f8f6f4) at twice the fp16 rate: keys then
-// carry about 2^-15 relative error instead of fp16's 2^-12.  fp32 queries are carried as
-// fp16 hi + lo.
+// the fp16 MFMA.  lo, at most 2^-11 of the key, goes to LDS in fp6 (E2M3; head_dim 128 with
+// 16-bit queries) or fp8 (E4M3) with a power-of-two scale per 32-element block, and meets a
+// copy of the query in the same format (also block-scaled) on the block-scaled MFMA
+// (v_mfma_scale_f32_32x32x64_f8f6f4) at four (fp6) or two (fp8) times the fp16 rate: its
+// rounding stays 2^-17 (fp6) or 2^-20 (fp8) below the block's largest key, against fp16's
+// 2^-12 of every key.  fp32 queries are carried as fp16 hi + lo.
 // fp8 (E4M3) keys with power-of-two block scales widen to fp16 exactly in one conversion
 // (v_cvt_scalef32_pk_f16_fp8), so they need no low part: one MFMA per k-step.
 //
@@ -34,10 +35,11 @@
 #include <type_traits>
 
 // The low part of 8/4-bit keys: 3 = fp6 (E2M3) with block scales on the block-scaled MFMA
-// at the fp6 rate (the built form for head_dim 128 and 16-bit queries; the others take 2); 2 = fp8 (E4M3)
-// likewise at the fp8 rate; 1 = exact fp16 on the fp16 MFMA (one more fp16 MFMA per k-step);
-// 0 = none: keys then carry fp16 rounding (2^-12 relative), which measured up to 4.9e-3 of
-// attention error against the 5e-3 tolerance, so 0 is kept only to reproduce that measurement.
+// at the fp6 rate (the built form for head_dim 128 and 16-bit queries; the others take 2);
+// 2 = fp8 (E4M3) likewise at the fp8 rate; 1 = exact fp16 on the fp16 MFMA (one more fp16
+// MFMA per k-step); 0 = none: keys then carry fp16 rounding (2^-12 relative), which measured
+// up to 4.9e-3 of attention error against the 5e-3 tolerance, so 0 is kept only to
+// reproduce that measurement.
 #ifndef KVQ_CHUNK_KLO
 #define KVQ_CHUNK_KLO 3
 #endif
