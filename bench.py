@@ -17,6 +17,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -54,9 +55,14 @@ def log(msg):
 
 
 def kernel_source_sha() -> str:
+    """Hash of the device sources with comments and blank space removed, so that a
+    comment edit does not count as a kernel change."""
     h = hashlib.sha256()
     for f in ("decode.hip", "chunk.hip", "append.hip", "merge.hip", "kvq_internal.h", "wave_ops.h"):
-        h.update((ROOT / "asymmetric_quantized_kv_amd" / "csrc" / f).read_bytes())
+        text = (ROOT / "asymmetric_quantized_kv_amd" / "csrc" / f).read_text()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
