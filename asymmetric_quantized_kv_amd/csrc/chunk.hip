@@ -31,6 +31,7 @@
 // (probabilities up to 256 stay exact in fp16), which makes the rescale of the
 // accumulators rare.
 #include "kvq_internal.h"
+#include "buffer_ops.h"
 
 #include <type_traits>
 
@@ -93,22 +94,6 @@ __device__ __forceinline__ uint32_t fp8x4(half2_t a, half2_t b, float scale) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
-template <int W>
-__device__ __forceinline__ void load_dw(const uint8_t* p, uint32_t* o) {
-  if constexpr (W % 4 == 0) {
-#pragma unroll
-    for (int i = 0; i < W / 4; ++i) {
-      const uint4 t = reinterpret_cast<const uint4*>(p)[i];
-      o[4 * i] = t.x; o[4 * i + 1] = t.y; o[4 * i + 2] = t.z; o[4 * i + 3] = t.w;
-    }
-  } else if constexpr (W == 2) {
-    const uint2 t = *reinterpret_cast<const uint2*>(p);
-    o[0] = t.x; o[1] = t.y;
-  } else {
-    o[0] = *reinterpret_cast<const uint32_t*>(p);
-  }
-}
-
 // fp16 magic numbers: 0x64xx reads as 1024 + xx when xx < 4 bits of exponent room, so
 // a code placed in the low mantissa bits comes back exactly after one packed subtract.
 constexpr uint32_t kMagic = 0x64646464u;
@@ -119,6 +104,14 @@ __device__ __forceinline__ void k8_pairs(uint32_t w, half2_t (&c)[2]) {
   const uint32_t x = w ^ 0x80808080u;                                            // c + 128
   c[0] = h2(__builtin_amdgcn_perm(kMagic, x, 0x04010400u)) - hconst(1152.f);
   c[1] = h2(__builtin_amdgcn_perm(kMagic, x, 0x04030402u)) - hconst(1152.f);
+}
+
+// (x & mask) | bits in one v_and_or_b32 (its VOP3 form takes no literal operand, so the
+// compiler would emit an and and an or); bits comes in a register
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t bits) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(mask), "v"(bits));
+  return r;
 }
 
 // the 8 codes of one dword of 4-bit keys as fp16 pairs (e2j, e2j+1), j = 0..3
@@ -211,21 +204,25 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(ChunkArgs a) {
     uint16_t kscale = 0;
     uint32_t vraw[4][VW];
     uint16_t vscale[4] = {0, 0, 0, 0};
+    // the tile's rows of each plane through a buffer resource based at the tile (64-bit
+    // tile offsets in scalar registers, per-thread 32-bit offsets fixed)
     auto fetch = [&](int t) {
       const int64_t kt0 = k_lo + (int64_t)t * NK;
-      load_dw<KW>(kc + kt0 * a.g.kc + k_off, kraw);
-      if constexpr (KB == kF8) kscale = ks[kt0 * a.g.ks + ks_off];
-      else if constexpr (KB != 16) kscale = *reinterpret_cast<const uint16_t*>(ks + kt0 * a.g.ks + ks_off);
+      buf_dwords<KW>(make_rsrc(kc + kt0 * a.g.kc, NK * a.g.kc), k_off, 0, kraw);
+      if constexpr (KB == kF8) kscale = buf_u8(make_rsrc(ks + kt0 * a.g.ks, NK * a.g.ks), ks_off, 0);
+      else if constexpr (KB != 16) kscale = buf_u16(make_rsrc(ks + kt0 * a.g.ks, NK * a.g.ks), ks_off, 0);
       if (v_on) {
-        const uint8_t* vt = vc + kt0 * a.g.vc;
-        const uint8_t* vst = vs + kt0 * a.g.vs;
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(vc + kt0 * a.g.vc, NK * a.g.vc);
+        const __amdgpu_buffer_rsrc_t rvs = make_rsrc(vs + kt0 * a.g.vs, NK * a.g.vs);
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-          load_dw<VW>(vt + kk * a.g.vc + v_off, vraw[kk]);
-          if constexpr (VB != 16) vscale[kk] = *reinterpret_cast<const uint16_t*>(vst + kk * a.g.vs + vs_off);
+          buf_dwords<VW>(rv, v_off, kk * a.g.vc, vraw[kk]);
+          if constexpr (VB != 16) vscale[kk] = buf_u16(rvs, vs_off, kk * a.g.vs);
         }
       }
     };
+    uint32_t bias;   // kHalfBias1024 in a register for and_or, set once
+    asm volatile("v_mov_b32 %0, %1" : "=v"(bias) : "i"(kHalfBias1024));
     auto produce = [&](int buf) {
       _Float16* bk = s_k + buf * KBUF;
       _Float16* bkl = s_kl + (KLO == 1 ? buf * KBUF : 0);
@@ -328,8 +325,10 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(ChunkArgs a) {
             for (int j = 0; j < 4; ++j) {
               const uint32_t sel = (uint32_t)j | ((uint32_t)(4 + j) << 16) | 0x0c000c00u;  // [a.bj, 0, b.bj, 0]
               const uint32_t q = __builtin_amdgcn_perm(wb[0], wa[0], sel);
-              const half2_t ce = h2((q & 0x000F000Fu) | kHalfBias1024) - hconst(1032.f);
-              const half2_t co = h2(((q >> 4) & 0x000F000Fu) | kHalfBias1024) - hconst(1032.f);
+              const half2_t ce = h2(and_or(q, 0x000F000Fu, bias)) - hconst(1032.f);
+              // high nibbles: 1024 + 16 u, so u - 8 = x / 16 - 72 (exact)
+              const half2_t co = __builtin_elementwise_fma(h2(and_or(q, 0x00F000F0u, bias)), hconst(0.0625f),
+                                                           hconst(-72.f));
               pr[2 * j][p] = u32(ce * d2);
               pr[2 * j + 1][p] = u32(co * d2);
             }

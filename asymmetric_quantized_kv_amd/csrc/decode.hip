@@ -32,6 +32,7 @@
 // The epilogue reduces the wave's partials, merges the four waves through LDS, and
 // writes either the normalized output (one split) or (o, m, l) for the merge kernel.
 #include "kvq_internal.h"
+#include "buffer_ops.h"
 #include "wave_ops.h"
 
 #ifndef KVQ_DECODE_DEPTH
@@ -55,43 +56,10 @@ __device__ __forceinline__ half2_t pack_rne(float a, float b) {
   return r;
 }
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-// Buffer resource over `bytes` bytes at p (raw, byte-addressed); loads through it take a
-// per-lane 32-bit offset and a wave-uniform offset, so addresses cost no vector ALU.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint8_t* p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p), 0, (int)bytes, 0x00020000);
-}
-
-template <int W>
-__device__ __forceinline__ void buf_dwords(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint32_t (&o)[W]) {
-  if constexpr (W % 4 == 0) {
-#pragma unroll
-    for (int i = 0; i < W / 4; ++i) {
-      const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(r, (int)(voff + 16 * i), (int)soff, 0);
-      o[4 * i] = t.x; o[4 * i + 1] = t.y; o[4 * i + 2] = t.z; o[4 * i + 3] = t.w;
-    }
-  } else if constexpr (W == 2) {
-    const u32x2 t = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0);
-    o[0] = t.x; o[1] = t.y;
-  } else {
-    static_assert(W == 1, "dword count");
-    o[0] = __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
-  }
-}
-
-__device__ __forceinline__ uint16_t buf_u16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, (int)soff, 0);
-}
-
-__device__ __forceinline__ uint16_t buf_u8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_amdgcn_raw_buffer_load_b8(r, (int)voff, (int)soff, 0);
-}
 
 // a . b over four signed bytes, starting a new sum (the VOP3 form takes the zero as an
 // inline constant; the accumulating two-operand form would need a register cleared first)
