@@ -697,11 +697,13 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
             const uint32_t sel = (uint32_t)k | (0x0cu << 8) | ((uint32_t)(4 + k) << 16) | (0x0cu << 24);
+            // the whole byte (even nibble + 16 x odd nibble) and the odd nibble alone; the
+            // epilogue takes the even sum as their difference (no mask for the even nibble)
             const uint32_t pr = __builtin_amdgcn_perm(vb[j], va[j], sel);
-            const half2_t ev = as_h2(pr & 0x000F000Fu), od = as_h2(pr & 0x00F000F0u);
+            const half2_t by = as_h2(pr), od = as_h2(pr & 0x00F000F0u);
 #pragma unroll
             for (int g = 0; g < GP; ++g) {
-              acc[g][8 * j + 2 * k] = __builtin_amdgcn_fdot2(w[g], ev, acc[g][8 * j + 2 * k], false);
+              acc[g][8 * j + 2 * k] = __builtin_amdgcn_fdot2(w[g], by, acc[g][8 * j + 2 * k], false);
               acc[g][8 * j + 2 * k + 1] = __builtin_amdgcn_fdot2(w[g], od, acc[g][8 * j + 2 * k + 1], false);
             }
           }
@@ -738,7 +740,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       float o;
-      if constexpr (VB == 4) o = acc[g][e] * ((e & 1) ? 1048576.f : 16777216.f) - 8.f * wsum[g];
+      if constexpr (VB == 4)
+        o = ((e & 1) ? acc[g][e] * 1048576.f : (acc[g][e] - acc[g][e + 1]) * 16777216.f) - 8.f * wsum[g];
       else if constexpr (VB == 8) o = acc[g][e] * 16777216.f - 128.f * wsum[g];
       else o = acc[g][e];
       o = strided_sum<LPT>(o);
