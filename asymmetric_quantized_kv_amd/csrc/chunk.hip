@@ -114,14 +114,15 @@ __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t b
   return r;
 }
 
-// the 8 codes of one dword of 4-bit keys as fp16 pairs (e2j, e2j+1), j = 0..3
-__device__ __forceinline__ void k4_pairs(uint32_t w, half2_t (&c)[4]) {
+// the 8 codes of one dword of 4-bit keys as fp16 pairs (e2j, e2j+1), j = 0..3; bias holds
+// kHalfBias1024
+__device__ __forceinline__ void k4_pairs(uint32_t w, uint32_t bias, half2_t (&c)[4]) {
   const uint32_t w4 = w >> 4;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const uint32_t sel = (uint32_t)j | ((uint32_t)(4 + j) << 16) | 0x0c000c00u;  // [w.bj, 0, w4.bj, 0]
     const uint32_t p = __builtin_amdgcn_perm(w4, w, sel);
-    c[j] = h2((p & 0x000F000Fu) | kHalfBias1024) - hconst(1032.f);
+    c[j] = h2(and_or(p, 0x000F000Fu, bias)) - hconst(1032.f);
   }
 }
 
@@ -255,7 +256,7 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(ChunkArgs a) {
               }
             } else {
               half2_t c[4];
-              k4_pairs(kraw[w], c);
+              k4_pairs(kraw[w], bias, c);
 #pragma unroll
               for (int j = 0; j < 4; ++j) {
                 hi[4 * w + j] = c[j] * d2;
