@@ -41,11 +41,11 @@ def compile_flags() -> list[str]:
     ]
 
 
-def _compile(src: str, defines=(), build_dir: Path = BUILD) -> Path:
-    build_dir.mkdir(parents=True, exist_ok=True)
-    obj = build_dir / (src + ".o")
+def _compile(src: str) -> Path:
+    BUILD.mkdir(parents=True, exist_ok=True)
+    obj = BUILD / (src + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [hipcc(), *compile_flags(), *[f"-D{d}" for d in defines], *lang, "-c", str(CSRC / src), "-o", str(obj)]
+    cmd = [hipcc(), *compile_flags(), *lang, "-c", str(CSRC / src), "-o", str(obj)]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
@@ -56,29 +56,24 @@ def _compile(src: str, defines=(), build_dir: Path = BUILD) -> Path:
     return obj
 
 
-def build(jobs: int | None = None, verbose: bool = True, defines=(), out: Path | None = None) -> Path:
-    """Compile and link.  ``defines`` (NAME=VALUE) and ``out`` build a variant library
-    elsewhere (objects go to a build folder of its own); the default is the in-tree one."""
-    out = Path(out) if out else LIB
-    build_dir = BUILD if out == LIB else BUILD / ("variant_" + out.stem)
+def build(jobs: int | None = None, verbose: bool = True) -> Path:
+    """Compile every source and link the in-tree library."""
     jobs = jobs or min(len(SOURCES), os.cpu_count() or 1)
     with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, defines, build_dir), SOURCES))
-    tmp = out.with_suffix(".so.tmp")
+        objs = list(ex.map(_compile, SOURCES))
+    tmp = LIB.with_suffix(".so.tmp")
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *map(str, objs), "-o", str(tmp)]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, out)
+    os.replace(tmp, LIB)
     if verbose:
-        print(f"built {out}")
-    return out
+        print(f"built {LIB}")
+    return LIB
 
 
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=None)
-    ap.add_argument("--define", action="append", default=[], help="NAME=VALUE passed to hipcc")
-    ap.add_argument("--out", default=None, help="library path (default: the in-tree libkvq.so)")
     a = ap.parse_args()
-    build(a.jobs, defines=a.define, out=a.out)
+    build(a.jobs)

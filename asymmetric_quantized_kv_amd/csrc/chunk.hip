@@ -35,16 +35,6 @@
 
 #include <type_traits>
 
-// The low part of 8/4-bit keys: 3 = fp6 (E2M3) with block scales on the block-scaled MFMA
-// at the fp6 rate (the built form for head_dim 128 and 16-bit queries; the others take 2);
-// 2 = fp8 (E4M3) likewise at the fp8 rate; 1 = exact fp16 on the fp16 MFMA (one more fp16
-// MFMA per k-step); 0 = none: keys then carry fp16 rounding (2^-12 relative), which measured
-// up to 4.9e-3 of attention error against the 5e-3 tolerance, so 0 is kept only to
-// reproduce that measurement.
-#ifndef KVQ_CHUNK_KLO
-#define KVQ_CHUNK_KLO 3
-#endif
-
 namespace kvq {
 namespace {
 
@@ -126,12 +116,18 @@ __device__ __forceinline__ void k4_pairs(uint32_t w, uint32_t bias, half2_t (&c)
   }
 }
 
-template <int KB, int VB, int D, bool QSPLIT, int KLO_>
+// The key low part's format: 3 = fp6 (E2M3), 2 = fp8 (E4M3), both with power-of-two block
+// scales on the block-scaled MFMA; 0 = none (fp16 and fp8 keys are exact in fp16).  fp6 needs
+// a whole block per producer thread (head_dim 128), and fp32 queries keep fp8 (the fp6 query
+// exchange would spill their registers in the tile loop).
+template <int KB, int D, bool QSPLIT>
+constexpr int key_lo_format() {
+  return KB == 16 || KB == kF8 ? 0 : (D == 128 && !QSPLIT ? 3 : 2);
+}
+
+template <int KB, int VB, int D, bool QSPLIT>
 __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(ChunkArgs a) {
-  // fp16 and fp8 keys are exact already; an fp6 low part needs a whole block per producer
-  // thread, and fp32 queries keep the fp8 one (the fp6 query exchange would spill their
-  // registers in the tile loop)
-  constexpr int KLO = KB == 16 || KB == kF8 ? 0 : (KLO_ == 3 && (D != 128 || QSPLIT) ? 2 : KLO_);
+  constexpr int KLO = key_lo_format<KB, D, QSPLIT>();
   constexpr bool KSPLIT = KLO != 0;
   constexpr int NK = kChunkKeys;   // keys per tile
   constexpr int KSTR = D + 8;      // halves per LDS key row
@@ -151,7 +147,6 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(ChunkArgs a) {
   static_assert(kChunkThreads == 768 && kChunkRows == 256, "8 consumer + 4 producer waves");
   // two tile buffers: the producers fill one while the consumers read the other
   __shared__ __attribute__((aligned(16))) _Float16 s_k[2 * KBUF];
-  __shared__ __attribute__((aligned(16))) _Float16 s_kl[KLO == 1 ? 2 * KBUF : 8];
   __shared__ __attribute__((aligned(16))) uint8_t s_kl8[KLO >= 2 ? 2 * NK * LSTR : 16];
   __shared__ __attribute__((aligned(4))) uint8_t s_kls[KLO >= 2 ? 2 * NK * NB : 4];
   __shared__ __attribute__((aligned(16))) uint8_t s_q8[KLO >= 2 ? kChunkRows * LSTR : 16];  // fp8 / fp6 queries
@@ -226,7 +221,6 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(ChunkArgs a) {
     asm volatile("v_mov_b32 %0, %1" : "=v"(bias) : "i"(kHalfBias1024));
     auto produce = [&](int buf) {
       _Float16* bk = s_k + buf * KBUF;
-      _Float16* bkl = s_kl + (KLO == 1 ? buf * KBUF : 0);
       _Float16* bv = s_vt + buf * VBUF;
       {
         half2_t hi[KE / 2], lo[KE / 2];
@@ -270,9 +264,6 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(ChunkArgs a) {
           const int off = k_key * KSTR + k_part * KE + 8 * i;
           *reinterpret_cast<uint4*>(&bk[off]) =
               make_uint4(u32(hi[4 * i]), u32(hi[4 * i + 1]), u32(hi[4 * i + 2]), u32(hi[4 * i + 3]));
-          if constexpr (KLO == 1)
-            *reinterpret_cast<uint4*>(&bkl[off]) =
-                make_uint4(u32(lo[4 * i]), u32(lo[4 * i + 1]), u32(lo[4 * i + 2]), u32(lo[4 * i + 3]));
         }
         if constexpr (KLO == 2) {
           // lo / 2^t as E4M3 with t = max(e, 1) - 26 for the fp16 exponent field e of the scale:
@@ -460,8 +451,9 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(ChunkArgs a) {
     for (int mm = 0; mm < NBH; ++mm) {
       // elements 8 hl + i (run 0) and 16 + 8 hl + i (run 1) of blocks 2 mm and 2 mm + 1 are here;
       // send the partner those of the block it converts, receive those of ours
-      const half8_t mine0 = qv[2 * (2 * mm + hl)], mine1 = qv[2 * (2 * mm + hl) + 1];
-      const half8_t send0 = qv[2 * (2 * mm + 1 - hl)], send1 = qv[2 * (2 * mm + 1 - hl) + 1];
+      // (selects, not an index by hl: a lane-dependent index would put qv in scratch memory)
+      const half8_t mine0 = hl ? qv[4 * mm + 2] : qv[4 * mm], mine1 = hl ? qv[4 * mm + 3] : qv[4 * mm + 1];
+      const half8_t send0 = hl ? qv[4 * mm] : qv[4 * mm + 2], send1 = hl ? qv[4 * mm + 1] : qv[4 * mm + 3];
       half8_t got0, got1;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
@@ -503,8 +495,8 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(ChunkArgs a) {
     for (int v = 0; v < 16; ++v) o[t][v] = 0.f;
 
   // one 32-key half of a tile: S^T = K Q^T, online softmax, O^T += V^T P^T
-  auto half = [&](auto masked, const _Float16* bk, const _Float16* bkl, const uint8_t* bkl8, const uint8_t* bks,
-                  const _Float16* bv, int64_t kt0, int st) {
+  auto half = [&](auto masked, const _Float16* bk, const uint8_t* bkl8, const uint8_t* bks, const _Float16* bv,
+                  int64_t kt0, int st) {
     float16_t sv;
 #pragma unroll
     for (int v = 0; v < 16; ++v) sv[v] = 0.f;
@@ -513,10 +505,6 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(ChunkArgs a) {
       const int off = (32 * st + col) * KSTR + 16 * k + 8 * hl;
       const half8_t ak = *reinterpret_cast<const half8_t*>(&bk[off]);
       sv = __builtin_amdgcn_mfma_f32_32x32x16_f16(ak, qv[k], sv, 0, 0, 0);
-      if constexpr (KLO == 1) {
-        const half8_t al = *reinterpret_cast<const half8_t*>(&bkl[off]);
-        sv = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, qv[k], sv, 0, 0, 0);
-      }
       if constexpr (QSPLIT) sv = __builtin_amdgcn_mfma_f32_32x32x16_f16(ak, ql[k], sv, 0, 0, 0);
     }
     if constexpr (KLO == 2) {
@@ -609,13 +597,12 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(ChunkArgs a) {
     if (wave_active) {
       const int buf = t & 1;
       const _Float16* bk = s_k + buf * KBUF;
-      const _Float16* bkl = s_kl + (KLO == 1 ? buf * KBUF : 0);
       const uint8_t* bkl8 = s_kl8 + (KLO >= 2 ? buf * NK * LSTR : 0);
       const uint8_t* bks = s_kls + (KLO >= 2 ? buf * NK * NB : 0);
       const _Float16* bv = s_vt + buf * VBUF;
       const int64_t kt0 = k_lo + (int64_t)t * NK;
-      half(masked, bk, bkl, bkl8, bks, bv, kt0, 0);
-      half(masked, bk, bkl, bkl8, bks, bv, kt0, 1);
+      half(masked, bk, bkl8, bks, bv, kt0, 0);
+      half(masked, bk, bkl8, bks, bv, kt0, 1);
     }
     __syncthreads();
   };
@@ -658,7 +645,7 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(ChunkArgs a) {
 
 template <int KB, int VB, int D, bool QSPLIT>
 const void* kernel_ptr() {
-  return reinterpret_cast<const void*>(&chunk_kernel<KB, VB, D, QSPLIT, KVQ_CHUNK_KLO>);
+  return reinterpret_cast<const void*>(&chunk_kernel<KB, VB, D, QSPLIT>);
 }
 
 template <int KB, int VB, int D>
@@ -667,9 +654,9 @@ hipError_t launch_t(const ChunkArgs& a, hipStream_t s) {
   const int64_t mt = (rows + kChunkRows - 1) / kChunkRows;
   dim3 grid((unsigned)mt, a.hkv, a.n_splits);
   if (a.q_dtype == 0)
-    hipLaunchKernelGGL((chunk_kernel<KB, VB, D, true, KVQ_CHUNK_KLO>), grid, dim3(kChunkThreads), 0, s, a);
+    hipLaunchKernelGGL((chunk_kernel<KB, VB, D, true>), grid, dim3(kChunkThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((chunk_kernel<KB, VB, D, false, KVQ_CHUNK_KLO>), grid, dim3(kChunkThreads), 0, s, a);
+    hipLaunchKernelGGL((chunk_kernel<KB, VB, D, false>), grid, dim3(kChunkThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -35,12 +35,7 @@
 #include "buffer_ops.h"
 #include "wave_ops.h"
 
-#ifndef KVQ_DECODE_DEPTH
-#define KVQ_DECODE_DEPTH 4   // steps of key/value codes requested ahead of the one computing
-#endif
-#ifndef KVQ_DECODE_MFMA_QK
-#define KVQ_DECODE_MFMA_QK 1 // 8/4-bit keys: Q.K on the matrix cores (int8 MFMA per 32-element block)
-#endif
+constexpr int kDecodeDepth = 4;   // steps of key/value codes requested ahead of the one computing
 
 namespace kvq {
 namespace {
@@ -261,7 +256,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   // block's digit sums is subtracted from each result.
   // (4-bit keys at group 16 keep the VALU path: the corrections do not fit beside 16 heads'
   // accumulators)
-  constexpr bool MQK = (KB == 8 || (KB == 4 && GP <= 8)) && KVQ_DECODE_MFMA_QK;
+  constexpr bool MQK = KB == 8 || (KB == 4 && GP <= 8);
   constexpr int NQ = (2 * GP + 7) / 8;   // quads of result rows that hold query rows
   i32x4 qA[MQK ? NB : 1];
   int qcorr[MQK && KB == 4 ? NQ : 1][2][MQK && KB == 4 ? NB : 1];   // 8 (256 S_hi + S_lo) per head, block
@@ -309,7 +304,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   // widened to fp16 (exactly; the block's power-of-two scale folds into the conversion).
   // Lane (r, h) loads token r's bytes [h D / 2, (h + 1) D / 2); k-step k takes its bytes
   // 8 k .. 8 k + 7 (block (h D / 2 + 8 k) / 32), and the query rows follow that order.
-  constexpr bool MQF = KB == kF8 && KVQ_DECODE_MFMA_QK;
+  constexpr bool MQF = KB == kF8;
   constexpr int NK8 = D / 16;                       // k-steps of one 32-token group
   constexpr int QROWS = QLO ? 2 * GP : GP;
   half8_t qF[MQF ? NK8 : 1];
@@ -348,7 +343,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   // PD steps ahead are requested before step s computes.  The last PD steps of phase A
   // request the first value steps of the chunk, and the last PD steps of phase C the
   // first key steps of the wave's next chunk, so the pipeline never drains.
-  constexpr int PD = KVQ_DECODE_DEPTH < NS ? KVQ_DECODE_DEPTH : NS - 1, R = PD + 1;
+  constexpr int PD = kDecodeDepth < NS ? kDecodeDepth : NS - 1, R = PD + 1;
   static_assert(PD >= 1, "prefetch depth");
   uint32_t kbuf[R][2][KW], vbuf[R][2][VW];
   uint16_t kscl[R][2], vscl[R][2];
