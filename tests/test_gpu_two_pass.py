@@ -9,6 +9,8 @@ no key must come back exactly as m = -inf, l = 0, o = 0.
 """
 from __future__ import annotations
 
+import ctypes
+
 import numpy as np
 import pytest
 
@@ -183,9 +185,13 @@ def test_partial_entry_points_reject_bad_splits():
                 kvq.kv_attend_decode_partial([h], 0, qd, 0.125, n_splits, per)
             assert e.value.code == kvq.KV_EINVAL
         small = torch.empty((1, 4, 3, 66), dtype=torch.float32, device="cuda")
-        with pytest.raises(kvq.KVError) as e:
+        with pytest.raises(ValueError):   # the binding checks the shape first
             kvq.kv_attend_decode_partial([h], 0, qd, 0.125, 4, 512, partials=small)
-        assert e.value.code == kvq.KV_EINVAL and "smaller" in str(e.value)
+        arr = (ctypes.c_void_p * 1)(h)     # the library checks the byte count itself
+        rc = kvq.lib().kv_attend_decode_partial(arr, 1, 0, qd.data_ptr(), kvq.KV_BF16, 4, 0.125, 4, 512,
+                                                small.data_ptr(), small.numel() * 4,
+                                                torch.cuda.current_stream().cuda_stream)
+        assert rc == kvq.KV_EINVAL and "smaller" in kvq.kv_last_error()
         qc = dev(q.repeat(10, axis=0), "bf16")
         for n_splits, per in [(2, 700), (1, 1024), (70000, 64)]:
             with pytest.raises(kvq.KVError) as e:
