@@ -23,6 +23,9 @@ _SIGS = {
     "kv_cache_create": (C.c_void_p, [C.c_int, C.c_int, C.c_int, C.c_int, C.c_int64]),
     "kv_cache_create_layered": (C.c_void_p, [C.POINTER(C.c_int), C.c_int, C.c_int, C.c_int, C.c_int64]),
     "kv_cache_layout": (C.c_int, [C.c_void_p, C.c_int]),
+    "kv_cache_shape": (C.c_int, [C.c_void_p, C.POINTER(C.c_int), C.POINTER(C.c_int), C.POINTER(C.c_int),
+                                 C.POINTER(C.c_int64)]),
+    "kv_cache_check_guard": (C.c_int, [C.c_void_p]),
     "kv_layered_footprint_bytes": (C.c_int64, [C.POINTER(C.c_int), C.c_int, C.c_int, C.c_int, C.c_int64]),
     "kv_cache_destroy": (None, [C.c_void_p]),
     "kv_append_quant": (C.c_int, [C.c_void_p, C.c_int, C.c_void_p, C.c_void_p, C.c_int, C.c_int64, C.c_void_p]),
@@ -125,6 +128,45 @@ def _stream(stream) -> int:
     return getattr(stream, "cuda_stream", stream)
 
 
+def _same_device(t, ref, name: str) -> None:
+    if t.device != ref.device:
+        raise ValueError(f"{name} is on {t.device}, expected {ref.device}")
+
+
+def _expect_f32(t, shape, name: str) -> None:
+    """A caller-supplied output: fp32 of exactly this shape."""
+    torch = _torch()
+    if t.dtype != torch.float32:
+        raise ValueError(f"{name} must be float32 (got {t.dtype})")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+
+
+def _cache_shape(cache: int):
+    """(n_layers, n_kv_heads, head_dim, max_tokens) of a cache, from the library."""
+    nl, hkv, d, mt = C.c_int(), C.c_int(), C.c_int(), C.c_int64()
+    _check(lib().kv_cache_shape(cache, C.byref(nl), C.byref(hkv), C.byref(d), C.byref(mt)))
+    return nl.value, hkv.value, d.value, mt.value
+
+
+def _sessions_shape(sessions):
+    if len(sessions) == 0:
+        raise ValueError("at least one session is needed")
+    return _cache_shape(sessions[0])
+
+
+def _check_q(q, n_rows: int, rows_name: str, head_dim: int, n_kv_heads: int) -> None:
+    if q.dim() != 3:
+        raise ValueError(f"q must be [{rows_name}, n_q_heads, head_dim] (got shape {tuple(q.shape)})")
+    if q.shape[0] != n_rows:
+        raise ValueError(f"q's first dimension must equal {rows_name} ({n_rows}, got {q.shape[0]})")
+    if q.shape[2] != head_dim:
+        raise ValueError(f"q's head_dim {q.shape[2]} differs from the cache's {head_dim}")
+    if q.shape[1] < 1 or q.shape[1] % n_kv_heads:
+        raise ValueError(f"n_q_heads {q.shape[1]} is not a positive multiple of n_kv_heads {n_kv_heads}")
+    _dtype_code(q)
+
+
 # ---------------------------------------------------------------------------
 # entry points
 # ---------------------------------------------------------------------------
@@ -155,9 +197,19 @@ def kv_cache_layout(cache: int, layer: int) -> int:
     return _check(lib().kv_cache_layout(cache, layer))
 
 
+def kv_cache_shape(cache: int):
+    """(n_layers, n_kv_heads, head_dim, max_tokens)."""
+    return _cache_shape(cache)
+
+
 def kv_layered_footprint_bytes(layouts, n_kv_heads: int, head_dim: int, max_tokens: int) -> int:
     arr, n = _layout_array(layouts)
     return _check(lib().kv_layered_footprint_bytes(arr, n, n_kv_heads, head_dim, max_tokens))
+
+
+def kv_cache_check_guard(cache: int) -> None:
+    """Raise KVError if the guard bytes after the cache's arena were overwritten."""
+    _check(lib().kv_cache_check_guard(cache))
 
 
 def kv_cache_destroy(cache: int) -> None:
@@ -168,6 +220,11 @@ def kv_append_quant(cache: int, layer: int, k, v, stream=None) -> None:
     """k, v: device tensors [n_new, n_kv_heads, head_dim] (fp32 / bf16 / fp16)."""
     if k.shape != v.shape or k.dtype != v.dtype or k.dim() != 3:
         raise ValueError("k and v must be [n_new, n_kv_heads, head_dim] of one dtype")
+    _, hkv, d, _ = _cache_shape(cache)
+    if tuple(k.shape[1:]) != (hkv, d):
+        raise ValueError(f"k and v must be [n_new, {hkv}, {d}] for this cache (got {tuple(k.shape)})")
+    _dtype_code(k)
+    _same_device(v, k, "v")
     _check(lib().kv_append_quant(cache, layer, _dev_ptr(k, "k"), _dev_ptr(v, "v"), _dtype_code(k),
                                  k.shape[0], _stream(stream)))
 
@@ -184,14 +241,17 @@ def kv_decode_workspace_bytes(sessions, layer: int, n_q_heads: int) -> int:
 def kv_attend_decode(sessions, layer: int, q, sm_scale: float, out=None, workspace=None, stream=None):
     """q: device [n_sessions, n_q_heads, head_dim]; returns out (fp32, same shape)."""
     torch = _torch()
+    _, hkv, d, _ = _sessions_shape(sessions)
+    _check_q(q, len(sessions), "the number of sessions", d, hkv)
     n_s, hq, d = q.shape
-    if n_s != len(sessions):
-        raise ValueError("q's first dimension must equal the number of sessions")
     if out is None:
         out = torch.empty((n_s, hq, d), dtype=torch.float32, device=q.device)
+    _expect_f32(out, q.shape, "out")
+    _same_device(out, q, "out")
     if workspace is None:
         nb = kv_decode_workspace_bytes(sessions, layer, hq)
         workspace = torch.empty(max(nb, 16), dtype=torch.uint8, device=q.device)
+    _same_device(workspace, q, "workspace")
     _check(lib().kv_attend_decode(_handles(sessions), len(sessions), layer, _dev_ptr(q, "q"), _dtype_code(q),
                                   hq, float(sm_scale), _dev_ptr(out, "out"), _dev_ptr(workspace, "workspace"),
                                   workspace.numel() * workspace.element_size(), _stream(stream)))
@@ -209,11 +269,13 @@ def kv_attend_decode_partial(sessions, layer: int, q, sm_scale: float, n_splits:
                              partials=None, stream=None):
     """First pass only; returns partials (fp32 [n_sessions, n_q_heads, n_splits, head_dim + 2])."""
     torch = _torch()
+    _, hkv, d, _ = _sessions_shape(sessions)
+    _check_q(q, len(sessions), "the number of sessions", d, hkv)
     n_s, hq, d = q.shape
-    if n_s != len(sessions):
-        raise ValueError("q's first dimension must equal the number of sessions")
     if partials is None:
         partials = torch.empty((n_s, hq, n_splits, d + 2), dtype=torch.float32, device=q.device)
+    _expect_f32(partials, (n_s, hq, n_splits, d + 2), "partials")
+    _same_device(partials, q, "partials")
     _check(lib().kv_attend_decode_partial(_handles(sessions), len(sessions), layer, _dev_ptr(q, "q"),
                                           _dtype_code(q), hq, float(sm_scale), n_splits, tokens_per_split,
                                           _dev_ptr(partials, "partials"),
@@ -233,6 +295,8 @@ def kv_merge_partials(partials, out=None, stream=None):
         rows *= x
     if out is None:
         out = torch.empty(lead + (d,), dtype=torch.float32, device=partials.device)
+    _expect_f32(out, lead + (d,), "out")
+    _same_device(out, partials, "out")
     _check(lib().kv_merge_partials(_dev_ptr(partials, "partials"), rows, n_splits, d, _dev_ptr(out, "out"),
                                    _stream(stream)))
     return out
@@ -249,11 +313,13 @@ def kv_attend_chunk_partial(cache: int, layer: int, q, n_new: int, sm_scale: flo
                             keys_per_split: int, partials=None, stream=None):
     """First pass only; returns partials (fp32 [n_new, n_q_heads, n_splits, head_dim + 2])."""
     torch = _torch()
+    _, hkv, d, _ = _cache_shape(cache)
+    _check_q(q, n_new, "n_new", d, hkv)
     n, hq, d = q.shape
-    if n != n_new:
-        raise ValueError("q's first dimension must equal n_new")
     if partials is None:
         partials = torch.empty((n, hq, n_splits, d + 2), dtype=torch.float32, device=q.device)
+    _expect_f32(partials, (n, hq, n_splits, d + 2), "partials")
+    _same_device(partials, q, "partials")
     _check(lib().kv_attend_chunk_partial(cache, layer, _dev_ptr(q, "q"), _dtype_code(q), hq, n_new,
                                          float(sm_scale), n_splits, keys_per_split, _dev_ptr(partials, "partials"),
                                          partials.numel() * partials.element_size(), _stream(stream)))
@@ -268,14 +334,17 @@ def kv_attend_chunk(cache: int, layer: int, q, n_new: int, sm_scale: float, out=
                     stream=None):
     """q: device [n_new, n_q_heads, head_dim]; returns out (fp32, same shape)."""
     torch = _torch()
+    _, hkv, d, _ = _cache_shape(cache)
+    _check_q(q, n_new, "n_new", d, hkv)
     n, hq, d = q.shape
-    if n != n_new:
-        raise ValueError("q's first dimension must equal n_new")
     if out is None:
         out = torch.empty((n, hq, d), dtype=torch.float32, device=q.device)
+    _expect_f32(out, q.shape, "out")
+    _same_device(out, q, "out")
     if workspace is None:
         nb = kv_chunk_workspace_bytes(cache, layer, hq, n_new)
         workspace = torch.empty(max(nb, 16), dtype=torch.uint8, device=q.device)
+    _same_device(workspace, q, "workspace")
     _check(lib().kv_attend_chunk(cache, layer, _dev_ptr(q, "q"), _dtype_code(q), hq, n_new, float(sm_scale),
                                  _dev_ptr(out, "out"), _dev_ptr(workspace, "workspace"),
                                  workspace.numel() * workspace.element_size(), _stream(stream)))
@@ -314,6 +383,9 @@ def kv_cache_plane(cache: int, layer: int, kv_head: int, plane: int):
 def kv_cache_copy_plane(cache: int, layer: int, kv_head: int, plane: int, row0: int, n_rows: int, dst,
                         stream=None):
     """Copy plane rows into the device uint8 tensor ``dst`` (n_rows * row_bytes bytes)."""
+    _, rb = kv_cache_plane(cache, layer, kv_head, plane)
+    if dst.numel() * dst.element_size() < n_rows * rb:
+        raise ValueError(f"dst holds {dst.numel() * dst.element_size()} bytes, the rows need {n_rows * rb}")
     _check(lib().kv_cache_copy_plane(cache, layer, kv_head, plane, row0, n_rows, _dev_ptr(dst, "dst"),
                                      _stream(stream)))
     return dst

@@ -64,6 +64,11 @@ bool layout_bits(int layout, int* kb, int* vb) {
   return true;
 }
 
+// Guard bytes after the planes of every arena: a fixed pattern that no kernel writes, checked by
+// kv_cache_check_guard (a write past the last plane would land there first).
+constexpr int64_t kGuardBytes = 256;
+constexpr int kGuardByte = 0xA5;
+
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 int64_t ceil_div(int64_t x, int64_t m) { return (x + m - 1) / m; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -280,13 +285,14 @@ kv_cache* kv_cache_create_layered(const int* layouts, int n_layers, int n_kv_hea
     return nullptr;
   }
   void* p = nullptr;
-  e = hipMalloc(&p, (size_t)bytes);
+  e = hipMalloc(&p, (size_t)(bytes + kGuardBytes));
   if (e != hipSuccess || !p) {
     (void)hipGetLastError();
-    fail(KV_ENOMEM, "hipMalloc of %lld bytes failed: %s", (long long)bytes, hipGetErrorString(e));
+    fail(KV_ENOMEM, "hipMalloc of %lld bytes failed: %s", (long long)(bytes + kGuardBytes), hipGetErrorString(e));
     return nullptr;
   }
   e = hipMemset(p, 0, (size_t)bytes);
+  if (e == hipSuccess) e = hipMemset(static_cast<uint8_t*>(p) + bytes, kGuardByte, kGuardBytes);
   if (e != hipSuccess) {
     (void)hipFree(p);
     fail(KV_EHIP, "hipMemset: %s", hipGetErrorString(e));
@@ -319,6 +325,31 @@ int kv_cache_layout(const kv_cache* cache, int layer) {
   if (!cache) return fail(KV_EINVAL, "cache is NULL");
   if (layer < 0 || layer >= cache->n_layers) return fail(KV_EINVAL, "layer %d out of range", layer);
   return cache->lg[layer].layout;
+}
+
+int kv_cache_shape(const kv_cache* cache, int* n_layers, int* n_kv_heads, int* head_dim, int64_t* max_tokens) {
+  clear_err();
+  if (!cache) return fail(KV_EINVAL, "cache is NULL");
+  if (n_layers) *n_layers = cache->n_layers;
+  if (n_kv_heads) *n_kv_heads = cache->hkv;
+  if (head_dim) *head_dim = cache->d;
+  if (max_tokens) *max_tokens = cache->max_tokens;
+  return KV_OK;
+}
+
+int kv_cache_check_guard(const kv_cache* cache) {
+  clear_err();
+  int rc = check_cache(cache);
+  if (rc) return rc;
+  uint8_t g[kGuardBytes];
+  hipError_t e = hipDeviceSynchronize();
+  if (e == hipSuccess) e = hipMemcpy(g, cache->arena + cache->bytes, (size_t)kGuardBytes, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(const_cast<kv_cache*>(cache), e, "guard read");
+  for (int64_t i = 0; i < kGuardBytes; ++i)
+    if (g[i] != kGuardByte)
+      return fail(KV_EINVAL, "guard byte %lld after the arena reads 0x%02x, not 0x%02x: something wrote past the planes",
+                  (long long)i, g[i], kGuardByte);
+  return KV_OK;
 }
 
 void kv_cache_destroy(kv_cache* cache) {
@@ -867,6 +898,27 @@ int chunk_launch(kv_cache* cache, int layer, const ChunkPrep& p, const void* q, 
   return KV_OK;
 }
 
+// kv_attend_decode's work once its arguments are checked and planned: the partial pass (or the
+// whole attention for one split) and the merge, with the partials in ws.
+int decode_run(kv_cache* const* sessions, int n_sessions, int layer, const DecodePrep& p, const void* q, int q_dtype,
+               int n_q_heads, float sm_scale, float* out, int n_splits, int64_t tps, float* ws, hipStream_t st) {
+  int32_t n_valid[kMaxSessions];
+  for (int i = 0; i < n_sessions && i < kMaxSessions; ++i) n_valid[i] = (int32_t)ceil_div(std::max<int64_t>(p.lens[i], 1), tps);
+  const bool compact = decode_compact(n_sessions, n_splits, n_valid);
+  int rc = decode_launch(sessions, n_sessions, layer, p, q, q_dtype, n_q_heads, sm_scale, n_splits, tps, n_splits > 1,
+                         ws, out, st, compact);
+  if (rc) return rc;
+  if (n_splits > 1) {
+    hipError_t e = merge_launch(ws, (int64_t)n_sessions * n_q_heads, n_splits, p.d, out, st,
+                                compact ? n_q_heads : 0, compact ? n_valid : nullptr);
+    if (e != hipSuccess) {
+      for (int i = 0; i < n_sessions; ++i) sessions[i]->poisoned = true;
+      return fail(KV_EHIP, "merge launch: %s", hipGetErrorString(e));
+    }
+  }
+  return KV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -876,7 +928,13 @@ int64_t kv_decode_workspace_bytes(kv_cache* const* sessions, int n_sessions, int
   DecodePrep p;
   int rc = decode_prepare(sessions, n_sessions, layer, n_q_heads, false, &p);
   if (rc) return rc;
-  const int64_t cap = decode_split_cap(p);
+  // no plan splits a context finer than kDecodeWaveTokens, so the splits are also bounded by
+  // the sessions' capacities (still a function of shapes only: a workspace sized once keeps
+  // fitting as the caches grow)
+  int64_t by_capacity = 1;
+  for (int i = 0; i < n_sessions; ++i)
+    by_capacity = std::max(by_capacity, ceil_div(sessions[i]->max_tokens, kDecodeWaveTokens));
+  const int64_t cap = std::min(decode_split_cap(p), by_capacity);
   if (cap <= 1) return 0;
   return (int64_t)n_sessions * n_q_heads * cap * (p.d + 2) * (int64_t)sizeof(float);
 }
@@ -905,23 +963,8 @@ int kv_attend_decode(kv_cache* const* sessions, int n_sessions, int layer, const
   decode_plan(p, &n_splits, &tps);
   const int64_t need = n_splits > 1 ? partial_bytes(n_sessions * (int64_t)n_q_heads, n_splits, p.d) : 0;
   if ((rc = check_workspace(workspace, ws_bytes, need))) return rc;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  float* ws = static_cast<float*>(workspace);
-  int32_t n_valid[kMaxSessions];
-  for (int i = 0; i < n_sessions && i < kMaxSessions; ++i) n_valid[i] = (int32_t)ceil_div(std::max<int64_t>(p.lens[i], 1), tps);
-  const bool compact = decode_compact(n_sessions, n_splits, n_valid);
-  if ((rc = decode_launch(sessions, n_sessions, layer, p, q, q_dtype, n_q_heads, sm_scale, n_splits, tps,
-                          n_splits > 1, ws, out, st, compact)))
-    return rc;
-  if (n_splits > 1) {
-    hipError_t e = merge_launch(ws, (int64_t)n_sessions * n_q_heads, n_splits, p.d, out, st,
-                                compact ? n_q_heads : 0, compact ? n_valid : nullptr);
-    if (e != hipSuccess) {
-      for (int i = 0; i < n_sessions; ++i) sessions[i]->poisoned = true;
-      return fail(KV_EHIP, "merge launch: %s", hipGetErrorString(e));
-    }
-  }
-  return KV_OK;
+  return decode_run(sessions, n_sessions, layer, p, q, q_dtype, n_q_heads, sm_scale, out, n_splits, tps,
+                    static_cast<float*>(workspace), static_cast<hipStream_t>(stream));
 }
 
 int kv_attend_decode_partial(kv_cache* const* sessions, int n_sessions, int layer, const void* q,

@@ -108,6 +108,17 @@ kv_cache* kv_cache_create_layered(const int* layouts, int n_layers, int n_kv_hea
 /* Layout code of one layer; < 0 on bad arguments. */
 int kv_cache_layout(const kv_cache* cache, int layer);
 
+/* Shape of a cache as created: any of the out pointers may be NULL.  KV_EINVAL for a NULL
+ * cache.  (Lets a binding check k, v, q and out against the cache before a call.) */
+int kv_cache_shape(const kv_cache* cache, int* n_layers, int* n_kv_heads, int* head_dim,
+                   int64_t* max_tokens);
+
+/* Debugging aid: the arena carries 256 guard bytes of a fixed pattern after its planes, which
+ * no kernel writes.  Waits for the device to finish all queued work, reads them back and
+ * returns KV_OK if they are intact, KV_EINVAL (with the first changed byte in
+ * kv_last_error) if something wrote past the planes, KV_EHIP if the read failed. */
+int kv_cache_check_guard(const kv_cache* cache);
+
 /* Free the arena.  The caller ensures no queued work still uses the cache.  NULL is a no-op. */
 void kv_cache_destroy(kv_cache* cache);
 
@@ -136,7 +147,9 @@ int kv_attend_decode(kv_cache* const* sessions, int n_sessions, int layer, const
                      int q_dtype, int n_q_heads, float sm_scale, float* out,
                      void* workspace, size_t ws_bytes, void* stream);
 
-/* Workspace bytes kv_attend_decode needs for these sessions; < 0 on bad arguments. */
+/* Workspace bytes kv_attend_decode needs for these sessions; < 0 on bad arguments.  It
+ * depends only on shapes (n_sessions, n_q_heads, head_dim, the sessions' max_tokens, the
+ * device), so a workspace sized once fits every later call on the same caches. */
 int64_t kv_decode_workspace_bytes(kv_cache* const* sessions, int n_sessions, int layer,
                                   int n_q_heads);
 

@@ -43,6 +43,8 @@ def gpu_cache(layout, n_layers, n_kv_heads, head_dim, max_tokens):
     h = kvq.kv_cache_create(layout, n_layers, n_kv_heads, head_dim, max_tokens)
     try:
         yield h
+        torch_mod().cuda.synchronize()
+        kvq.kv_cache_check_guard(h)   # nothing wrote past the planes
     finally:
         torch_mod().cuda.synchronize()
         kvq.kv_cache_destroy(h)

@@ -97,6 +97,8 @@ def test_null_handles_are_rejected(built_library):
     assert L.kv_session_bytes(None) == kvq.KV_EINVAL
     assert L.kv_session_save(None, None, 0, None) == kvq.KV_EINVAL
     assert L.kv_session_load(None, None, 0, None) == kvq.KV_EINVAL
+    assert L.kv_cache_shape(None, None, None, None, None) == kvq.KV_EINVAL
+    assert L.kv_cache_check_guard(None) == kvq.KV_EINVAL
 
 
 def test_merge_checks_arguments_on_the_host(built_library):
@@ -158,3 +160,72 @@ def test_header_compiles_as_c99_and_links(tmp_path, built_library):
                     f"-Wl,-rpath,{lib_dir}"], check=True)
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0 and r.stdout.strip() == "ok", (r.returncode, r.stdout, r.stderr)
+
+
+def test_binding_checks_tensors_against_the_cache(monkeypatch):
+    """The binding rejects tensors whose shape, dtype or head_dim disagree with the cache before
+    any pointer reaches the library (a mismatch would make the kernels read or write past an
+    allocation).  The cache shape comes from kv_cache_shape; here it is stubbed, since creating a
+    cache needs a GPU, and CPU tensors stand in (a well-formed call then stops at the device check)."""
+    import torch
+    monkeypatch.setattr(_lib, "_cache_shape", lambda cache: (1, 4, 128, 1000))
+    f32, bf16 = torch.float32, torch.bfloat16
+
+    def rejects(fn, *args, match, **kw):
+        with pytest.raises((ValueError, TypeError)) as e:
+            fn(*args, **kw)
+        assert match in str(e.value), str(e.value)
+
+    z = lambda *shape, dt=bf16: torch.zeros(shape, dtype=dt)
+    # append: k, v [n_new, n_kv_heads, head_dim] of the cache
+    rejects(kvq.kv_append_quant, 1, 0, z(5, 4, 64), z(5, 4, 64), match="[n_new, 4, 128]")
+    rejects(kvq.kv_append_quant, 1, 0, z(5, 2, 128), z(5, 2, 128), match="[n_new, 4, 128]")
+    rejects(kvq.kv_append_quant, 1, 0, z(5, 4, 128), z(5, 4, 128, dt=f32), match="one dtype")
+    rejects(kvq.kv_append_quant, 1, 0, z(5, 4, 128, dt=torch.int32), z(5, 4, 128, dt=torch.int32), match="dtype")
+    rejects(kvq.kv_append_quant, 1, 0, z(5, 4, 128), z(5, 4, 128), match="device tensor")   # shapes fine
+    # decode: q [n_sessions, n_q_heads, head_dim], out fp32 of q's shape
+    rejects(kvq.kv_attend_decode, [1], 0, z(1, 8, 64), 0.1, match="head_dim")
+    rejects(kvq.kv_attend_decode, [1, 1], 0, z(1, 8, 128), 0.1, match="number of sessions")
+    rejects(kvq.kv_attend_decode, [1], 0, z(1, 6, 128), 0.1, match="multiple of n_kv_heads")
+    rejects(kvq.kv_attend_decode, [1], 0, z(1, 8, 128), 0.1, out=z(1, 8, 128), match="float32")
+    rejects(kvq.kv_attend_decode, [1], 0, z(1, 8, 128), 0.1, out=z(1, 8, 64, dt=f32), match="shape")
+    rejects(kvq.kv_attend_decode, [], 0, z(0, 8, 128), 0.1, match="session")
+    rejects(kvq.kv_attend_decode_partial, [1], 0, z(1, 8, 128), 0.1, 2, 512, partials=z(1, 8, 3, 130, dt=f32),
+            match="shape")
+    # chunk: q [n_new, n_q_heads, head_dim]
+    rejects(kvq.kv_attend_chunk, 1, 0, z(3, 8, 128), 4, 0.1, match="n_new")
+    rejects(kvq.kv_attend_chunk, 1, 0, z(4, 8, 96), 4, 0.1, match="head_dim")
+    rejects(kvq.kv_attend_chunk, 1, 0, z(4, 8, 128), 4, 0.1, out=z(4, 8, 128, dt=torch.float16), match="float32")
+    rejects(kvq.kv_attend_chunk_partial, 1, 0, z(4, 8, 128), 4, 0.1, 2, 64, partials=z(4, 8, 2, 128, dt=f32),
+            match="shape")
+    rejects(kvq.kv_attend_chunk, 1, 0, z(4, 8, 128), 4, 0.1, workspace=z(16, dt=torch.uint8), match="device tensor")
+    # merge: out [..., head_dim] fp32
+    rejects(kvq.kv_merge_partials, z(4, 3, 130, dt=f32), out=z(4, 129, dt=f32), match="shape")
+
+
+def test_host_library_under_address_and_undefined_behavior_sanitizers(tmp_path):
+    """The host half of libkvq (argument checks, shape and footprint arithmetic, planning) built
+    with g++ -fsanitize=address,undefined, the kernel launchers replaced by failing stubs, and
+    driven by tests/c/host_checks.c: every size, offset and status path it reaches must run clean."""
+    import shutil
+    import subprocess
+    gxx, gcc = shutil.which("g++"), shutil.which("gcc")
+    if gxx is None or gcc is None:
+        pytest.skip("no g++/gcc")
+    rocm = Path("/opt/rocm")
+    csrc = ROOT / "asymmetric_quantized_kv_amd" / "csrc"
+    so = tmp_path / "libkvq_hostsan.so"
+    san = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer", "-g"]
+    subprocess.run([gxx, "-std=c++17", "-O1", "-shared", "-fPIC", "-D__HIP_PLATFORM_AMD__", *san,
+                    "-I", str(rocm / "include"), "-I", str(ROOT / "include"), "-I", str(csrc),
+                    str(csrc / "kvq_host.cpp"), str(ROOT / "tests" / "c" / "device_stubs.cpp"),
+                    "-o", str(so), "-L", str(rocm / "lib"), "-lamdhip64", f"-Wl,-rpath,{rocm / 'lib'}"],
+                   check=True, capture_output=True)
+    exe = tmp_path / "host_checks"
+    subprocess.run([gcc, "-std=c99", "-Wall", "-Werror", *san, "-I", str(ROOT / "include"),
+                    str(ROOT / "tests" / "c" / "host_checks.c"), "-o", str(exe), str(so), f"-Wl,-rpath,{tmp_path}"],
+                   check=True, capture_output=True)
+    env = dict(__import__("os").environ, ASAN_OPTIONS="detect_leaks=0:abort_on_error=1",
+               UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1")
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=300, env=env)
+    assert r.returncode == 0 and r.stdout.strip() == "ok", (r.returncode, r.stdout, r.stderr[-3000:])

@@ -170,7 +170,7 @@ def test_codes_exact_rational(bits):
 def _codec_cases():
     out = []
     for ln in (GOLD / "codec_cases.txt").read_text().splitlines():
-        if not ln.strip() or ln.startswith("#"):
+        if not ln.strip() or ln.startswith("#") or ln.startswith("@"):
             continue
         head, xs, codes = ln.split("|")
         name, bits, dhex = head.split()
@@ -185,6 +185,27 @@ def test_codec_golden_cases(case):
     assert gd == dbits
     assert gc[:len(codes)] == codes
     assert all(c == 0 for c in gc[len(xs):])
+
+
+def _scale_rows():
+    out = []
+    for ln in (GOLD / "codec_cases.txt").read_text().splitlines():
+        if ln.startswith("@scales"):
+            head, amaxes, hexbytes = ln.split("|")
+            out.append((int(head.split()[1]), [float(v) for v in amaxes.split()], [int(b, 16) for b in hexbytes.split()]))
+    return out
+
+
+@pytest.mark.parametrize("case", _scale_rows(), ids=lambda c: f"{c[0]}-bit")
+def test_scale_plane_bytes_golden(case):
+    """The stored scale plane of a row: each block's fp16 d, little-endian, in block order."""
+    bits, amaxes, want = case
+    row = np.zeros((1, 128), np.float32)
+    for b, a in enumerate(amaxes):
+        row[0, 32 * b] = a
+    _, scale_bytes = O.encode_rows(row, bits)
+    assert scale_bytes.shape == (1, 8)
+    assert scale_bytes[0].tolist() == want
 
 
 def test_nibble_packing_golden():
