@@ -31,6 +31,8 @@ _SIGS = {
     "kv_append_quant": (C.c_int, [C.c_void_p, C.c_int, C.c_void_p, C.c_void_p, C.c_int, C.c_int64, C.c_void_p]),
     "kv_attend_decode": (C.c_int, [C.c_void_p, C.c_int, C.c_int, C.c_void_p, C.c_int, C.c_int, C.c_float,
                                    C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
+    "kv_attend_decode_static": (C.c_int, [C.c_void_p, C.c_int, C.c_int, C.c_void_p, C.c_int, C.c_int, C.c_float,
+                                          C.c_void_p, C.c_void_p]),
     "kv_decode_workspace_bytes": (C.c_int64, [C.c_void_p, C.c_int, C.c_int, C.c_int]),
     "kv_decode_plan": (C.c_int, [C.c_void_p, C.c_int, C.c_int, C.c_int, C.POINTER(C.c_int),
                                  C.POINTER(C.c_int64)]),
@@ -255,6 +257,18 @@ def kv_attend_decode(sessions, layer: int, q, sm_scale: float, out=None, workspa
     _check(lib().kv_attend_decode(_handles(sessions), len(sessions), layer, _dev_ptr(q, "q"), _dtype_code(q),
                                   hq, float(sm_scale), _dev_ptr(out, "out"), _dev_ptr(workspace, "workspace"),
                                   workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def kv_attend_decode_static(sessions, layer: int, q, sm_scale: float, out, stream=None):
+    """kv_attend_decode with the library's static device scratch for the split partials: no
+    allocation anywhere, so out (fp32, q's shape) must be supplied."""
+    _, hkv, d, _ = _sessions_shape(sessions)
+    _check_q(q, len(sessions), "the number of sessions", d, hkv)
+    _expect_f32(out, q.shape, "out")
+    _same_device(out, q, "out")
+    _check(lib().kv_attend_decode_static(_handles(sessions), len(sessions), layer, _dev_ptr(q, "q"), _dtype_code(q),
+                                         q.shape[1], float(sm_scale), _dev_ptr(out, "out"), _stream(stream)))
     return out
 
 

@@ -18,7 +18,7 @@ ROOT = PKG.parent
 CSRC = PKG / "csrc"
 BUILD = ROOT / "_build"
 LIB = PKG / "libkvq.so"
-SOURCES = ["kvq_host.cpp", "append.hip", "decode.hip", "merge.hip", "chunk.hip"]
+SOURCES = ["kvq_host.cpp", "append.hip", "decode.hip", "merge.hip", "chunk.hip", "scratch.hip"]
 ARCH = "gfx950"
 
 

@@ -967,6 +967,31 @@ int kv_attend_decode(kv_cache* const* sessions, int n_sessions, int layer, const
                     static_cast<float*>(workspace), static_cast<hipStream_t>(stream));
 }
 
+int kv_attend_decode_static(kv_cache* const* sessions, int n_sessions, int layer, const void* q,
+                            int q_dtype, int n_q_heads, float sm_scale, float* out, void* stream) {
+  clear_err();
+  DecodePrep p;
+  int rc = decode_prepare(sessions, n_sessions, layer, n_q_heads, true, &p);
+  if (rc) return rc;
+  if ((rc = check_q_out(q, q_dtype, out, "out"))) return rc;
+  int n_splits;
+  int64_t tps;
+  decode_plan(p, &n_splits, &tps);
+  const int64_t need = n_splits > 1 ? partial_bytes(n_sessions * (int64_t)n_q_heads, n_splits, p.d) : 0;
+  if (need > (int64_t)kStaticScratchBytes)
+    return fail(KV_EINVAL,
+                "the split plan of this call (%d splits x %lld rows) needs %lld bytes of partials, more than the %lld "
+                "bytes of static scratch; use kv_attend_decode with a workspace",
+                n_splits, (long long)n_sessions * n_q_heads, (long long)need, (long long)kStaticScratchBytes);
+  float* ws = nullptr;
+  if (need > 0) {
+    hipError_t e = static_scratch(p.device, &ws);
+    if (e != hipSuccess) return fail(KV_EHIP, "static scratch lookup: %s", hipGetErrorString(e));
+  }
+  return decode_run(sessions, n_sessions, layer, p, q, q_dtype, n_q_heads, sm_scale, out, n_splits, tps, ws,
+                    static_cast<hipStream_t>(stream));
+}
+
 int kv_attend_decode_partial(kv_cache* const* sessions, int n_sessions, int layer, const void* q,
                              int q_dtype, int n_q_heads, float sm_scale, int n_splits,
                              int64_t tokens_per_split, float* partials, size_t partials_bytes,

@@ -16,6 +16,8 @@ constexpr int kChunkRows = 256;     // query rows per chunk-prefill workgroup (3
 constexpr int kChunkKeys = 64;      // keys per chunk-prefill tile
 constexpr uint32_t kXcds = 8;       // accelerator dies of an MI355X; workgroups are dealt round-robin
 
+constexpr size_t kStaticScratchBytes = size_t(16) << 20;   // device scratch of kv_attend_decode_static
+
 constexpr int kF8 = 9;              // "bits" marker of fp8 (E4M3) codes with power-of-two block scales
 
 __host__ __device__ constexpr int code_row_bytes(int bits, int d) {
@@ -108,6 +110,10 @@ hipError_t launch_decode(const DecodeArgs& a, int kbits, int vbits, int d, int g
                          hipStream_t s);
 hipError_t launch_chunk(const ChunkArgs& a, int kbits, int vbits, int d, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
+
+// Device address of the library's static scratch (kStaticScratchBytes) on `device`, looked up
+// once per device and kept.
+hipError_t static_scratch(int device, float** ptr);
 
 // Kernel symbols, for occupancy queries by the split planner.
 const void* decode_kernel_for(int kbits, int vbits, int d, int gp);

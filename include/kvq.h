@@ -147,6 +147,18 @@ int kv_attend_decode(kv_cache* const* sessions, int n_sessions, int layer, const
                      int q_dtype, int n_q_heads, float sm_scale, float* out,
                      void* workspace, size_t ws_bytes, void* stream);
 
+/* kv_attend_decode without a workspace and without any allocation, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation).  The split partials live in a static device array of the library
+ * (16 MiB per device, held from module load until the process ends).  Same arguments,
+ * split plan and results as kv_attend_decode (bit for bit).  Errors as kv_attend_decode,
+ * plus KV_EINVAL when the plan's partials (n_splits * n_sessions * n_q_heads *
+ * (head_dim + 2) * 4 bytes, see kv_decode_plan) exceed 16 MiB; a one-split plan needs none.
+ * Every call on a device shares that device's array: calls that overlap on one device (on
+ * different streams, or from different threads) race for it and must not be issued. */
+int kv_attend_decode_static(kv_cache* const* sessions, int n_sessions, int layer, const void* q,
+                            int q_dtype, int n_q_heads, float sm_scale, float* out, void* stream);
+
 /* Workspace bytes kv_attend_decode needs for these sessions; < 0 on bad arguments.  It
  * depends only on shapes (n_sessions, n_q_heads, head_dim, the sessions' max_tokens, the
  * device), so a workspace sized once fits every later call on the same caches. */

@@ -8,6 +8,10 @@ hipError_t launch_append(const AppendArgs&, int, int, int, int, hipStream_t) { r
 hipError_t launch_decode(const DecodeArgs&, int, int, int, int, hipStream_t) { return hipErrorInvalidValue; }
 hipError_t launch_chunk(const ChunkArgs&, int, int, int, hipStream_t) { return hipErrorInvalidValue; }
 hipError_t launch_merge(const MergeArgs&, hipStream_t) { return hipErrorInvalidValue; }
+hipError_t static_scratch(int, float** ptr) {
+  *ptr = nullptr;
+  return hipErrorInvalidValue;
+}
 const void* decode_kernel_for(int, int, int, int) { return nullptr; }
 const void* chunk_kernel_for(int, int, int, bool) { return nullptr; }
 }  // namespace kvq

@@ -67,6 +67,7 @@ int main(void) {
   int64_t t = 0;
   EXPECT(kv_append_quant(NULL, 0, NULL, NULL, 0, 1, NULL) == KV_EINVAL);
   EXPECT(kv_attend_decode(NULL, 1, 0, NULL, 0, 4, 0.1f, NULL, NULL, 0, NULL) == KV_EINVAL);
+  EXPECT(kv_attend_decode_static(NULL, 1, 0, NULL, 0, 4, 0.1f, NULL, NULL) == KV_EINVAL);
   EXPECT(kv_attend_chunk(NULL, 0, NULL, 0, 4, 1, 0.1f, NULL, NULL, 0, NULL) == KV_EINVAL);
   EXPECT(kv_decode_plan(NULL, 1, 0, 4, &n, &t) == KV_EINVAL);
   EXPECT(kv_chunk_plan(NULL, 0, 4, 1, &n, &t) == KV_EINVAL);

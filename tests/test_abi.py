@@ -99,6 +99,7 @@ def test_null_handles_are_rejected(built_library):
     assert L.kv_session_load(None, None, 0, None) == kvq.KV_EINVAL
     assert L.kv_cache_shape(None, None, None, None, None) == kvq.KV_EINVAL
     assert L.kv_cache_check_guard(None) == kvq.KV_EINVAL
+    assert L.kv_attend_decode_static(None, 1, 0, None, 0, 4, 0.1, None, None) == kvq.KV_EINVAL
 
 
 def test_merge_checks_arguments_on_the_host(built_library):
@@ -190,6 +191,8 @@ def test_binding_checks_tensors_against_the_cache(monkeypatch):
     rejects(kvq.kv_attend_decode, [1], 0, z(1, 8, 128), 0.1, out=z(1, 8, 128), match="float32")
     rejects(kvq.kv_attend_decode, [1], 0, z(1, 8, 128), 0.1, out=z(1, 8, 64, dt=f32), match="shape")
     rejects(kvq.kv_attend_decode, [], 0, z(0, 8, 128), 0.1, match="session")
+    rejects(kvq.kv_attend_decode_static, [1], 0, z(1, 8, 128), 0.1, z(1, 8, 128), match="float32")
+    rejects(kvq.kv_attend_decode_static, [1], 0, z(1, 8, 128), 0.1, z(1, 8, 128, dt=f32), match="device tensor")
     rejects(kvq.kv_attend_decode_partial, [1], 0, z(1, 8, 128), 0.1, 2, 512, partials=z(1, 8, 3, 130, dt=f32),
             match="shape")
     # chunk: q [n_new, n_q_heads, head_dim]
