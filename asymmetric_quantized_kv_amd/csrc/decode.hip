@@ -34,6 +34,7 @@
 #include "kvq_internal.h"
 #include "buffer_ops.h"
 #include "wave_ops.h"
+#include "merge_row.h"
 
 constexpr int kDecodeDepth = 4;   // steps of key/value codes requested ahead of the one computing
 
@@ -90,9 +91,54 @@ __device__ __forceinline__ float load_q(const void* q, int dt, int64_t i) {
   return h2f(b);
 }
 
+// A fused split launch: every workgroup writes its partial (o, m, l) with agent-scope atomic
+// stores and then counts itself on its session's counter for the KV head; the one that brings
+// the count to the number of splits reads all of them back with agent-scope atomic loads and
+// writes the merged rows (out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s, M = max_s m_s;
+// splits with m = -inf drop out), then leaves the counter at zero for the next call.
+// Agent-scope atomic accesses are coherent across the XCDs' separate L2 caches on their own
+// (stores write through, loads read past this L2's lines); a workgroup counts only after its
+// stores have completed (vmcnt(0) ahead of the barrier), and the last one loads only after its
+// count has returned.  That takes the place of a release and an acquire fence, each of which
+// writes back or invalidates the whole L2 here.  One lane does the count, as a vector atomic.
+// A partial's word: an agent-scope atomic store (written through past this XCD's L2), so the
+// merging workgroup of the same launch can read it on any XCD.
+__device__ __forceinline__ void st_partial(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int D>
+__device__ void merge_if_last(const DecodeArgs& a, const SessionRef& S, int64_t srow, int head, int tid, int* s_last) {
+  const int n_s = a.compact ? (int)((S.len + a.tps - 1) / a.tps) : a.n_splits;
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this lane's partial stores have completed
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t before = __hip_atomic_fetch_add(S.counters + head, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int last = before + 1u == (uint32_t)n_s;
+    if (last) __hip_atomic_store(S.counters + head, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *s_last = last;
+  }
+  __syncthreads();
+  if (!*s_last) return;
+  // the same row merge as the standalone merge kernels would run under this plan
+  const float* p0 = a.ws + srow * a.n_splits * (int64_t)(D + 2);
+  float* o0 = a.out + srow * D;
+  if (merge_seq_form(D, a.n_splits)) {
+    constexpr int LPR = D / 8;
+    for (int i = tid; i < a.group * LPR; i += 256)
+      merge_row_seq<D, true>(p0 + (i / LPR) * a.n_splits * (int64_t)(D + 2), n_s, i % LPR, o0 + (i / LPR) * D);
+  } else {
+    for (int g = tid >> 6; g < a.group; g += 4)   // a wave per row, every lane active
+      merge_row_wave<true>(p0 + g * a.n_splits * (int64_t)(D + 2), n_s, D, o0 + g * D, tid & 63);
+  }
+}
+
 // QLO: fp8 keys with fp32 queries, which carry an fp16 low part (16-bit queries are
 // exact in fp16 after the power-of-two prescale)
-template <int KB, int VB, int D, int GP, int E, bool QLO = false>
+// ONE: every wave holds at most one chunk (a split of at most 4 x 128 tokens): all of its key
+// and value codes are requested before the query is prepared, so a small launch pays one
+// memory latency instead of a chain of them.
+template <int KB, int VB, int D, int GP, int E, bool QLO = false, bool ONE = false>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   constexpr int LPT = D / E;           // lanes per token
   constexpr int TPS = 64 / LPT;        // tokens per half step
@@ -118,6 +164,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint32_t s_w[4][CT / 2][GP];  // fp16 p of token pairs
   __shared__ float s_o[4][GP][D];
   __shared__ float s_ml[4][2][GP];
+  __shared__ int s_last;                                   // fused launches: this workgroup merges
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int head = blockIdx.x;
@@ -144,8 +191,9 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     if (a.partial) {
       for (int i = tid; i < a.group * (D + 2); i += 256) {
         const int g = i / (D + 2), e = i % (D + 2);
-        a.ws[((srow + g) * a.n_splits + split) * (D + 2) + e] = e == D ? -INFINITY : 0.f;
+        st_partial(a.ws + ((srow + g) * a.n_splits + split) * (D + 2) + e, e == D ? -INFINITY : 0.f);
       }
+      if (a.fused) merge_if_last<D>(a, S, srow, head, tid, &s_last);
     }
     return;
   }
@@ -154,6 +202,102 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const uint8_t* ks = kc + S.cap * KC;
   const uint8_t* vc = ks + S.cap * KS;
   const uint8_t* vs = vc + S.cap * VC;
+
+  const int sub = lane % LPT, grp = lane / LPT, e0 = sub * E, blk = e0 / kBlock;
+  // Q.K on the matrix cores: 8/4-bit keys (int8 MFMA per 32-element block; 4-bit keys at group
+  // 16 keep the VALU path) and fp8 keys (fp16 MFMA over the widened keys)
+  constexpr bool MQK = KB == 8 || (KB == 4 && GP <= 8);
+  constexpr bool MQF = KB == kF8;
+  constexpr bool MQ = MQK || MQF;
+
+  // ---- the first key (and, for ONE, value) codes go out before the query is prepared ------
+  const uint32_t koff = grp * KC + sub * (KW * 4), ksoff = grp * KS + blk * (KB == kF8 ? 1 : 2);
+  const uint32_t voff = grp * VC + sub * (VW * 4), vsoff = grp * VS + blk * 2;
+  const int64_t n_chunks = te > ts ? (te - ts + CT - 1) / CT : 0;
+  // Load pipeline: step s of a phase uses ring slot s % R, and the codes of the step
+  // PD steps ahead are requested before step s computes.  The last PD steps of phase A
+  // request the first value steps of the chunk, and the last PD steps of phase C the
+  // first key steps of the wave's next chunk, so the pipeline never drains.
+  constexpr int PD = ONE ? NS : (kDecodeDepth < NS ? kDecodeDepth : NS - 1), R = ONE ? NS : PD + 1;
+  static_assert(PD >= 1, "prefetch depth");
+  uint32_t kbuf[R][2][KW], vbuf[R][2][VW];
+  uint16_t kscl[R][2], vscl[R][2];
+  // address = chunk resource + loop-invariant lane offset + constant step offset
+  struct Rsrc { __amdgpu_buffer_rsrc_t kc, ks, vc, vs; };
+  // an empty range (n = 0) makes every load through it return 0 without touching memory
+  auto chunk_rsrc = [&](int64_t c, int n) {
+    const int64_t c0 = ts + c * CT;
+    return Rsrc{make_rsrc(kc + c0 * KC, n * KC), make_rsrc(ks + c0 * KS, n * KS),
+                make_rsrc(vc + c0 * VC, n * VC), make_rsrc(vs + c0 * VS, n * VS)};
+  };
+  auto load_k = [&](const Rsrc& r, int s) {
+    const int slot = s % R;
+    buf_dwords<KW>(r.kc, koff, s * STEP * KC, kbuf[slot][0]);
+    buf_dwords<KW>(r.kc, koff + TPS * KC, s * STEP * KC, kbuf[slot][1]);
+    if constexpr (KB == kF8) {
+      kscl[slot][0] = buf_u8(r.ks, ksoff, s * STEP * KS);
+      kscl[slot][1] = buf_u8(r.ks, ksoff + TPS * KS, s * STEP * KS);
+    } else if constexpr (KB != 16) {
+      kscl[slot][0] = buf_u16(r.ks, ksoff, s * STEP * KS);
+      kscl[slot][1] = buf_u16(r.ks, ksoff + TPS * KS, s * STEP * KS);
+    }
+  };
+  // MFMA key groups: 32 tokens each; lane (r, h) loads token r's bytes 32 b + 16 h .. + 16 of
+  // every block b, and its fp16 scales (a ring of RK groups, PDK groups ahead)
+  constexpr int NG = CT / 32, PDK = ONE ? NG : 2, RK = ONE ? NG : PDK + 1;
+  constexpr int KQW = KB == 8 ? 4 : 2;   // code dwords per lane and block
+  uint32_t kq[MQK ? RK : 1][MQK ? NB : 1][KQW];
+  uint32_t kqs[MQK ? RK : 1][MQK ? (NB + 1) / 2 : 1];
+  const uint32_t kqoff = (lane & 31) * KC + (KB == 8 ? 16 : 8) * (lane >> 5), kqsoff = (lane & 31) * KS;
+  constexpr int KFW = MQF ? D / 8 : 1;   // fp8 code dwords per lane and group
+  uint32_t kf[MQF ? RK : 1][KFW];
+  uint32_t kfs[MQF ? RK : 1];
+  const uint32_t kfoff = (lane & 31) * KC + (D / 2) * (lane >> 5), kfsoff = (lane & 31) * KS;
+  auto load_kg = [&](const Rsrc& r, int j) {
+    if constexpr (MQF) {
+      const int slot = j % RK;
+      buf_dwords<KFW>(r.kc, kfoff, j * 32 * KC, kf[slot]);
+      if constexpr (KS == 4) kfs[slot] = __builtin_amdgcn_raw_buffer_load_b32(r.ks, (int)kfsoff, (int)(j * 32 * KS), 0);
+      else kfs[slot] = buf_u16(r.ks, kfsoff, j * 32 * KS);
+    }
+    if constexpr (MQK) {
+      const int slot = j % RK;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) buf_dwords<KQW>(r.kc, kqoff + (KB == 8 ? 32 : 16) * b, j * 32 * KC, kq[slot][b]);
+      if constexpr (NB == 4) {
+        const u32x2 t = __builtin_amdgcn_raw_buffer_load_b64(r.ks, (int)kqsoff, (int)(j * 32 * KS), 0);
+        kqs[slot][0] = t.x;
+        kqs[slot][1] = t.y;
+      } else {
+        static_assert(NB == 2, "head_dim 64 or 128");
+        kqs[slot][0] = __builtin_amdgcn_raw_buffer_load_b32(r.ks, (int)kqsoff, (int)(j * 32 * KS), 0);
+      }
+    }
+  };
+  auto load_v = [&](const Rsrc& r, int s) {
+    const int slot = s % R;
+    buf_dwords<VW>(r.vc, voff, s * STEP * VC, vbuf[slot][0]);
+    buf_dwords<VW>(r.vc, voff + TPS * VC, s * STEP * VC, vbuf[slot][1]);
+    if constexpr (VB != 16) {
+      vscl[slot][0] = buf_u16(r.vs, vsoff, s * STEP * VS);
+      vscl[slot][1] = buf_u16(r.vs, vsoff + TPS * VS, s * STEP * VS);
+    }
+  };
+  int64_t c = __builtin_amdgcn_readfirstlane(wave);
+  Rsrc rc = chunk_rsrc(c, CT);
+  if (c < n_chunks) {
+    if constexpr (MQ) {
+#pragma unroll
+      for (int j = 0; j < PDK; ++j) load_kg(rc, j);
+    } else {
+#pragma unroll
+      for (int s = 0; s < PD; ++s) load_k(rc, s);
+    }
+    if constexpr (ONE) {
+#pragma unroll
+      for (int s = 0; s < NS; ++s) load_v(rc, s);
+    }
+  }
 
   // ---- query preparation: fp32 copy, then per (head, block) two int8 digits -------
   for (int i = tid; i < GP * D; i += 256) {
@@ -196,7 +340,6 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   }
   __syncthreads();
 
-  const int sub = lane % LPT, grp = lane / LPT, e0 = sub * E, blk = e0 / kBlock;
   uint32_t qa_r[GP][QW], qb_r[GP][QW];
   int corr_a[GP], corr_b[GP];
   float qsc[GP];        // raw score -> base-2 logit, applied once per token in phase B
@@ -256,7 +399,6 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   // block's digit sums is subtracted from each result.
   // (4-bit keys at group 16 keep the VALU path: the corrections do not fit beside 16 heads'
   // accumulators)
-  constexpr bool MQK = KB == 8 || (KB == 4 && GP <= 8);
   constexpr int NQ = (2 * GP + 7) / 8;   // quads of result rows that hold query rows
   i32x4 qA[MQK ? NB : 1];
   int qcorr[MQK && KB == 4 ? NQ : 1][2][MQK && KB == 4 ? NB : 1];   // 8 (256 S_hi + S_lo) per head, block
@@ -304,7 +446,6 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   // widened to fp16 (exactly; the block's power-of-two scale folds into the conversion).
   // Lane (r, h) loads token r's bytes [h D / 2, (h + 1) D / 2); k-step k takes its bytes
   // 8 k .. 8 k + 7 (block (h D / 2 + 8 k) / 32), and the query rows follow that order.
-  constexpr bool MQF = KB == kF8;
   constexpr int NK8 = D / 16;                       // k-steps of one 32-token group
   constexpr int QROWS = QLO ? 2 * GP : GP;
   half8_t qF[MQF ? NK8 : 1];
@@ -323,7 +464,6 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       }
     }
   }
-  constexpr bool MQ = MQK || MQF;
 
   float acc[GP][E];
   float wsum[GP], lsum[GP], m[GP];
@@ -336,89 +476,6 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     for (int e = 0; e < E; ++e) acc[g][e] = 0.f;
   }
 
-  const uint32_t koff = grp * KC + sub * (KW * 4), ksoff = grp * KS + blk * (KB == kF8 ? 1 : 2);
-  const uint32_t voff = grp * VC + sub * (VW * 4), vsoff = grp * VS + blk * 2;
-  const int64_t n_chunks = te > ts ? (te - ts + CT - 1) / CT : 0;
-  // Load pipeline: step s of a phase uses ring slot s % R, and the codes of the step
-  // PD steps ahead are requested before step s computes.  The last PD steps of phase A
-  // request the first value steps of the chunk, and the last PD steps of phase C the
-  // first key steps of the wave's next chunk, so the pipeline never drains.
-  constexpr int PD = kDecodeDepth < NS ? kDecodeDepth : NS - 1, R = PD + 1;
-  static_assert(PD >= 1, "prefetch depth");
-  uint32_t kbuf[R][2][KW], vbuf[R][2][VW];
-  uint16_t kscl[R][2], vscl[R][2];
-  // address = chunk resource + loop-invariant lane offset + constant step offset
-  struct Rsrc { __amdgpu_buffer_rsrc_t kc, ks, vc, vs; };
-  // an empty range (n = 0) makes every load through it return 0 without touching memory
-  auto chunk_rsrc = [&](int64_t c, int n) {
-    const int64_t c0 = ts + c * CT;
-    return Rsrc{make_rsrc(kc + c0 * KC, n * KC), make_rsrc(ks + c0 * KS, n * KS),
-                make_rsrc(vc + c0 * VC, n * VC), make_rsrc(vs + c0 * VS, n * VS)};
-  };
-  auto load_k = [&](const Rsrc& r, int s) {
-    const int slot = s % R;
-    buf_dwords<KW>(r.kc, koff, s * STEP * KC, kbuf[slot][0]);
-    buf_dwords<KW>(r.kc, koff + TPS * KC, s * STEP * KC, kbuf[slot][1]);
-    if constexpr (KB == kF8) {
-      kscl[slot][0] = buf_u8(r.ks, ksoff, s * STEP * KS);
-      kscl[slot][1] = buf_u8(r.ks, ksoff + TPS * KS, s * STEP * KS);
-    } else if constexpr (KB != 16) {
-      kscl[slot][0] = buf_u16(r.ks, ksoff, s * STEP * KS);
-      kscl[slot][1] = buf_u16(r.ks, ksoff + TPS * KS, s * STEP * KS);
-    }
-  };
-  // MFMA key groups: 32 tokens each; lane (r, h) loads token r's bytes 32 b + 16 h .. + 16 of
-  // every block b, and its fp16 scales (a ring of RK groups, PDK groups ahead)
-  constexpr int NG = CT / 32, PDK = 2, RK = PDK + 1;
-  constexpr int KQW = KB == 8 ? 4 : 2;   // code dwords per lane and block
-  uint32_t kq[MQK ? RK : 1][MQK ? NB : 1][KQW];
-  uint32_t kqs[MQK ? RK : 1][MQK ? (NB + 1) / 2 : 1];
-  const uint32_t kqoff = (lane & 31) * KC + (KB == 8 ? 16 : 8) * (lane >> 5), kqsoff = (lane & 31) * KS;
-  constexpr int KFW = MQF ? D / 8 : 1;   // fp8 code dwords per lane and group
-  uint32_t kf[MQF ? RK : 1][KFW];
-  uint32_t kfs[MQF ? RK : 1];
-  const uint32_t kfoff = (lane & 31) * KC + (D / 2) * (lane >> 5), kfsoff = (lane & 31) * KS;
-  auto load_kg = [&](const Rsrc& r, int j) {
-    if constexpr (MQF) {
-      const int slot = j % RK;
-      buf_dwords<KFW>(r.kc, kfoff, j * 32 * KC, kf[slot]);
-      if constexpr (KS == 4) kfs[slot] = __builtin_amdgcn_raw_buffer_load_b32(r.ks, (int)kfsoff, (int)(j * 32 * KS), 0);
-      else kfs[slot] = buf_u16(r.ks, kfsoff, j * 32 * KS);
-    }
-    if constexpr (MQK) {
-      const int slot = j % RK;
-#pragma unroll
-      for (int b = 0; b < NB; ++b) buf_dwords<KQW>(r.kc, kqoff + (KB == 8 ? 32 : 16) * b, j * 32 * KC, kq[slot][b]);
-      if constexpr (NB == 4) {
-        const u32x2 t = __builtin_amdgcn_raw_buffer_load_b64(r.ks, (int)kqsoff, (int)(j * 32 * KS), 0);
-        kqs[slot][0] = t.x;
-        kqs[slot][1] = t.y;
-      } else {
-        static_assert(NB == 2, "head_dim 64 or 128");
-        kqs[slot][0] = __builtin_amdgcn_raw_buffer_load_b32(r.ks, (int)kqsoff, (int)(j * 32 * KS), 0);
-      }
-    }
-  };
-  auto load_v = [&](const Rsrc& r, int s) {
-    const int slot = s % R;
-    buf_dwords<VW>(r.vc, voff, s * STEP * VC, vbuf[slot][0]);
-    buf_dwords<VW>(r.vc, voff + TPS * VC, s * STEP * VC, vbuf[slot][1]);
-    if constexpr (VB != 16) {
-      vscl[slot][0] = buf_u16(r.vs, vsoff, s * STEP * VS);
-      vscl[slot][1] = buf_u16(r.vs, vsoff + TPS * VS, s * STEP * VS);
-    }
-  };
-  int64_t c = __builtin_amdgcn_readfirstlane(wave);
-  Rsrc rc = chunk_rsrc(c, CT);
-  if (c < n_chunks) {
-    if constexpr (MQ) {
-#pragma unroll
-      for (int j = 0; j < PDK; ++j) load_kg(rc, j);
-    } else {
-#pragma unroll
-      for (int s = 0; s < PD; ++s) load_k(rc, s);
-    }
-  }
   for (; c < n_chunks; c += 4) {
     const int64_t c0 = ts + c * CT;
     const bool tail = c0 + CT > te;
@@ -430,7 +487,9 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       constexpr int VPER = (PD + PDK - 1) / PDK;
 #pragma unroll
       for (int j = 0; j < NG; ++j) {
-        if (j + PDK < NG) {
+        if constexpr (ONE) {
+          // every code of the chunk is in flight already
+        } else if (j + PDK < NG) {
           load_kg(rc, j + PDK);
         } else {
 #pragma unroll
@@ -519,8 +578,10 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         const int la = s * STEP + grp, lb = la + TPS;
-        if (s + PD < NS) load_k(rc, s + PD);
-        else load_v(rc, s + PD - NS);
+        if constexpr (!ONE) {
+          if (s + PD < NS) load_k(rc, s + PD);
+          else load_v(rc, s + PD - NS);
+        }
         const uint32_t* ka = kbuf[s % R][0];
         const uint32_t* kb = kbuf[s % R][1];
         float da = 1.f, db = 1.f;
@@ -665,7 +726,9 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     // ---- phase C: values (codes of step s + 1 in flight while step s computes) ---
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      if (s + PD < NS) load_v(rc, s + PD);
+      if constexpr (ONE) {
+        // one chunk per wave: nothing more to request
+      } else if (s + PD < NS) load_v(rc, s + PD);
       else if constexpr (MQ) {   // the next chunk's first PDK key groups (none: an empty range)
         if (s + PD - NS < PDK) load_kg(rn, s + PD - NS);
         if (s == NS - 1) {        // chunks of fewer value steps than PDK + 1: the rest at the end
@@ -729,9 +792,12 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   }
 
   // ---- epilogue: wave partials -> workgroup partial -------------------------------
+  // the lane's sums of its elements e0 .. e0 + E - 1, then one reduce-scatter over the lanes
+  // that share those elements (lane % LPT): each lane ends with GP * D / 64 of the wave's sums
+  constexpr int NV = GP * E, NF = GP * D / 64;
+  float ov[NV];
 #pragma unroll
   for (int g = 0; g < GP; ++g) {
-    const float lw = wave_sum(lsum[g]);
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       float o;
@@ -739,9 +805,21 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         o = ((e & 1) ? acc[g][e] * 1048576.f : (acc[g][e] - acc[g][e + 1]) * 16777216.f) - 8.f * wsum[g];
       else if constexpr (VB == 8) o = acc[g][e] * 16777216.f - 128.f * wsum[g];
       else o = acc[g][e];
-      o = strided_sum<LPT>(o);
-      if (grp == 0) s_o[wave][g][e0 + e] = o;
+      ov[g * E + e] = o;
     }
+  }
+  reduce_scatter<LPT>(ov, lane);
+  {
+    const int first = reduce_scatter_first<LPT, NV>(lane);
+#pragma unroll
+    for (int i = 0; i < NF; ++i) {
+      const int idx = first + i, g = idx / E;
+      s_o[wave][g][e0 + idx % E] = ov[i];
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < GP; ++g) {
+    const float lw = wave_sum(lsum[g]);
     if (lane == 0) {
       s_ml[wave][0][g] = m[g];
       s_ml[wave][1][g] = lw;
@@ -771,26 +849,41 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       a.out[row * D + e] = o / l;
     } else {
       float* p = a.ws + (row * a.n_splits + split) * (D + 2);
-      p[e] = o;
+      st_partial(p + e, o);
       if (e == 0) {
-        p[D] = M;
-        p[D + 1] = l;
+        st_partial(p + D, M);
+        st_partial(p + D + 1, l);
       }
     }
   }
+  if (a.partial && a.fused) merge_if_last<D>(a, S, srow, head, tid, &s_last);
 }
 
 template <int GP>
 constexpr int lane_elems() { return GP <= 2 ? 32 : (GP == 4 ? 16 : 8); }
 
+// The single-chunk variant keeps a whole chunk's key and value codes in registers: only where
+// they take at most 64 registers a lane (and the query group is small) does it fit beside the
+// rest of the kernel.
+template <int KB, int VB, int D, int GP>
+constexpr bool one_chunk_variant() {
+  constexpr int kbytes = KB == 16 ? 2 * D : (KB == 4 ? D / 2 : D), vbytes = VB == 16 ? 2 * D : (VB == 4 ? D / 2 : D);
+  return GP <= 8 && kDecodeChunk * (kbytes + vbytes) / 64 <= 256;
+}
+
 template <int KB, int VB, int D, int GP>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
   constexpr int E = lane_elems<GP>();
   const dim3 grid(a.hkv, a.compact ? a.n_pieces : a.n_sess, a.compact ? 1 : a.n_splits);
-  if (KB == kF8 && a.q_dtype == 0)
-    hipLaunchKernelGGL((decode_kernel<KB, VB, D, GP, E, KB == kF8>), grid, dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL((decode_kernel<KB, VB, D, GP, E>), grid, dim3(256), 0, s, a);
+  const bool one = one_chunk_variant<KB, VB, D, GP>() && a.one_chunk;
+  constexpr bool OK1 = one_chunk_variant<KB, VB, D, GP>();
+  if (KB == kF8 && a.q_dtype == 0) {
+    if (one) hipLaunchKernelGGL((decode_kernel<KB, VB, D, GP, E, KB == kF8, OK1>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((decode_kernel<KB, VB, D, GP, E, KB == kF8>), grid, dim3(256), 0, s, a);
+  } else {
+    if (one) hipLaunchKernelGGL((decode_kernel<KB, VB, D, GP, E, false, OK1>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((decode_kernel<KB, VB, D, GP, E>), grid, dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 

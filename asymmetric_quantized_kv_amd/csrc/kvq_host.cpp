@@ -31,7 +31,9 @@ struct kv_cache {
   int64_t max_tokens;
   std::vector<LayerGeom> lg;
   uint8_t* arena;
-  int64_t bytes;
+  int64_t bytes;          // the planes (the footprint)
+  int64_t counter_off;    // then one uint32 split counter per (layer, KV head), zero between calls
+  int64_t guard_off;      // then kGuardBytes guard bytes
   std::vector<int64_t> len;
   int device;
   bool poisoned;
@@ -143,16 +145,27 @@ constexpr int kMaxSplitsChunk = 64;
 std::mutex g_plan_mu;
 
 // resident workgroups of `kernel` (`threads` per workgroup) on `device`; 0 if unknown
+int g_cus[64];   // compute units per device, 0 until asked, -1 when the query failed
+
+int device_cus_locked(int device) {
+  if (device < 0 || device >= 64) return 0;
+  if (g_cus[device] == 0 && hipDeviceGetAttribute(&g_cus[device], hipDeviceAttributeMultiprocessorCount, device) != hipSuccess) {
+    (void)hipGetLastError();
+    g_cus[device] = -1;
+  }
+  return std::max(g_cus[device], 0);
+}
+
+int device_cus(int device) {
+  std::lock_guard<std::mutex> lk(g_plan_mu);
+  return device_cus_locked(device);
+}
+
 int64_t resident_slots(int device, const void* kernel, int threads = 256) {
-  static int cus[64];
   static std::vector<std::pair<const void*, int>> per_cu;
   std::lock_guard<std::mutex> lk(g_plan_mu);
-  if (device < 0 || device >= 64) return 0;
-  if (cus[device] == 0 && hipDeviceGetAttribute(&cus[device], hipDeviceAttributeMultiprocessorCount, device) != hipSuccess) {
-    (void)hipGetLastError();
-    cus[device] = -1;
-  }
-  if (cus[device] <= 0) return 0;
+  const int cus = device_cus_locked(device);
+  if (cus <= 0) return 0;
   int n = -1;
   for (auto& e : per_cu)
     if (e.first == kernel) n = e.second;
@@ -164,7 +177,7 @@ int64_t resident_slots(int device, const void* kernel, int threads = 256) {
     per_cu.emplace_back(kernel, std::max(n, 1));
     n = std::max(n, 1);
   }
-  return (int64_t)cus[device] * n;
+  return (int64_t)cus * n;
 }
 
 int64_t split_cap(int64_t base, int64_t slots, int64_t hard_cap) {
@@ -284,15 +297,17 @@ kv_cache* kv_cache_create_layered(const int* layouts, int n_layers, int n_kv_hea
     fail(KV_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
     return nullptr;
   }
+  const int64_t counter_off = round_up(bytes, 256);
+  const int64_t guard_off = counter_off + round_up(4 * (int64_t)n_layers * n_kv_heads, 256);
   void* p = nullptr;
-  e = hipMalloc(&p, (size_t)(bytes + kGuardBytes));
+  e = hipMalloc(&p, (size_t)(guard_off + kGuardBytes));
   if (e != hipSuccess || !p) {
     (void)hipGetLastError();
-    fail(KV_ENOMEM, "hipMalloc of %lld bytes failed: %s", (long long)(bytes + kGuardBytes), hipGetErrorString(e));
+    fail(KV_ENOMEM, "hipMalloc of %lld bytes failed: %s", (long long)(guard_off + kGuardBytes), hipGetErrorString(e));
     return nullptr;
   }
-  e = hipMemset(p, 0, (size_t)bytes);
-  if (e == hipSuccess) e = hipMemset(static_cast<uint8_t*>(p) + bytes, kGuardByte, kGuardBytes);
+  e = hipMemset(p, 0, (size_t)guard_off);
+  if (e == hipSuccess) e = hipMemset(static_cast<uint8_t*>(p) + guard_off, kGuardByte, kGuardBytes);
   if (e != hipSuccess) {
     (void)hipFree(p);
     fail(KV_EHIP, "hipMemset: %s", hipGetErrorString(e));
@@ -306,6 +321,8 @@ kv_cache* kv_cache_create_layered(const int* layouts, int n_layers, int n_kv_hea
   c->lg = std::move(lg);
   c->arena = static_cast<uint8_t*>(p);
   c->bytes = bytes;
+  c->counter_off = counter_off;
+  c->guard_off = guard_off;
   c->len.assign(n_layers, 0);
   c->device = dev;
   c->poisoned = false;
@@ -343,7 +360,7 @@ int kv_cache_check_guard(const kv_cache* cache) {
   if (rc) return rc;
   uint8_t g[kGuardBytes];
   hipError_t e = hipDeviceSynchronize();
-  if (e == hipSuccess) e = hipMemcpy(g, cache->arena + cache->bytes, (size_t)kGuardBytes, hipMemcpyDeviceToHost);
+  if (e == hipSuccess) e = hipMemcpy(g, cache->arena + cache->guard_off, (size_t)kGuardBytes, hipMemcpyDeviceToHost);
   if (e != hipSuccess) return hip_fail(const_cast<kv_cache*>(cache), e, "guard read");
   for (int64_t i = 0; i < kGuardBytes; ++i)
     if (g[i] != kGuardByte)
@@ -712,7 +729,7 @@ bool decode_compact(int n_sessions, int n_splits, const int32_t* n_valid) {
 
 int decode_launch(kv_cache* const* sessions, int n_sessions, int layer, const DecodePrep& p, const void* q,
                   int q_dtype, int n_q_heads, float sm_scale, int n_splits, int64_t tps, bool partial, float* ws,
-                  float* out, hipStream_t st, bool compact = false) {
+                  float* out, hipStream_t st, bool compact = false, bool fused = false) {
   DecodeArgs a;
   memset(&a, 0, sizeof(a));
   a.hkv = p.hkv;
@@ -720,6 +737,7 @@ int decode_launch(kv_cache* const* sessions, int n_sessions, int layer, const De
   a.group = p.group;
   a.n_splits = n_splits;
   a.partial = partial ? 1 : 0;
+  a.fused = partial && fused ? 1 : 0;
   a.tps = tps;
   a.q = q;
   a.q_dtype = q_dtype;
@@ -738,6 +756,7 @@ int decode_launch(kv_cache* const* sessions, int n_sessions, int layer, const De
       const int r = order[b0 + i];
       const kv_cache* c = sessions[r];
       a.sess[i].base = layer_base(c, layer);
+      a.sess[i].counters = reinterpret_cast<uint32_t*>(c->arena + c->counter_off) + (int64_t)layer * c->hkv;
       a.sess[i].cap = c->lg[layer].g.cap;
       a.sess[i].len = c->len[layer];
       a.sess[i].row = (int32_t)r;
@@ -748,6 +767,10 @@ int decode_launch(kv_cache* const* sessions, int n_sessions, int layer, const De
       a.sess[i].piece0 = a.n_pieces;
       a.n_pieces += (int32_t)ceil_div(std::max<int64_t>(a.sess[i].len, 1), tps);
     }
+    // a launch of one round (a workgroup per compute unit at most) whose waves each hold a
+    // single chunk is latency-bound: it takes the variant that requests all codes up front
+    const int64_t wgs = (int64_t)a.hkv * (compact ? a.n_pieces : (int64_t)nb * n_splits);
+    a.one_chunk = tps <= kDecodeWaveTokens && wgs <= device_cus(p.device) ? 1 : 0;
     hipError_t e = launch_decode(a, p.kbits, p.vbits, p.d, p.gp, st);
     if (e != hipSuccess) {
       for (int i = 0; i < n_sessions; ++i) sessions[i]->poisoned = true;
@@ -905,16 +928,24 @@ int decode_run(kv_cache* const* sessions, int n_sessions, int layer, const Decod
   int32_t n_valid[kMaxSessions];
   for (int i = 0; i < n_sessions && i < kMaxSessions; ++i) n_valid[i] = (int32_t)ceil_div(std::max<int64_t>(p.lens[i], 1), tps);
   const bool compact = decode_compact(n_sessions, n_splits, n_valid);
-  int rc = decode_launch(sessions, n_sessions, layer, p, q, q_dtype, n_q_heads, sm_scale, n_splits, tps, n_splits > 1,
-                         ws, out, st, compact);
-  if (rc) return rc;
+  // Split partials and their merge in one launch: the last workgroup of each (session, KV
+  // head) to finish merges.  Its split counters live in the session's arena, so launches of
+  // more than kMaxSessions sessions stay independent; a cache passed twice in one call would
+  // share its counters between two rows and takes the separate merge instead.
+  bool repeated = false;
   if (n_splits > 1) {
-    hipError_t e = merge_launch(ws, (int64_t)n_sessions * n_q_heads, n_splits, p.d, out, st,
-                                compact ? n_q_heads : 0, compact ? n_valid : nullptr);
-    if (e != hipSuccess) {
-      for (int i = 0; i < n_sessions; ++i) sessions[i]->poisoned = true;
-      return fail(KV_EHIP, "merge launch: %s", hipGetErrorString(e));
-    }
+    std::vector<const kv_cache*> seen(sessions, sessions + n_sessions);
+    std::sort(seen.begin(), seen.end());
+    repeated = std::adjacent_find(seen.begin(), seen.end()) != seen.end();
+  }
+  int rc = decode_launch(sessions, n_sessions, layer, p, q, q_dtype, n_q_heads, sm_scale, n_splits, tps, n_splits > 1,
+                         ws, out, st, compact, /*fused=*/!repeated);
+  if (rc || !repeated) return rc;
+  hipError_t e = merge_launch(ws, (int64_t)n_sessions * n_q_heads, n_splits, p.d, out, st,
+                              compact ? n_q_heads : 0, compact ? n_valid : nullptr);
+  if (e != hipSuccess) {
+    for (int i = 0; i < n_sessions; ++i) sessions[i]->poisoned = true;
+    return fail(KV_EHIP, "merge launch: %s", hipGetErrorString(e));
   }
   return KV_OK;
 }

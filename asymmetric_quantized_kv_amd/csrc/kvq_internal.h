@@ -49,6 +49,7 @@ struct AppendArgs {
 
 struct SessionRef {
   const uint8_t* base;    // arena + layer * Hkv * region of this session
+  uint32_t* counters;     // fused launches: the session's split counters of the layer, one per KV head
   int64_t cap;
   int64_t len;
   int32_t row;            // index of the session in the call (rows of q / out / workspace)
@@ -65,6 +66,13 @@ struct DecodeArgs {
   // i's busy splits are pieces sess[i].piece0 .. + ceil(len / tps) - 1 of n_pieces; a split
   // past a session's end then has no workgroup and no partial
   int compact, n_pieces;
+  // fused != 0 (with partial): the last workgroup of each (session, KV head) to finish merges
+  // that head's partials into out, found with the session's split counter for the head (left
+  // at zero between calls)
+  int fused;
+  // one_chunk != 0: tps <= kDecodeWaveTokens (each wave holds at most one chunk) and the grid
+  // fits the device at one workgroup per compute unit
+  int one_chunk;
   int q_dtype;
   int64_t tps;            // tokens per split, multiple of kDecodeWaveTokens
   const void* q;

@@ -64,16 +64,54 @@ __device__ __forceinline__ float wave_sum(float x) {
   return (readlane(x, 0) + readlane(x, 16)) + (readlane(x, 32) + readlane(x, 48));
 }
 
-// Sum over the lanes that share (lane % N), N = 1, 2, 4, 8, 16 (strided groups).
-template <int N>
-__device__ __forceinline__ float strided_sum(float x) {
-  if constexpr (N <= 1) x += dpp<kDppRor(1)>(x);
-  if constexpr (N <= 2) x += dpp<kDppRor(2)>(x);
-  if constexpr (N <= 4) x += dpp<kDppRor(4)>(x);
-  if constexpr (N <= 8) x += dpp<kDppRor(8)>(x);
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
+// Reduce-scatter over the lanes that share lane % LPT (LPT = 2, 4, 8, 16): every lane
+// brings V values, and afterwards v[0 .. V * LPT / 64) of lane l hold sums over its
+// 64 / LPT lanes, of the original indices reduce_scatter_first<LPT, V>(l) + i.  Each step
+// halves the values a lane keeps: at distance DIST (32, 16, ..., LPT) the lane keeps the
+// lower half if (lane & DIST) == 0, else the upper half, and adds its partner's copy of it.
+// The two cross-row steps are one v_permlane32_swap / v_permlane16_swap per pair (the swap
+// trades the upper 32 lanes (odd rows) of the first operand for the lower 32 lanes (even
+// rows) of the second), the steps inside a row a DPP or swizzle move.
+template <int DIST>
+__device__ __forceinline__ float fold_pair(float x, float y, int lane) {
+  if constexpr (DIST == 32 || DIST == 16) {
+    const auto r = DIST == 32 ? __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false)
+                              : __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+    // lanes with (lane & DIST) == 0: own x + partner's x; the others: partner's y + own y
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  } else {
+    const bool hi = lane & DIST;
+    const float keep = hi ? y : x, send = hi ? x : y;
+    float got;
+    if constexpr (DIST == 8) got = dpp<kDppRor(8)>(send);          // rotating a row by 8 pairs l with l ^ 8
+    else if constexpr (DIST == 2) got = dpp<kDppXor2>(send);
+    else got = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(send), 0x1F | (DIST << 10)));  // bit mode: l ^ DIST
+    return keep + got;
+  }
+}
+
+template <int DIST, int LPT, int N, int V>
+__device__ __forceinline__ void reduce_scatter_step(float (&v)[V], int lane) {
+  if constexpr (DIST >= LPT) {
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) v[i] = fold_pair<DIST>(v[i], v[i + N / 2], lane);
+    reduce_scatter_step<DIST / 2, LPT, N / 2>(v, lane);
+  }
+}
+
+template <int LPT, int V>
+__device__ __forceinline__ void reduce_scatter(float (&v)[V], int lane) {
+  static_assert(LPT >= 2 && LPT <= 16 && V * LPT % 64 == 0, "reduce_scatter shape");
+  reduce_scatter_step<32, LPT, V>(v, lane);
+}
+
+template <int LPT, int V>
+__device__ __forceinline__ int reduce_scatter_first(int lane) {
+  int first = 0, n = V;
+#pragma unroll
+  for (int dist = 32; dist >= LPT; dist /= 2, n /= 2)
+    if (lane & dist) first += n / 2;
+  return first;
 }
 
 // Order LDS traffic between the lanes of one wave (no workgroup barrier).

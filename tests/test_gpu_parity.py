@@ -194,6 +194,37 @@ def test_decode_more_sessions_than_one_launch():
             kvq.kv_cache_destroy(h)
 
 
+def test_decode_same_cache_twice_in_one_call():
+    """A cache listed twice in one call (two queries over the same context) next to another
+    cache: each row must match the oracle, and a second call must too (the split merge's
+    per-head state is back at rest)."""
+    log("decode with a repeated cache")
+    d, hkv, g = 128, 2, 4
+    lens = [3000, 1500]
+    hs, ocs = [], []
+    try:
+        for i, n in enumerate(lens):
+            k, v, _ = I.workload_small(820 + i, n, hkv, d, hkv * g, 1, bf16=True, n_outliers=4)
+            h = kvq.kv_cache_create("K8V4", 1, hkv, d, n)
+            kvq.kv_append_quant(h, 0, dev(k, "bf16"), dev(v, "bf16"))
+            oc = O.OracleCache(O.LAYOUT_IDS["K8V4"], 1, hkv, d, n)
+            oc.append(0, host_inputs(k, "bf16"), host_inputs(v, "bf16"))
+            hs.append(h)
+            ocs.append(oc)
+        order = [0, 1, 0]
+        for rep in range(2):
+            q = I.bf16_round(I.normal((len(order), hkv * g, d), 830 + rep, 9))
+            out = kvq.kv_attend_decode([hs[i] for i in order], 0, dev(q, "bf16"), d ** -0.5)
+            want = O.attend_decode([ocs[i] for i in order], 0, host_inputs(q, "bf16"), d ** -0.5)
+            err = max_err(out, want)
+            log(f"  call {rep}: max err {err:.3e}")
+            assert err <= TOL
+    finally:
+        torch_mod().cuda.synchronize()
+        for h in hs:
+            kvq.kv_cache_destroy(h)
+
+
 def test_decode_128_tokens_exact_workload():
     log("decode 128 tokens")
     c = I.decode_128_tokens()
