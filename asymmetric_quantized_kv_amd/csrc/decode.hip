@@ -167,7 +167,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   __shared__ int s_last;                                   // fused launches: this workgroup merges
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int head = blockIdx.x;
+  const int vhead = blockIdx.x, head = vhead / a.hsplit;   // the workgroup's part of KV head `head`
   int sl = blockIdx.y, split = blockIdx.z;
   // the full grid's session, read before the launch kind is known (no wait on a.compact
   // first: the empty asm keeps the compiler from sinking these loads past the branch)
@@ -183,7 +183,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     sl = lo;
     S = a.sess[sl];
   }
-  const int64_t srow = S.row * a.hq + (int64_t)head * a.group;  // first q row
+  const int64_t srow = S.row * a.hq + (int64_t)vhead * a.group;  // first q row
   const int64_t ts = (int64_t)split * a.tps;
   const int64_t te = min(ts + a.tps, S.len);
   if (ts >= S.len) {
@@ -193,7 +193,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         const int g = i / (D + 2), e = i % (D + 2);
         st_partial(a.ws + ((srow + g) * a.n_splits + split) * (D + 2) + e, e == D ? -INFINITY : 0.f);
       }
-      if (a.fused) merge_if_last<D>(a, S, srow, head, tid, &s_last);
+      if (a.fused) merge_if_last<D>(a, S, srow, vhead, tid, &s_last);
     }
     return;
   }
@@ -856,7 +856,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       }
     }
   }
-  if (a.partial && a.fused) merge_if_last<D>(a, S, srow, head, tid, &s_last);
+  if (a.partial && a.fused) merge_if_last<D>(a, S, srow, vhead, tid, &s_last);
 }
 
 template <int GP>
@@ -874,7 +874,7 @@ constexpr bool one_chunk_variant() {
 template <int KB, int VB, int D, int GP>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
   constexpr int E = lane_elems<GP>();
-  const dim3 grid(a.hkv, a.compact ? a.n_pieces : a.n_sess, a.compact ? 1 : a.n_splits);
+  const dim3 grid(a.hkv * a.hsplit, a.compact ? a.n_pieces : a.n_sess, a.compact ? 1 : a.n_splits);
   const bool one = one_chunk_variant<KB, VB, D, GP>() && a.one_chunk;
   constexpr bool OK1 = one_chunk_variant<KB, VB, D, GP>();
   if (KB == kF8 && a.q_dtype == 0) {

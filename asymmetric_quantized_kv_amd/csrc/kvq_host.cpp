@@ -32,7 +32,7 @@ struct kv_cache {
   std::vector<LayerGeom> lg;
   uint8_t* arena;
   int64_t bytes;          // the planes (the footprint)
-  int64_t counter_off;    // then one uint32 split counter per (layer, KV head), zero between calls
+  int64_t counter_off;    // then kMaxHeadSplit uint32 split counters per (layer, KV head), zero between calls
   int64_t guard_off;      // then kGuardBytes guard bytes
   std::vector<int64_t> len;
   int device;
@@ -298,7 +298,7 @@ kv_cache* kv_cache_create_layered(const int* layouts, int n_layers, int n_kv_hea
     return nullptr;
   }
   const int64_t counter_off = round_up(bytes, 256);
-  const int64_t guard_off = counter_off + round_up(4 * (int64_t)n_layers * n_kv_heads, 256);
+  const int64_t guard_off = counter_off + round_up(4 * (int64_t)n_layers * n_kv_heads * kMaxHeadSplit, 256);
   void* p = nullptr;
   e = hipMalloc(&p, (size_t)(guard_off + kGuardBytes));
   if (e != hipSuccess || !p) {
@@ -675,6 +675,7 @@ int decode_prepare(kv_cache* const* sessions, int n_sessions, int layer, int n_q
 // splits past its end exit at once.  With lengths that differ a lot, many splits let the
 // long sessions spread over the device while short ones take one workgroup each.
 constexpr int64_t kDecodeWgFixedTokens = 256;   // per-workgroup overhead, in streamed tokens
+constexpr int kMinSplitGroup = 2;               // query heads a workgroup keeps when a head's group is split
 
 int64_t decode_split_cap(const DecodePrep& p) {
   const int64_t slots = p.slots > 0 ? p.slots : 1024;
@@ -756,7 +757,7 @@ int decode_launch(kv_cache* const* sessions, int n_sessions, int layer, const De
       const int r = order[b0 + i];
       const kv_cache* c = sessions[r];
       a.sess[i].base = layer_base(c, layer);
-      a.sess[i].counters = reinterpret_cast<uint32_t*>(c->arena + c->counter_off) + (int64_t)layer * c->hkv;
+      a.sess[i].counters = reinterpret_cast<uint32_t*>(c->arena + c->counter_off) + (int64_t)layer * c->hkv * kMaxHeadSplit;
       a.sess[i].cap = c->lg[layer].g.cap;
       a.sess[i].len = c->len[layer];
       a.sess[i].row = (int32_t)r;
@@ -767,11 +768,21 @@ int decode_launch(kv_cache* const* sessions, int n_sessions, int layer, const De
       a.sess[i].piece0 = a.n_pieces;
       a.n_pieces += (int32_t)ceil_div(std::max<int64_t>(a.sess[i].len, 1), tps);
     }
-    // a launch of one round (a workgroup per compute unit at most) whose waves each hold a
-    // single chunk is latency-bound: it takes the variant that requests all codes up front
+    // A launch of one round (a workgroup per compute unit at most) is latency-bound: it splits
+    // each KV head's query group over up to kMaxHeadSplit workgroups while they still fit (each
+    // reads the head's codes; the chain of work per workgroup shrinks), and if its waves hold a
+    // single chunk each, takes the variant that requests all codes up front.
     const int64_t wgs = (int64_t)a.hkv * (compact ? a.n_pieces : (int64_t)nb * n_splits);
-    a.one_chunk = tps <= kDecodeWaveTokens && wgs <= device_cus(p.device) ? 1 : 0;
-    hipError_t e = launch_decode(a, p.kbits, p.vbits, p.d, p.gp, st);
+    const int64_t cus = device_cus(p.device);
+    a.hsplit = 1;
+    for (int hs = kMaxHeadSplit; hs > 1; hs /= 2)
+      if (p.group % hs == 0 && p.group / hs >= kMinSplitGroup && wgs * hs <= cus) {
+        a.hsplit = hs;
+        break;
+      }
+    a.group = p.group / a.hsplit;
+    a.one_chunk = tps <= kDecodeWaveTokens && wgs * a.hsplit <= cus ? 1 : 0;
+    hipError_t e = launch_decode(a, p.kbits, p.vbits, p.d, decode_group_pad(a.group), st);
     if (e != hipSuccess) {
       for (int i = 0; i < n_sessions; ++i) sessions[i]->poisoned = true;
       return fail(KV_EHIP, "decode launch: %s", hipGetErrorString(e));

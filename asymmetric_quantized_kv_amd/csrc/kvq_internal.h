@@ -11,6 +11,7 @@ constexpr int kGranule = 256;       // capacity granule (tokens)
 constexpr int kMaxSessions = 64;    // sessions per decode launch (kernel-argument table)
 constexpr int kDecodeChunk = 128;   // tokens one wave scores before its softmax update
 constexpr int kDecodeWaveTokens = 4 * kDecodeChunk;  // split granularity of decode
+constexpr int kMaxHeadSplit = 2;    // decode workgroups per KV head at most (see DecodeArgs::hsplit)
 constexpr int kChunkThreads = 768;  // threads per chunk-prefill workgroup: 8 consumer + 4 producer waves
 constexpr int kChunkRows = 256;     // query rows per chunk-prefill workgroup (32 per consumer wave)
 constexpr int kChunkKeys = 64;      // keys per chunk-prefill tile
@@ -70,6 +71,10 @@ struct DecodeArgs {
   // that head's partials into out, found with the session's split counter for the head (left
   // at zero between calls)
   int fused;
+  // hsplit: workgroups per KV head (1 or kMaxHeadSplit = 2); workgroup part j of KV head h takes query
+  // heads j * group .. (j + 1) * group - 1 of the head's group (group = the KV head's group /
+  // hsplit), and grid x = hkv * hsplit
+  int hsplit;
   // one_chunk != 0: tps <= kDecodeWaveTokens (each wave holds at most one chunk) and the grid
   // fits the device at one workgroup per compute unit
   int one_chunk;
