@@ -50,7 +50,7 @@ struct AppendArgs {
 
 struct SessionRef {
   const uint8_t* base;    // arena + layer * Hkv * region of this session
-  uint32_t* counters;     // fused launches: the session's split counters of the layer, one per KV head
+  uint32_t* counters;     // fused launches: the session's split counters of the layer, kMaxHeadSplit per KV head
   int64_t cap;
   int64_t len;
   int32_t row;            // index of the session in the call (rows of q / out / workspace)

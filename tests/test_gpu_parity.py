@@ -76,6 +76,29 @@ def test_append_codec_edge_cases(layout):
         assert_planes_equal(h, oc, 0)
 
 
+@pytest.mark.parametrize("layout", ["K8V4", "K4V8"])
+def test_append_infinite_elements(layout):
+    """Blocks holding +-inf saturate their scale at 65504 and the infinities take the
+    clamped code (the block's other elements their quotient by 65504), as in the format;
+    the neighbouring blocks of the same row are unaffected."""
+    rng = np.random.default_rng(31)
+    rows = rng.standard_normal((6, 64)).astype(np.float32) * np.float32(3.0)
+    rows[0, 5] = np.inf
+    rows[1, 40] = -np.inf
+    rows[2, 0], rows[2, 31] = np.inf, -np.inf
+    rows[3, 33:40] = np.float32(7e4)           # a finite block whose scale saturates too
+    rows[3, 34] = np.inf
+    rows[4, :32] = 0.0
+    rows[4, 7] = -np.inf
+    k = rows[:, None, :]
+    v = rows[::-1, None, :].copy()
+    oc = O.OracleCache(O.LAYOUT_IDS[layout], 1, 1, 64, len(rows))
+    oc.append(0, k, v)
+    with gpu_cache(layout, 1, 1, 64, len(rows)) as h:
+        kvq.kv_append_quant(h, 0, dev(k, "f32"), dev(v, "f32"))
+        assert_planes_equal(h, oc, 0)
+
+
 def _mx_edge_rows():
     """Rows of two 32-element blocks, values y * 2^e on E4M3's grid and its midpoints:
     ties to even (normal and subnormal), the 448 saturation, -0, an all-zero block, and
