@@ -32,6 +32,7 @@
 // accumulators rare.
 #include "kvq_internal.h"
 #include "buffer_ops.h"
+#include "wave_ops.h"
 
 #include <type_traits>
 
@@ -74,6 +75,21 @@ __device__ __forceinline__ float swap32_max(float x) {
 __device__ __forceinline__ float swap32_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Power-of-two prescale of a wave's query rows, lane_amax being the largest |q| among this
+// lane's elements: returns 2^(127 - sb), which puts the wave's largest |q| in [2^14, 2^15),
+// and sets *score_scale = qk_scale 2^(sb - 127).  Both are wave-uniform; the score scale is
+// formed by adding to qk_scale's exponent field (integer work on scalar registers), so sb is
+// clamped to keep that exponent normal (a query needs it only beyond 2^100 or below 2^-100),
+// and a zero, subnormal or non-finite qk_scale takes no prescale.
+__device__ __forceinline__ float wave_prescale(float lane_amax, float qk_scale, float* score_scale) {
+  const uint32_t qb = __float_as_uint(qk_scale);
+  const int eq = (int)((qb >> 23) & 255);
+  int sb = max((int)((__float_as_uint(wave_max(lane_amax)) >> 23) & 255) - 14, 1);
+  sb = eq == 0 || eq == 255 ? 127 : min(max(sb, 128 - eq), 381 - eq);
+  *score_scale = __uint_as_float(qb + ((uint32_t)(sb - 127) << 23));
+  return __uint_as_float((uint32_t)(254 - sb) << 23);
 }
 
 // four fp16 values / 2^t as four E4M3 bytes (the conversion divides by its scale operand)
@@ -374,9 +390,13 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(ChunkArgs a) {
   const int64_t pos = valid ? base_pos + tok : -1;
   const bool wave_active = r0 < rows;
 
-  // Q^T as the B operand: lane (col, hl) holds d = 16 k + 8 hl .. + 7 of its row.
+  // Q^T as the B operand: lane (col, hl) holds d = 16 k + 8 hl .. + 7 of its row.  The wave's
+  // rows are first scaled by a power of two 2^-k that puts their largest |q| in [2^14, 2^15),
+  // so fp16 holds them for any magnitude (16-bit queries exactly); 2^k goes into the score
+  // scale, one for the wave.
   half8_t qv[NKS];
   half8_t ql[QSPLIT ? NKS : 1];
+  float qks;   // raw score -> base-2 logit (wave-uniform)
   {
     // 8 consecutive elements per k-step: one 16-byte load each (two for fp32), all issued
     // before the first conversion
@@ -389,14 +409,20 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(ChunkArgs a) {
         raw[2 * k] = valid ? src[4 * k] : make_float4(0.f, 0.f, 0.f, 0.f);
         raw[2 * k + 1] = valid ? src[4 * k + 1] : make_float4(0.f, 0.f, 0.f, 0.f);
       }
+      float am = 0.f;
+#pragma unroll
+      for (int k = 0; k < 2 * NKS; ++k)
+        am = fmaxf(am, fmaxf(fmaxf(fabsf(raw[k].x), fabsf(raw[k].y)), fmaxf(fabsf(raw[k].z), fabsf(raw[k].w))));
+      const float qi = wave_prescale(am, a.qk_scale, &qks);
 #pragma unroll
       for (int k = 0; k < NKS; ++k) {
         const float x[8] = {raw[2 * k].x, raw[2 * k].y, raw[2 * k].z, raw[2 * k].w,
                             raw[2 * k + 1].x, raw[2 * k + 1].y, raw[2 * k + 1].z, raw[2 * k + 1].w};
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          qv[k][i] = (_Float16)x[i];
-          ql[k][i] = (_Float16)(x[i] - (float)qv[k][i]);
+          const float y = x[i] * qi;
+          qv[k][i] = (_Float16)y;
+          ql[k][i] = (_Float16)(y - (float)qv[k][i]);
         }
       }
     } else {                  // bf16 or fp16 queries
@@ -405,13 +431,24 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(ChunkArgs a) {
 #pragma unroll
       for (int k = 0; k < NKS; ++k) raw[k] = valid ? src[2 * k] : make_uint4(0u, 0u, 0u, 0u);
       const bool bf = a.q_dtype == 1;
+      // the largest magnitude from the bits: without the sign, bf16 and fp16 magnitudes
+      // order as their bit patterns
+      uint32_t mb = 0;
+#pragma unroll
+      for (int k = 0; k < NKS; ++k) {
+        const uint32_t w[4] = {raw[k].x, raw[k].y, raw[k].z, raw[k].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) mb = max(mb, max(w[j] & 0x7fffu, (w[j] >> 16) & 0x7fffu));
+      }
+      const float qi = wave_prescale(bf ? __uint_as_float(mb << 16) : (float)__builtin_bit_cast(_Float16, (uint16_t)mb),
+                                     a.qk_scale, &qks);
 #pragma unroll
       for (int k = 0; k < NKS; ++k) {
         const uint32_t w[4] = {raw[k].x, raw[k].y, raw[k].z, raw[k].w};
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const uint16_t b = (uint16_t)(w[i / 2] >> (16 * (i & 1)));
-          qv[k][i] = bf ? (_Float16)__uint_as_float((uint32_t)b << 16) : __builtin_bit_cast(_Float16, b);
+          qv[k][i] = (_Float16)((bf ? __uint_as_float((uint32_t)b << 16) : (float)__builtin_bit_cast(_Float16, b)) * qi);
         }
       }
     }
@@ -556,7 +593,7 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(ChunkArgs a) {
     float mx = sv[0];
 #pragma unroll
     for (int v = 1; v < 16; ++v) mx = fmaxf(mx, sv[v]);
-    mx = swap32_max(mx) * a.qk_scale;
+    mx = swap32_max(mx) * qks;
     const bool move = mx > m + kLazyMax;
     if (__any(move)) {
       const float mn = move ? mx : m;
@@ -573,8 +610,8 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(ChunkArgs a) {
 #pragma unroll
     for (int v = 0; v < 16; v += 2) {
       half2_t pp;
-      pp.x = (_Float16)__builtin_amdgcn_exp2f(fmaf(sv[v], a.qk_scale, -mu));
-      pp.y = (_Float16)__builtin_amdgcn_exp2f(fmaf(sv[v + 1], a.qk_scale, -mu));
+      pp.x = (_Float16)__builtin_amdgcn_exp2f(fmaf(sv[v], qks, -mu));
+      pp.y = (_Float16)__builtin_amdgcn_exp2f(fmaf(sv[v + 1], qks, -mu));
       l = __builtin_amdgcn_fdot2(pp, hconst(1.f), l, false);   // sum of the rounded weights
       pb[v >> 3][v & 7] = pp.x;
       pb[v >> 3][(v & 7) + 1] = pp.y;

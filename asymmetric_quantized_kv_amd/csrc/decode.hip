@@ -133,7 +133,7 @@ __device__ void merge_if_last(const DecodeArgs& a, const SessionRef& S, int64_t 
   }
 }
 
-// QLO: fp8 keys with fp32 queries, which carry an fp16 low part (16-bit queries are
+// QLO: fp8 or fp16 keys with fp32 queries, which carry an fp16 low part (16-bit queries are
 // exact in fp16 after the power-of-two prescale)
 // ONE: every wave holds at most one chunk (a split of at most 4 x 128 tokens): all of its key
 // and value codes are requested before the query is prepared, so a small launch pays one
@@ -157,7 +157,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 
   __shared__ float s_q[GP][D];
   __shared__ float s_qs[GP];
-  __shared__ float s_qi[GP];                               // fp8 keys: power-of-two query prescale
+  __shared__ float s_qi[GP];                               // fp8 / fp16 keys: power-of-two query prescale
   __shared__ __attribute__((aligned(16))) int8_t s_qa[GP][D];
   __shared__ __attribute__((aligned(16))) int8_t s_qb[GP][D];
   __shared__ float s_sc[4][CT][GP];                        // raw scores of a chunk
@@ -309,9 +309,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   // the integer dot products then carry 16 bits of the query
   // (wave w prepares heads w, w + 4, ...: lanes split the elements, a DPP max gives amax)
   for (int g = wave; g < GP; g += 4) {
-    if constexpr (KB == 16) {
-      if (lane == 0) s_qs[g] = a.qk_scale;
-    } else if constexpr (KB == kF8) {
+    if constexpr (KB == 16 || KB == kF8) {
       // q' = q * 2^-k with max |q'| in [2^14, 2^15): fp16 holds q' without overflow and
       // 16-bit queries exactly
       float amax = 0.f;
@@ -348,11 +346,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     qsc[g] = s_qs[g];
     corr_a[g] = 0;
     corr_b[g] = 0;
-    if constexpr (KB == 16) {
-#pragma unroll
-      for (int j = 0; j < QW; ++j)
-        qa_r[g][j] = __builtin_bit_cast(uint32_t, pack_rne(s_q[g][e0 + 2 * j], s_q[g][e0 + 2 * j + 1]));
-    } else if constexpr (KB == kF8) {
+    if constexpr (KB == 16 || KB == kF8) {
       const float qi = s_qi[g];
 #pragma unroll
       for (int j = 0; j < QW; ++j) {
@@ -610,6 +604,13 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
             for (int j = 0; j < KW; ++j) {
               xa = __builtin_amdgcn_fdot2(as_h2(qa_r[g][j]), as_h2(ka[j]), xa, false);
               xb = __builtin_amdgcn_fdot2(as_h2(qa_r[g][j]), as_h2(kb[j]), xb, false);
+            }
+            if constexpr (QLO) {
+#pragma unroll
+              for (int j = 0; j < KW; ++j) {
+                xa = __builtin_amdgcn_fdot2(as_h2(qb_r[g][j]), as_h2(ka[j]), xa, false);
+                xb = __builtin_amdgcn_fdot2(as_h2(qb_r[g][j]), as_h2(kb[j]), xb, false);
+              }
             }
             pa[g] = group_sum<LPT>(xa);
             pb[g] = group_sum<LPT>(xb);
@@ -877,9 +878,10 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
   const dim3 grid(a.hkv * a.hsplit, a.compact ? a.n_pieces : a.n_sess, a.compact ? 1 : a.n_splits);
   const bool one = one_chunk_variant<KB, VB, D, GP>() && a.one_chunk;
   constexpr bool OK1 = one_chunk_variant<KB, VB, D, GP>();
-  if (KB == kF8 && a.q_dtype == 0) {
-    if (one) hipLaunchKernelGGL((decode_kernel<KB, VB, D, GP, E, KB == kF8, OK1>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((decode_kernel<KB, VB, D, GP, E, KB == kF8>), grid, dim3(256), 0, s, a);
+  constexpr bool HL = KB == kF8 || KB == 16;   // keys met by an fp16 query: fp32 queries add a low part
+  if (HL && a.q_dtype == 0) {
+    if (one) hipLaunchKernelGGL((decode_kernel<KB, VB, D, GP, E, HL, OK1>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((decode_kernel<KB, VB, D, GP, E, HL>), grid, dim3(256), 0, s, a);
   } else {
     if (one) hipLaunchKernelGGL((decode_kernel<KB, VB, D, GP, E, false, OK1>), grid, dim3(256), 0, s, a);
     else hipLaunchKernelGGL((decode_kernel<KB, VB, D, GP, E>), grid, dim3(256), 0, s, a);

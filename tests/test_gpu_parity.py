@@ -306,6 +306,104 @@ def test_chunk_matches_oracle(case):
         assert err <= TOL
 
 
+def _outlier_queries(shape, seed, factor, top=None):
+    """N(0, 1) queries whose four channels per query head are `factor` times larger (the
+    same channels in every row), optionally one channel raised to +-`top`: the shape of the
+    activation outliers of trained models, and a magnitude past fp16's range."""
+    q = I.normal(shape, seed, 9)
+    rng = np.random.default_rng(seed)
+    d = shape[-1]
+    for h in range(shape[1]):
+        ch = rng.choice(d, 4, replace=False)
+        q[:, h, ch] *= np.float32(factor)
+        if top is not None:
+            q[:, h, ch[0]] = np.float32(top) * np.sign(q[:, h, ch[0]] + 1e-30)
+    return q.astype(np.float32)
+
+
+QUERY_OUTLIER_LAYOUTS = ["K8V4", "K4V8", "K8V8", "K4V4", "FP16", "KF8V4"]
+
+
+@pytest.mark.parametrize("layout", QUERY_OUTLIER_LAYOUTS)
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+def test_decode_query_outlier_channels(layout, dtype):
+    """Queries with 4 channels per head 64 times the rest: the query's per-head scale then
+    spans the outliers, and the other channels must keep their precision."""
+    log(f"decode outlier queries {layout} {dtype}")
+    d, hkv, g = 128, 2, 4
+    lens = [900, 2100]
+    q = _outlier_queries((len(lens), hkv * g, d), 41, 64.0) * np.float32(0.25)
+    if dtype == "bf16":
+        q = I.bf16_round(q)
+    hs, ocs = [], []
+    try:
+        for i, n in enumerate(lens):
+            k, v, _ = I.workload_small(4400 + i, n, hkv, d, hkv * g, 1, bf16=(dtype == "bf16"))
+            h = kvq.kv_cache_create(layout, 1, hkv, d, n)
+            kvq.kv_append_quant(h, 0, dev(k, dtype), dev(v, dtype))
+            oc = O.OracleCache(O.LAYOUT_IDS[layout], 1, hkv, d, n)
+            oc.append(0, host_inputs(k, dtype), host_inputs(v, dtype))
+            hs.append(h)
+            ocs.append(oc)
+        out = kvq.kv_attend_decode(hs, 0, dev(q, dtype), d ** -0.5)
+        err = max_err(out, O.attend_decode(ocs, 0, host_inputs(q, dtype), d ** -0.5))
+        log(f"  max err {err:.3e}")
+        assert err <= TOL
+    finally:
+        torch_mod().cuda.synchronize()
+        for h in hs:
+            kvq.kv_cache_destroy(h)
+
+
+@pytest.mark.parametrize("layout", ["K8V4", "FP16", "KF8V4"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_queries_beyond_fp16_range(layout, dtype):
+    """A query channel at +-2^17 (past fp16's 65504) with the others ~1e-2: decode and chunk
+    must scale the query into range rather than overflow it."""
+    log(f"queries beyond fp16 {layout} {dtype}")
+    d, hkv, g, n_ctx, n_new = 128, 2, 4, 500, 40
+    n = n_ctx + n_new
+    k, v, _ = I.workload_small(4500, n, hkv, d, hkv * g, 1, bf16=(dtype == "bf16"))
+    k = (k * np.float32(1e-4)).astype(np.float32)     # keep the logits moderate
+    if dtype == "bf16":
+        k = I.bf16_round(k)
+    q = _outlier_queries((n_new, hkv * g, d), 45, 0.01, top=2.0 ** 17) * np.float32(0.01)
+    q[np.abs(q) > 1] *= np.float32(100.0)            # the top channel back at +-2^17
+    if dtype == "bf16":
+        q = I.bf16_round(q)
+    oc = O.OracleCache(O.LAYOUT_IDS[layout], 1, hkv, d, n)
+    oc.append(0, host_inputs(k, dtype), host_inputs(v, dtype))
+    with gpu_cache(layout, 1, hkv, d, n) as h:
+        kvq.kv_append_quant(h, 0, dev(k, dtype), dev(v, dtype))
+        qd = dev(q, dtype)
+        out_c = kvq.kv_attend_chunk(h, 0, qd, n_new, d ** -0.5)
+        err_c = max_err(out_c, O.attend_chunk(oc, 0, host_inputs(q, dtype), n_new, d ** -0.5))
+        out_d = kvq.kv_attend_decode([h], 0, dev(q[-1:], dtype), d ** -0.5)
+        err_d = max_err(out_d, O.attend_decode([oc], 0, host_inputs(q[-1:], dtype), d ** -0.5))
+        log(f"  chunk max err {err_c:.3e}, decode max err {err_d:.3e}")
+        assert err_c <= TOL and err_d <= TOL
+
+
+@pytest.mark.parametrize("layout", ["K8V4", "K4V8", "FP16", "KF8V4"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_chunk_query_outlier_channels(layout, dtype):
+    log(f"chunk outlier queries {layout} {dtype}")
+    d, hkv, g, n_ctx, n_new = 128, 2, 4, 1500, 100
+    n = n_ctx + n_new
+    k, v, _ = I.workload_small(4600, n, hkv, d, hkv * g, 1, bf16=(dtype == "bf16"))
+    q = _outlier_queries((n_new, hkv * g, d), 47, 64.0) * np.float32(0.25)
+    if dtype == "bf16":
+        q = I.bf16_round(q)
+    oc = O.OracleCache(O.LAYOUT_IDS[layout], 1, hkv, d, n)
+    oc.append(0, host_inputs(k, dtype), host_inputs(v, dtype))
+    with gpu_cache(layout, 1, hkv, d, n) as h:
+        kvq.kv_append_quant(h, 0, dev(k, dtype), dev(v, dtype))
+        out = kvq.kv_attend_chunk(h, 0, dev(q, dtype), n_new, d ** -0.5)
+        err = max_err(out, O.attend_chunk(oc, 0, host_inputs(q, dtype), n_new, d ** -0.5))
+        log(f"  max err {err:.3e}")
+        assert err <= TOL
+
+
 @pytest.mark.parametrize("layout,d,dtype", [("K8V4", 128, "bf16"), ("K4V4", 128, "f16"), ("K8V8", 64, "bf16"),
                                             ("K4V8", 128, "f32")])
 def test_chunk_keys_spanning_five_decades(layout, d, dtype):
