@@ -44,6 +44,22 @@
  *   - every call is asynchronous on `stream` (a hipStream_t; NULL = the null stream).
  *     The cached length of a layer advances when kv_append_quant is enqueued.
  *   - a handle must not be used from two threads at once; handles are independent.
+ *
+ * Numerics of the attention calls (outputs are fp32, within 5e-3 of exact attention over
+ * the dequantized cache on the tested workloads):
+ *   - queries of any finite magnitude.  Decode with 8- and 4-bit keys carries each query
+ *     head as q ~ s (256 hi + lo), s = max|q| / 32512 (integer digits): an absolute error
+ *     of at most max|q| / 65024 per element, so a channel far larger than the rest leaves
+ *     the rest that much resolution.  Decode with fp8 or fp16 keys and the chunk path
+ *     scale the query by a power of two that puts its largest element (per head in
+ *     decode, per 32 query rows in the chunk path) in [2^14, 2^15) and carry it in fp16:
+ *     16-bit queries exactly, fp32 queries as an fp16 high and low part.
+ *   - the chunk path carries dequantized keys and values in fp16 (keys as an fp16 high
+ *     part plus a scaled 6- or 8-bit low part): their magnitudes must stay below 65504,
+ *     or the outputs are not finite.  Decode takes 8- and 4-bit keys exactly (integer dot
+ *     products, then the block scale) and applies value scales to fp16 weights p * d.
+ *   - a NaN input element gives unspecified codes; an infinity saturates its block's scale
+ *     at 65504 and takes the clamped code, as the format above gives.
  */
 #ifndef KVQ_H
 #define KVQ_H
