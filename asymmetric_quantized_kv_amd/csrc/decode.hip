@@ -711,11 +711,12 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       const float mn = fmaxf(m[g], cm);
       const float mu = mn == -INFINITY ? 0.f : mn;
       const float alpha = __builtin_amdgcn_exp2f(m[g] - mu);
-      const float p0 = __builtin_amdgcn_exp2f(sa - mu), p1 = __builtin_amdgcn_exp2f(sb - mu);
+      const _Float16 p0 = (_Float16)__builtin_amdgcn_exp2f(sa - mu), p1 = (_Float16)__builtin_amdgcn_exp2f(sb - mu);
       // phase C pairs token 16 s + r with 16 s + r + 8 (r < 8) in one fp16x2 word
-      reinterpret_cast<_Float16*>(&s_w[wave][wpair0][g])[whalf0] = (_Float16)p0;
-      reinterpret_cast<_Float16*>(&s_w[wave][wpair1][g])[whalf1] = (_Float16)p1;
-      lsum[g] = lsum[g] * alpha + (p0 + p1);
+      reinterpret_cast<_Float16*>(&s_w[wave][wpair0][g])[whalf0] = p0;
+      reinterpret_cast<_Float16*>(&s_w[wave][wpair1][g])[whalf1] = p1;
+      // the normalizer sums the same fp16 weights the values are weighted with
+      lsum[g] = lsum[g] * alpha + ((float)p0 + (float)p1);
       if (alpha != 1.f) {  // wave-uniform
 #pragma unroll
         for (int e = 0; e < E; ++e) acc[g][e] *= alpha;

@@ -217,6 +217,37 @@ def test_decode_more_sessions_than_one_launch():
             kvq.kv_cache_destroy(h)
 
 
+@pytest.mark.parametrize("layout", ["K8V4", "K4V8", "K8V8", "FP16", "KF8V4"])
+@pytest.mark.parametrize("vscale", [1e-2, 1e-4])
+@pytest.mark.parametrize("shape", ["peaked", "flat"])
+def test_decode_small_values(layout, vscale, shape):
+    """Values scaled by 1e-2 and 1e-4 (small value scales: p times the scale then falls among
+    fp16's subnormals for many tokens), under an attention peaked on a few of 32,768 tokens
+    or spread over all of them, judged by the error relative to the output's magnitude."""
+    log(f"decode small values, {shape} {layout} x{vscale}")
+    d, hkv, g, n = 128, 2, 4, 32768
+    k, v, _ = I.workload_small(4700, n, hkv, d, hkv * g, 1, bf16=True)
+    v = I.bf16_round(v * np.float32(vscale) + np.float32(vscale))   # a nonzero mean: a flat
+    rng = np.random.default_rng(47)                                   # attention's output
+    q = np.empty((1, hkv * g, d), np.float32)
+    for h in range(hkv * g):
+        if shape == "peaked":   # each head aligned with three tokens' keys
+            q[0, h] = k[rng.choice(n, 3, replace=False), h // g].sum(0) * np.float32(1.2)
+        else:                   # logits within +-0.1 of each other
+            q[0, h] = rng.standard_normal(d).astype(np.float32) * np.float32(0.01)
+    q = I.bf16_round(q)
+    oc = O.OracleCache(O.LAYOUT_IDS[layout], 1, hkv, d, n)
+    oc.append(0, k, v)
+    with gpu_cache(layout, 1, hkv, d, n) as h:
+        kvq.kv_append_quant(h, 0, dev(k, "bf16"), dev(v, "bf16"))
+        out = kvq.kv_attend_decode([h], 0, dev(q, "bf16"), d ** -0.5)
+        want = O.attend_decode([oc], 0, q, d ** -0.5)
+        got = out.detach().cpu().numpy().astype(np.float64)
+        rel = float(np.max(np.abs(got - want)) / np.max(np.abs(want)))
+        log(f"  max err relative to max |out|: {rel:.3e}")
+        assert rel <= TOL
+
+
 def test_decode_same_cache_twice_in_one_call():
     """A cache listed twice in one call (two queries over the same context) next to another
     cache: each row must match the oracle, and a second call must too (the split merge's
