@@ -191,3 +191,20 @@ def test_code_rounding_identity_for_every_quotient():
     # the plain addend 1/2 would fail at |y| = 1/2 - 2^-25: the pin has teeth
     y = np.float32(0.5) - np.float32(2.0 ** -25)
     assert np.trunc(y + np.float32(0.5)) == 1.0 and np.trunc(y + c) == 0.0
+
+
+def test_the_boundary_check_catches_plausible_mistakes():
+    """The boundary cases above fail a quotient without the correction step, and one with
+    the residual's sign flipped (planted on the CPU, on every 64th fp16 scale)."""
+    ks = np.arange(128, dtype=np.float64) + 0.5
+    no_corr = flipped = 0
+    for d in positive_fp16_scales()[::64]:
+        r = rn32(1 / Fraction(float(d)))
+        base = (ks * np.float64(d)).astype(np.float32)
+        x = np.concatenate([base, np.nextafter(base, np.float32(np.inf)), np.nextafter(base, np.float32(-np.inf))])
+        want = codes(x / np.full_like(x, d), 127)
+        t = (x.astype(np.float64) * np.float64(r)).astype(np.float32)
+        no_corr += int(np.sum(codes(t, 127) != want))
+        dd, rr = np.full_like(x, d), np.full_like(x, r)
+        flipped += int(np.sum(codes(fma32(fma32(dd, t, x), rr, t), 127) != want))
+    assert no_corr > 0 and flipped > 0
