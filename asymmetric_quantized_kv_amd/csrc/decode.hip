@@ -108,8 +108,8 @@ __device__ __forceinline__ void st_partial(float* p, float v) {
 }
 
 template <int D>
-__device__ void merge_if_last(const DecodeArgs& a, const SessionRef& S, int64_t srow, int head, int tid, int* s_last) {
-  const int n_s = a.compact ? (int)((S.len + a.tps - 1) / a.tps) : a.n_splits;
+__device__ void merge_if_last(const DecodeArgs& a, const SessionRef& S, int n_s, int64_t srow, int head, int tid,
+                              int* s_last) {
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this lane's partial stores have completed
   __syncthreads();
   if (tid == 0) {
@@ -138,7 +138,9 @@ __device__ void merge_if_last(const DecodeArgs& a, const SessionRef& S, int64_t 
 // ONE: every wave holds at most one chunk (a split of at most 4 x 128 tokens): all of its key
 // and value codes are requested before the query is prepared, so a small launch pays one
 // memory latency instead of a chain of them.
-template <int KB, int VB, int D, int GP, int E, bool QLO = false, bool ONE = false>
+// STREAM: a streamed launch (DecodeArgs::stream), each workgroup taking in turn the part of
+// every session its block range overlaps
+template <int KB, int VB, int D, int GP, int E, bool QLO = false, bool ONE = false, bool STREAM = false>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   constexpr int LPT = D / E;           // lanes per token
   constexpr int TPS = 64 / LPT;        // tokens per half step
@@ -168,32 +170,64 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int vhead = blockIdx.x, head = vhead / a.hsplit;   // the workgroup's part of KV head `head`
-  int sl = blockIdx.y, split = blockIdx.z;
-  // the full grid's session, read before the launch kind is known (no wait on a.compact
-  // first: the empty asm keeps the compiler from sinking these loads past the branch)
-  SessionRef S = a.sess[min(sl, kMaxSessions - 1)];
-  asm volatile("" : "+s"(S.base), "+s"(S.cap), "+s"(S.len));
-  if (a.compact) {   // blockIdx.y enumerates the busy (session, split) pairs: the last session
-    int lo = 0, hi = a.n_sess - 1;   // whose first piece is at or before it
+  // streamed launches: blocks [blk, blk_end) of the sessions' blocks laid end to end
+  int64_t blk = 0, blk_end = 0;
+  if constexpr (STREAM) {
+    blk = a.wg_block0[blockIdx.y];
+    blk_end = a.wg_block0[blockIdx.y + 1];
+    if (blk >= blk_end) return;
+  }
+  do {   // once, or (streamed) once per session the block range overlaps
+  SessionRef S;
+  int split, n_merge;   // the partial's index among the session's, and their number
+  int64_t ts, te;       // the session's tokens [ts, te) taken here
+  bool part;            // write a partial (else the normalized output)
+  if constexpr (STREAM) {
+    int lo = 0, hi = a.n_sess - 1;   // the last session whose first block is at or before blk
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (a.sess[mid].piece0 <= sl) lo = mid; else hi = mid - 1;
+      if (a.sess[mid].piece0 <= blk) lo = mid; else hi = mid - 1;
     }
-    split = sl - a.sess[lo].piece0;
-    sl = lo;
-    S = a.sess[sl];
+    S = a.sess[lo];
+    const int64_t first = S.piece0, nb = (S.len + kDecodeWaveTokens - 1) / kDecodeWaveTokens;
+    const int64_t b1 = min(blk_end, first + nb);
+    ts = (blk - first) * kDecodeWaveTokens;
+    te = min(S.len, (b1 - first) * kDecodeWaveTokens);
+    split = (int)blockIdx.y - S.wfirst;
+    n_merge = S.nseg;
+    part = S.nseg > 1;
+    blk = b1;
+  } else {
+    int sl = blockIdx.y;
+    split = blockIdx.z;
+    // the full grid's session, read before the launch kind is known (no wait on a.compact
+    // first: the empty asm keeps the compiler from sinking these loads past the branch)
+    S = a.sess[min(sl, kMaxSessions - 1)];
+    asm volatile("" : "+s"(S.base), "+s"(S.cap), "+s"(S.len));
+    if (a.compact) {   // blockIdx.y enumerates the busy (session, split) pairs: the last session
+      int lo = 0, hi = a.n_sess - 1;   // whose first piece is at or before it
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (a.sess[mid].piece0 <= sl) lo = mid; else hi = mid - 1;
+      }
+      split = sl - a.sess[lo].piece0;
+      sl = lo;
+      S = a.sess[sl];
+    }
+    ts = (int64_t)split * a.tps;
+    te = min(ts + a.tps, S.len);
+    n_merge = a.compact ? (int)((S.len + a.tps - 1) / a.tps) : a.n_splits;
+    part = a.partial;
   }
   const int64_t srow = S.row * a.hq + (int64_t)vhead * a.group;  // first q row
-  const int64_t ts = (int64_t)split * a.tps;
-  const int64_t te = min(ts + a.tps, S.len);
   if (ts >= S.len) {
     // a split past this session's end (shorter sessions in a batch): an empty partial
-    if (a.partial) {
+    if (part) {
       for (int i = tid; i < a.group * (D + 2); i += 256) {
         const int g = i / (D + 2), e = i % (D + 2);
         st_partial(a.ws + ((srow + g) * a.n_splits + split) * (D + 2) + e, e == D ? -INFINITY : 0.f);
       }
-      if (a.fused) merge_if_last<D>(a, S, srow, vhead, tid, &s_last);
+      if (a.fused) merge_if_last<D>(a, S, n_merge, srow, vhead, tid, &s_last);
     }
     return;
   }
@@ -847,7 +881,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       }
     }
     const int64_t row = srow + g;
-    if (!a.partial) {
+    if (!part) {
       a.out[row * D + e] = o / l;
     } else {
       float* p = a.ws + (row * a.n_splits + split) * (D + 2);
@@ -858,7 +892,9 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       }
     }
   }
-  if (a.partial && a.fused) merge_if_last<D>(a, S, srow, vhead, tid, &s_last);
+  if (part && a.fused) merge_if_last<D>(a, S, n_merge, srow, vhead, tid, &s_last);
+  if constexpr (STREAM) __syncthreads();   // the next session's query preparation rewrites LDS
+  } while (STREAM && blk < blk_end);
 }
 
 template <int GP>
@@ -876,10 +912,16 @@ constexpr bool one_chunk_variant() {
 template <int KB, int VB, int D, int GP>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
   constexpr int E = lane_elems<GP>();
+  constexpr bool HL = KB == kF8 || KB == 16;   // keys met by an fp16 query: fp32 queries add a low part
+  if (a.stream) {
+    const dim3 grid(a.hkv * a.hsplit, a.n_wg, 1);
+    if (HL && a.q_dtype == 0) hipLaunchKernelGGL((decode_kernel<KB, VB, D, GP, E, HL, false, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((decode_kernel<KB, VB, D, GP, E, false, false, true>), grid, dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
   const dim3 grid(a.hkv * a.hsplit, a.compact ? a.n_pieces : a.n_sess, a.compact ? 1 : a.n_splits);
   const bool one = one_chunk_variant<KB, VB, D, GP>() && a.one_chunk;
   constexpr bool OK1 = one_chunk_variant<KB, VB, D, GP>();
-  constexpr bool HL = KB == kF8 || KB == 16;   // keys met by an fp16 query: fp32 queries add a low part
   if (HL && a.q_dtype == 0) {
     if (one) hipLaunchKernelGGL((decode_kernel<KB, VB, D, GP, E, HL, OK1>), grid, dim3(256), 0, s, a);
     else hipLaunchKernelGGL((decode_kernel<KB, VB, D, GP, E, HL>), grid, dim3(256), 0, s, a);
@@ -909,31 +951,32 @@ hipError_t launch_d(const DecodeArgs& a, int d, int gp, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-template <int KB, int VB, int D>
+template <int KB, int VB, int D, bool ST, bool QL>
 const void* ptr_g(int gp) {
   switch (gp) {
-    case 1: return reinterpret_cast<const void*>(&decode_kernel<KB, VB, D, 1, lane_elems<1>()>);
-    case 2: return reinterpret_cast<const void*>(&decode_kernel<KB, VB, D, 2, lane_elems<2>()>);
-    case 4: return reinterpret_cast<const void*>(&decode_kernel<KB, VB, D, 4, lane_elems<4>()>);
-    case 8: return reinterpret_cast<const void*>(&decode_kernel<KB, VB, D, 8, lane_elems<8>()>);
-    default: return reinterpret_cast<const void*>(&decode_kernel<KB, VB, D, 16, lane_elems<16>()>);
+    case 1: return reinterpret_cast<const void*>(&decode_kernel<KB, VB, D, 1, lane_elems<1>(), QL, false, ST>);
+    case 2: return reinterpret_cast<const void*>(&decode_kernel<KB, VB, D, 2, lane_elems<2>(), QL, false, ST>);
+    case 4: return reinterpret_cast<const void*>(&decode_kernel<KB, VB, D, 4, lane_elems<4>(), QL, false, ST>);
+    case 8: return reinterpret_cast<const void*>(&decode_kernel<KB, VB, D, 8, lane_elems<8>(), QL, false, ST>);
+    default: return reinterpret_cast<const void*>(&decode_kernel<KB, VB, D, 16, lane_elems<16>(), QL, false, ST>);
   }
 }
 
-template <int KB, int VB>
-const void* ptr_d(int d, int gp) {
-  return d == 64 ? ptr_g<KB, VB, 64>(gp) : ptr_g<KB, VB, 128>(gp);
+template <int KB, int VB, bool QL = false>
+const void* ptr_d(int d, int gp, bool st) {
+  if (st) return d == 64 ? ptr_g<KB, VB, 64, true, QL>(gp) : ptr_g<KB, VB, 128, true, QL>(gp);
+  return d == 64 ? ptr_g<KB, VB, 64, false, false>(gp) : ptr_g<KB, VB, 128, false, false>(gp);
 }
 
 }  // namespace
 
-const void* decode_kernel_for(int kbits, int vbits, int d, int gp) {
-  if (kbits == 16) return ptr_d<16, 16>(d, gp);
-  if (kbits == kF8) return ptr_d<kF8, 4>(d, gp);
-  if (kbits == 8 && vbits == 8) return ptr_d<8, 8>(d, gp);
-  if (kbits == 8) return ptr_d<8, 4>(d, gp);
-  if (vbits == 8) return ptr_d<4, 8>(d, gp);
-  return ptr_d<4, 4>(d, gp);
+const void* decode_kernel_for(int kbits, int vbits, int d, int gp, bool stream, bool q_fp32) {
+  if (kbits == 16) return q_fp32 && stream ? ptr_d<16, 16, true>(d, gp, true) : ptr_d<16, 16>(d, gp, stream);
+  if (kbits == kF8) return q_fp32 && stream ? ptr_d<kF8, 4, true>(d, gp, true) : ptr_d<kF8, 4>(d, gp, stream);
+  if (kbits == 8 && vbits == 8) return ptr_d<8, 8>(d, gp, stream);
+  if (kbits == 8) return ptr_d<8, 4>(d, gp, stream);
+  if (vbits == 8) return ptr_d<4, 8>(d, gp, stream);
+  return ptr_d<4, 4>(d, gp, stream);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int kbits, int vbits, int d, int gp, hipStream_t s) {

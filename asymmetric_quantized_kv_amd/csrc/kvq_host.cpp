@@ -441,6 +441,7 @@ struct SessionHeader {
   int64_t reserved;
 };
 static_assert(sizeof(SessionHeader) == 32, "header layout");
+static_assert(sizeof(DecodeArgs) <= 4096, "decode kernel arguments");
 
 int64_t session_data_offset(int n_layers) {
   return round_up((int64_t)sizeof(SessionHeader) + 12 * (int64_t)n_layers, 64);
@@ -728,9 +729,80 @@ bool decode_compact(int n_sessions, int n_splits, const int32_t* n_valid) {
   return empty && pieces <= 65535;
 }
 
+// Sessions longest first (stable): workgroups are dispatched in launch order, so the long
+// sessions' work starts early and the short ones fill the tail.
+std::vector<int> longest_first(const std::vector<int64_t>& lens) {
+  std::vector<int> order(lens.size());
+  for (size_t i = 0; i < order.size(); ++i) order[i] = (int)i;
+  std::stable_sort(order.begin(), order.end(), [&](int x, int y) { return lens[x] > lens[y]; });
+  return order;
+}
+
+// A streamed launch (DecodeArgs::stream): the sessions' blocks of kDecodeWaveTokens tokens,
+// longest session first and laid end to end, are cut into n_wg ranges per KV head, one
+// workgroup each and all resident at once, so no workgroup waits for a second round or
+// streams alone at the end.  A session overlapped by several ranges leaves one partial per
+// range, merged in the launch.  Each part of a session a workgroup takes costs it the
+// session's query preparation and an epilogue besides its blocks, so the cut balances blocks
+// plus kDecodeWgFixedTokens per part: a range over many short sessions holds fewer blocks.
+struct StreamPlan {
+  int n_wg = 0;
+  int max_seg = 0;                             // partials per row the workspace must hold
+  std::vector<int32_t> wg_block0;              // n_wg + 1 range bounds
+  std::vector<int32_t> block0, wfirst, nseg;   // per session, in longest-first order
+};
+
+StreamPlan stream_plan(const DecodePrep& p, const std::vector<int>& order, int n_wg) {
+  StreamPlan sp;
+  const int n = (int)order.size();
+  std::vector<int64_t> nb(n);
+  int64_t total = 0;
+  sp.block0.resize(n);
+  for (int i = 0; i < n; ++i) {
+    sp.block0[i] = (int32_t)total;
+    nb[i] = ceil_div(std::max<int64_t>(p.lens[order[i]], 1), kDecodeWaveTokens);
+    total += nb[i];
+  }
+  sp.n_wg = (int)std::max<int64_t>(1, std::min<int64_t>(n_wg, total));
+  const double part = (double)kDecodeWgFixedTokens / kDecodeWaveTokens;   // a part's fixed cost, in blocks
+  const double target = ((double)total + part * (double)(n + sp.n_wg - 1)) / sp.n_wg;
+  sp.wg_block0.assign(sp.n_wg + 1, (int32_t)total);
+  sp.wg_block0[0] = 0;
+  int w = 0;
+  double cum = 0;
+  int64_t b = 0;
+  for (int i = 0; i < n; ++i) {
+    cum += part;                         // the session's first part
+    for (int64_t j = 0; j < nb[i]; ++j) {
+      cum += 1.0;
+      ++b;
+      if (cum >= target * (w + 1) && w + 1 < sp.n_wg && b < total) {
+        sp.wg_block0[++w] = (int32_t)b;   // the next workgroup starts at block b
+        if (j + 1 < nb[i]) cum += part;   // and takes the rest of this session as a new part
+      }
+    }
+  }
+  // the workgroup of block x: the last range starting at or before it (ranges past the last
+  // cut are empty and start at `total`, beyond every block)
+  auto range_of = [&](int64_t x) {
+    return (int)(std::upper_bound(sp.wg_block0.begin(), sp.wg_block0.begin() + sp.n_wg, (int32_t)x) -
+                 sp.wg_block0.begin()) - 1;
+  };
+  sp.wfirst.resize(n);
+  sp.nseg.resize(n);
+  for (int i = 0; i < n; ++i) {
+    const int w0 = range_of(sp.block0[i]), w1 = range_of(sp.block0[i] + nb[i] - 1);
+    sp.wfirst[i] = w0;
+    sp.nseg[i] = w1 - w0 + 1;
+    sp.max_seg = std::max(sp.max_seg, sp.nseg[i]);
+  }
+  return sp;
+}
+
 int decode_launch(kv_cache* const* sessions, int n_sessions, int layer, const DecodePrep& p, const void* q,
                   int q_dtype, int n_q_heads, float sm_scale, int n_splits, int64_t tps, bool partial, float* ws,
-                  float* out, hipStream_t st, bool compact = false, bool fused = false) {
+                  float* out, hipStream_t st, bool compact = false, bool fused = false,
+                  const StreamPlan* stream = nullptr) {
   DecodeArgs a;
   memset(&a, 0, sizeof(a));
   a.hkv = p.hkv;
@@ -745,11 +817,35 @@ int decode_launch(kv_cache* const* sessions, int n_sessions, int layer, const De
   a.qk_scale = sm_scale * 1.4426950408889634f;
   a.ws = ws;
   a.out = out;
-  // Longest sessions first: workgroups are dispatched in launch order, so the long
-  // sessions' splits start early and the short ones fill the tail.
-  std::vector<int> order(n_sessions);
-  for (int i = 0; i < n_sessions; ++i) order[i] = i;
-  std::stable_sort(order.begin(), order.end(), [&](int x, int y) { return p.lens[x] > p.lens[y]; });
+  const std::vector<int> order = longest_first(p.lens);
+  if (stream) {   // one launch of every session (the caller checked n_sessions <= kMaxSessions)
+    a.n_splits = stream->max_seg;
+    a.partial = 1;
+    a.fused = 1;
+    a.stream = 1;
+    a.n_wg = stream->n_wg;
+    for (int w = 0; w <= stream->n_wg; ++w) a.wg_block0[w] = stream->wg_block0[w];
+    a.n_sess = n_sessions;
+    for (int i = 0; i < n_sessions; ++i) {
+      const kv_cache* c = sessions[order[i]];
+      a.sess[i].base = layer_base(c, layer);
+      a.sess[i].counters = reinterpret_cast<uint32_t*>(c->arena + c->counter_off) + (int64_t)layer * c->hkv * kMaxHeadSplit;
+      a.sess[i].cap = c->lg[layer].g.cap;
+      a.sess[i].len = c->len[layer];
+      a.sess[i].row = (int32_t)order[i];
+      a.sess[i].piece0 = stream->block0[i];
+      a.sess[i].wfirst = stream->wfirst[i];
+      a.sess[i].nseg = stream->nseg[i];
+    }
+    a.hsplit = 1;
+    a.one_chunk = 0;
+    hipError_t e = launch_decode(a, p.kbits, p.vbits, p.d, decode_group_pad(a.group), st);
+    if (e != hipSuccess) {
+      for (int i = 0; i < n_sessions; ++i) sessions[i]->poisoned = true;
+      return fail(KV_EHIP, "decode launch: %s", hipGetErrorString(e));
+    }
+    return KV_OK;
+  }
   for (int b0 = 0; b0 < n_sessions; b0 += kMaxSessions) {
     const int nb = std::min(kMaxSessions, n_sessions - b0);
     a.n_sess = nb;
@@ -932,23 +1028,48 @@ int chunk_launch(kv_cache* cache, int layer, const ChunkPrep& p, const void* q, 
   return KV_OK;
 }
 
-// kv_attend_decode's work once its arguments are checked and planned: the partial pass (or the
-// whole attention for one split) and the merge, with the partials in ws.
-int decode_run(kv_cache* const* sessions, int n_sessions, int layer, const DecodePrep& p, const void* q, int q_dtype,
-               int n_q_heads, float sm_scale, float* out, int n_splits, int64_t tps, float* ws, hipStream_t st) {
-  int32_t n_valid[kMaxSessions];
+// Split partials and their merge in one launch: the last workgroup of each (session, KV head)
+// to finish merges.  Its split counters live in the session's arena, so launches of more than
+// kMaxSessions sessions stay independent; a cache passed twice in one call would share its
+// counters between two rows and takes the separate merge instead.
+bool repeated_cache(kv_cache* const* sessions, int n_sessions) {
+  std::vector<const kv_cache*> seen(sessions, sessions + n_sessions);
+  std::sort(seen.begin(), seen.end());
+  return std::adjacent_find(seen.begin(), seen.end()) != seen.end();
+}
+
+void decode_valid(const DecodePrep& p, int n_sessions, int64_t tps, int32_t* n_valid) {
   for (int i = 0; i < n_sessions && i < kMaxSessions; ++i) n_valid[i] = (int32_t)ceil_div(std::max<int64_t>(p.lens[i], 1), tps);
+}
+
+// Where the split plan would launch only the busy workgroups of uneven sessions (one launch,
+// fused merge), a streamed launch takes its place when the device's resident workgroups per KV
+// head fit the range table and the workspace (ws_bytes) holds its partials.
+bool decode_stream(kv_cache* const* sessions, int n_sessions, const DecodePrep& p, int q_dtype, int n_q_heads,
+                   int n_splits, int64_t tps, int64_t ws_bytes, StreamPlan* sp) {
+  if (n_sessions < 2 || n_sessions > kMaxSessions || n_splits <= 1) return false;
+  int32_t n_valid[kMaxSessions];
+  decode_valid(p, n_sessions, tps, n_valid);
+  if (!decode_compact(n_sessions, n_splits, n_valid) || repeated_cache(sessions, n_sessions)) return false;
+  const int64_t slots = resident_slots(p.device, decode_kernel_for(p.kbits, p.vbits, p.d, p.gp, true, q_dtype == KV_F32));
+  const int64_t n_wg = std::min<int64_t>(slots > 0 ? slots / p.hkv : 0, decode_split_cap(p));
+  if (n_wg < 2 || n_wg > kMaxStreamWg) return false;
+  *sp = stream_plan(p, longest_first(p.lens), (int)n_wg);
+  return partial_bytes(n_sessions * (int64_t)n_q_heads, sp->max_seg, p.d) <= ws_bytes;
+}
+
+// kv_attend_decode's work once its arguments are checked and planned: the streamed launch, or
+// the partial pass (or the whole attention for one split) and the merge, with the partials in ws.
+int decode_run(kv_cache* const* sessions, int n_sessions, int layer, const DecodePrep& p, const void* q, int q_dtype,
+               int n_q_heads, float sm_scale, float* out, int n_splits, int64_t tps, float* ws, hipStream_t st,
+               const StreamPlan* stream = nullptr) {
+  if (stream)
+    return decode_launch(sessions, n_sessions, layer, p, q, q_dtype, n_q_heads, sm_scale, n_splits, tps, true, ws, out,
+                         st, false, true, stream);
+  int32_t n_valid[kMaxSessions];
+  decode_valid(p, n_sessions, tps, n_valid);
   const bool compact = decode_compact(n_sessions, n_splits, n_valid);
-  // Split partials and their merge in one launch: the last workgroup of each (session, KV
-  // head) to finish merges.  Its split counters live in the session's arena, so launches of
-  // more than kMaxSessions sessions stay independent; a cache passed twice in one call would
-  // share its counters between two rows and takes the separate merge instead.
-  bool repeated = false;
-  if (n_splits > 1) {
-    std::vector<const kv_cache*> seen(sessions, sessions + n_sessions);
-    std::sort(seen.begin(), seen.end());
-    repeated = std::adjacent_find(seen.begin(), seen.end()) != seen.end();
-  }
+  const bool repeated = n_splits > 1 && repeated_cache(sessions, n_sessions);
   int rc = decode_launch(sessions, n_sessions, layer, p, q, q_dtype, n_q_heads, sm_scale, n_splits, tps, n_splits > 1,
                          ws, out, st, compact, /*fused=*/!repeated);
   if (rc || !repeated) return rc;
@@ -1003,10 +1124,12 @@ int kv_attend_decode(kv_cache* const* sessions, int n_sessions, int layer, const
   int n_splits;
   int64_t tps;
   decode_plan(p, &n_splits, &tps);
-  const int64_t need = n_splits > 1 ? partial_bytes(n_sessions * (int64_t)n_q_heads, n_splits, p.d) : 0;
+  StreamPlan sp;
+  const bool streamed = workspace && decode_stream(sessions, n_sessions, p, q_dtype, n_q_heads, n_splits, tps, (int64_t)ws_bytes, &sp);
+  const int64_t need = n_splits > 1 ? partial_bytes(n_sessions * (int64_t)n_q_heads, streamed ? sp.max_seg : n_splits, p.d) : 0;
   if ((rc = check_workspace(workspace, ws_bytes, need))) return rc;
   return decode_run(sessions, n_sessions, layer, p, q, q_dtype, n_q_heads, sm_scale, out, n_splits, tps,
-                    static_cast<float*>(workspace), static_cast<hipStream_t>(stream));
+                    static_cast<float*>(workspace), static_cast<hipStream_t>(stream), streamed ? &sp : nullptr);
 }
 
 int kv_attend_decode_static(kv_cache* const* sessions, int n_sessions, int layer, const void* q,
@@ -1019,7 +1142,9 @@ int kv_attend_decode_static(kv_cache* const* sessions, int n_sessions, int layer
   int n_splits;
   int64_t tps;
   decode_plan(p, &n_splits, &tps);
-  const int64_t need = n_splits > 1 ? partial_bytes(n_sessions * (int64_t)n_q_heads, n_splits, p.d) : 0;
+  StreamPlan sp;
+  const bool streamed = decode_stream(sessions, n_sessions, p, q_dtype, n_q_heads, n_splits, tps, (int64_t)kStaticScratchBytes, &sp);
+  const int64_t need = n_splits > 1 ? partial_bytes(n_sessions * (int64_t)n_q_heads, streamed ? sp.max_seg : n_splits, p.d) : 0;
   if (need > (int64_t)kStaticScratchBytes)
     return fail(KV_EINVAL,
                 "the split plan of this call (%d splits x %lld rows) needs %lld bytes of partials, more than the %lld "
@@ -1031,7 +1156,7 @@ int kv_attend_decode_static(kv_cache* const* sessions, int n_sessions, int layer
     if (e != hipSuccess) return fail(KV_EHIP, "static scratch lookup: %s", hipGetErrorString(e));
   }
   return decode_run(sessions, n_sessions, layer, p, q, q_dtype, n_q_heads, sm_scale, out, n_splits, tps, ws,
-                    static_cast<hipStream_t>(stream));
+                    static_cast<hipStream_t>(stream), streamed ? &sp : nullptr);
 }
 
 int kv_attend_decode_partial(kv_cache* const* sessions, int n_sessions, int layer, const void* q,

@@ -12,6 +12,7 @@ constexpr int kMaxSessions = 64;    // sessions per decode launch (kernel-argume
 constexpr int kDecodeChunk = 128;   // tokens one wave scores before its softmax update
 constexpr int kDecodeWaveTokens = 4 * kDecodeChunk;  // split granularity of decode
 constexpr int kMaxHeadSplit = 2;    // decode workgroups per KV head at most (see DecodeArgs::hsplit)
+constexpr int kMaxStreamWg = 128;   // workgroups per KV head of a streamed decode launch at most
 constexpr int kChunkThreads = 768;  // threads per chunk-prefill workgroup: 8 consumer + 4 producer waves
 constexpr int kChunkRows = 256;     // query rows per chunk-prefill workgroup (32 per consumer wave)
 constexpr int kChunkKeys = 64;      // keys per chunk-prefill tile
@@ -54,7 +55,10 @@ struct SessionRef {
   int64_t cap;
   int64_t len;
   int32_t row;            // index of the session in the call (rows of q / out / workspace)
-  int32_t piece0;         // compact launches: index of its first busy split among all sessions
+  int32_t piece0;         // compact launches: index of its first busy split among all sessions;
+                          // streamed launches: index of its first token block among all sessions
+  int32_t wfirst, nseg;   // streamed launches: the first workgroup (per KV head) whose block range
+                          // overlaps the session, and how many do (its partials; 1: no merge)
 };
 
 struct DecodeArgs {
@@ -78,6 +82,11 @@ struct DecodeArgs {
   // one_chunk != 0: tps <= kDecodeWaveTokens (each wave holds at most one chunk) and the grid
   // fits the device at one workgroup per compute unit
   int one_chunk;
+  // stream != 0 (fused, one launch): the sessions' token blocks of kDecodeWaveTokens, laid end
+  // to end in session order, are cut into n_wg ranges, one per workgroup of each KV head (grid
+  // y): workgroup w takes blocks [wg_block0[w], wg_block0[w + 1]), the part of every session
+  // that range overlaps, all workgroups in one round
+  int stream, n_wg;
   int q_dtype;
   int64_t tps;            // tokens per split, multiple of kDecodeWaveTokens
   const void* q;
@@ -85,6 +94,7 @@ struct DecodeArgs {
   float* ws;              // [S][Hq][n_splits][D + 2] partials when partial
   float* out;             // [S][Hq][D] otherwise
   SessionRef sess[kMaxSessions];
+  int32_t wg_block0[kMaxStreamWg + 1];
 };
 
 struct ChunkArgs {
@@ -129,7 +139,9 @@ hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
 hipError_t static_scratch(int device, float** ptr);
 
 // Kernel symbols, for occupancy queries by the split planner.
-const void* decode_kernel_for(int kbits, int vbits, int d, int gp);
+// stream: the streamed variant; q_fp32: with fp32 queries (which carry a low part for fp16 and
+// fp8 keys in that variant)
+const void* decode_kernel_for(int kbits, int vbits, int d, int gp, bool stream = false, bool q_fp32 = false);
 const void* chunk_kernel_for(int kbits, int vbits, int d, bool q_fp32);
 
 }  // namespace kvq

@@ -156,6 +156,15 @@ int kv_append_quant(kv_cache* cache, int layer, const void* k, const void* v, in
  * head_dim); their lengths may differ.  q: device [n_sessions][n_q_heads][head_dim] of
  * q_dtype.  out: device fp32, same shape.  workspace: device scratch of at least
  * kv_decode_workspace_bytes(...) bytes (may be NULL when that is 0).
+ * Launch: the split plan of kv_decode_plan, its partials merged in the same launch (in a
+ * second launch when a cache is passed twice); or, for
+ * 2..64 sessions of uneven lengths (the plan would leave some session's later splits empty),
+ * no cache passed twice, at most 128 resident workgroups per KV head (4 or more KV heads at
+ * two workgroups per compute unit) and a workspace that holds its partials, a
+ * streamed launch: the sessions' 512-token blocks, longest session first and laid end to
+ * end, are cut into one range per resident workgroup of each KV head (balancing blocks plus a
+ * fixed cost per session part), and a session that several ranges overlap is merged from
+ * their partials.  Both compute the same attention to within rounding; each is deterministic.
  * Errors: KV_EINVAL (mismatched sessions, n_q_heads % n_kv_heads, group size > 16,
  * small workspace, null/misaligned pointers), KV_EEMPTY (a session with len == 0),
  * KV_EHIP. */
@@ -167,8 +176,9 @@ int kv_attend_decode(kv_cache* const* sessions, int n_sessions, int layer, const
  * allocate device memory (code under HIP graph capture, tight serving loops, harnesses that
  * forbid allocation).  The split partials live in a static device array of the library
  * (16 MiB per device, held from module load until the process ends).  Same arguments,
- * split plan and results as kv_attend_decode (bit for bit).  Errors as kv_attend_decode,
- * plus KV_EINVAL when the plan's partials (n_splits * n_sessions * n_q_heads *
+ * launch and results as kv_attend_decode (bit for bit), except that a streamed launch whose
+ * partials exceed 16 MiB gives way to the split plan here.  Errors as kv_attend_decode,
+ * plus KV_EINVAL when the split plan's partials (n_splits * n_sessions * n_q_heads *
  * (head_dim + 2) * 4 bytes, see kv_decode_plan) exceed 16 MiB; a one-split plan needs none.
  * Every call on a device shares that device's array: calls that overlap on one device (on
  * different streams, or from different threads) race for it and must not be issued. */
@@ -184,9 +194,10 @@ int64_t kv_decode_workspace_bytes(kv_cache* const* sessions, int n_sessions, int
 /* The two passes of kv_attend_decode, callable one by one (to time or overlap them, or to
  * merge partials computed elsewhere, e.g. on several devices).
  *
- * kv_decode_plan: the split kv_attend_decode uses for these sessions -- the context is cut
- * into *n_splits ranges of *tokens_per_split tokens (a multiple of 512) covering the
- * longest session.  Errors as kv_attend_decode (KV_EEMPTY for an empty session).
+ * kv_decode_plan: the split kv_attend_decode uses for these sessions (unless it takes the
+ * streamed launch) -- the context is cut into *n_splits ranges of *tokens_per_split tokens
+ * (a multiple of 512) covering the longest session.  Errors as kv_attend_decode (KV_EEMPTY
+ * for an empty session).
  *
  * kv_attend_decode_partial: the first pass alone, with a split of the caller's choice
  * (1 <= n_splits <= 65535; tokens_per_split a positive multiple of 512 with n_splits *

@@ -12,6 +12,6 @@ hipError_t static_scratch(int, float** ptr) {
   *ptr = nullptr;
   return hipErrorInvalidValue;
 }
-const void* decode_kernel_for(int, int, int, int) { return nullptr; }
+const void* decode_kernel_for(int, int, int, int, bool, bool) { return nullptr; }
 const void* chunk_kernel_for(int, int, int, bool) { return nullptr; }
 }  // namespace kvq

@@ -93,12 +93,15 @@ def test_decode_partials_and_merge(case):
             err = max_err(kvq.kv_merge_partials(p), want)
             log(f"  merged err {err:.3e}")
             assert err <= TOL
-        # the one-call path is these two passes under its own plan
+        # the one-call path is these two passes under its own plan (uneven sessions may take a
+        # streamed launch instead, whose ranges the partial call cannot express: there the
+        # oracle alone is the check)
         n_splits, per = kvq.kv_decode_plan(sessions, 0, hq)
         assert n_splits >= 1 and per % 512 == 0 and n_splits * per >= max(lens)
         full = kvq.kv_attend_decode(sessions, 0, qd, scale)
         assert max_err(full, want) <= TOL
-        if n_splits > 1:
+        uneven = len(lens) > 1 and any(-(-n // per) < n_splits for n in lens)
+        if n_splits > 1 and not uneven:
             two = kvq.kv_merge_partials(kvq.kv_attend_decode_partial(sessions, 0, qd, scale, n_splits, per))
             assert torch.equal(full, two)
     finally:
