@@ -100,7 +100,8 @@ __device__ __forceinline__ void encode_block(const float (&x)[kBlock], uint32_t 
     scales_row[blk] = (uint8_t)(e + 127);
   } else {
     constexpr float qmax = BITS == 8 ? 127.f : 7.f;
-    const float d32 = fminf(amax / qmax, 65504.f);       // IEEE division, saturate
+    const float raw = amax / qmax;                        // IEEE division
+    const float d32 = fminf(raw, 65504.f);                // saturate
     const _Float16 d16 = (_Float16)d32;                   // round to nearest even
     const float d = (float)d16;
     // y = x / d without a division per element: r = RN(1 / d) from the hardware reciprocal
@@ -127,17 +128,28 @@ __device__ __forceinline__ void encode_block(const float (&x)[kBlock], uint32_t 
     // addend just below 1/2 keeps |y| = 1/2 - 2^-25 from rounding up to 1 in the addition,
     // while a tie k + 1/2 still rounds up to k + 1 (every fp32 |y| in [2^-30, 512) checked
     // against round-half-away; below that both give 0, above it both clamp).
+    // The clamp can only act when d is below fp16's normal range (its rounding there may lose
+    // far more than 2^-11) or saturated: otherwise d >= (amax / qmax)(1 - 2^-11 - 2^-23), so
+    // |y| <= qmax (1 + 2^-10) < qmax + 1/2 for every element of the block.  A wave none of
+    // whose blocks has such a d skips it.
+    const bool clamp = d < 6.103515625e-05f || raw > 65504.f;
     int q[kBlock];
+    if (__builtin_amdgcn_ballot_w64(clamp) != 0) {
 #pragma unroll
-    for (int i = 0; i < kBlock; ++i) {
-      const float t = y[i] + __builtin_copysignf(0.49999997f, y[i]);
-      q[i] = (int)fminf(fmaxf(t, -qmax), qmax);
+      for (int i = 0; i < kBlock; ++i) {
+        const float t = y[i] + __builtin_copysignf(0.49999997f, y[i]);
+        q[i] = (int)fminf(fmaxf(t, -qmax), qmax);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kBlock; ++i) q[i] = (int)(y[i] + __builtin_copysignf(0.49999997f, y[i]));
     }
     if constexpr (BITS == 8) {
+      // low bytes of four codes into one dword: two byte permutes (0x0c selects a zero byte)
 #pragma unroll
       for (int h = 0; h < 8; ++h)
-        w[h] = (q[4 * h] & 0xff) | ((q[4 * h + 1] & 0xff) << 8) | ((q[4 * h + 2] & 0xff) << 16) |
-               ((uint32_t)(q[4 * h + 3] & 0xff) << 24);
+        w[h] = __builtin_amdgcn_perm((uint32_t)q[4 * h + 1], (uint32_t)q[4 * h], 0x0c0c0400u) |
+               __builtin_amdgcn_perm((uint32_t)q[4 * h + 3], (uint32_t)q[4 * h + 2], 0x04000c0cu);
     } else {
 #pragma unroll
       for (int h = 0; h < 4; ++h) w[h] = 0;
