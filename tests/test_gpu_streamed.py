@@ -1,5 +1,6 @@
 """GPU parity of the streamed decode launch: uneven sessions in one fused call, their token
-blocks laid end to end and cut into equal workgroup ranges (a range may hold the tail of one
+blocks laid end to end and cut into one range per resident workgroup of each KV head,
+balanced by blocks plus a fixed cost per session part (a range may hold the tail of one
 session and the head of the next; a long session spans many ranges and leaves a partial per
 range, merged in the launch).
 
@@ -171,3 +172,38 @@ def test_streamed_decode_tracks_growing_sessions():
         torch.cuda.synchronize()
         for h in sessions:
             kvq.kv_cache_destroy(h)
+
+
+def test_streamed_decode_random_batches():
+    """Seeded random batches (2 to 64 sessions, log-uniform lengths from 1 to 6,000 tokens,
+    4 or 8 KV heads, groups 2 to 8, a random layout), each against the oracle: the cut's
+    corner cases (ranges inside one session, ranges over many, sessions of one block) come
+    up in many combinations."""
+    torch = torch_mod()
+    rng = np.random.default_rng(4242)
+    layouts = ["K8V4", "K4V8", "K8V8", "K4V4", "FP16", "KF8V4"]
+    ran = 0
+    for case in range(16):
+        n = int(rng.integers(2, 65))
+        lens = [int(x) for x in np.exp(rng.uniform(0, np.log(6000), n)).astype(np.int64).clip(1, 6000)]
+        hkv = int(rng.choice([4, 8]))
+        g = int(rng.choice([2, 4, 8]))
+        layout = str(rng.choice(layouts))
+        d = 64
+        hq = hkv * g
+        sessions, ocs = _build(layout, lens, hkv, d, hq, 1700 + 37 * case, True)
+        try:
+            if not _uneven(sessions, hq):
+                log(f"  case {case}: even plan, skipped")
+                continue
+            q = I.bf16_round(I.normal((n, hq, d), 1800 + case, 9))
+            want = O.attend_decode(ocs, 0, q, d ** -0.5)
+            err = max_err(kvq.kv_attend_decode(sessions, 0, dev(q, "bf16"), d ** -0.5), want)
+            log(f"  case {case}: {layout} Hkv {hkv} G {g}, {n} sessions, {sum(lens)} tokens: err {err:.3e}")
+            assert err <= TOL
+            ran += 1
+        finally:
+            torch.cuda.synchronize()
+            for h in sessions:
+                kvq.kv_cache_destroy(h)
+    assert ran >= 10
