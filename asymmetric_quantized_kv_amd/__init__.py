@@ -11,7 +11,7 @@ from ._lib import (  # noqa: F401
     KV_PLANE_KC, KV_PLANE_KS, KV_PLANE_VC, KV_PLANE_VS,
     lib, kv_cache_create, kv_cache_create_layered, kv_cache_layout, kv_cache_shape, kv_cache_check_guard, kv_layered_footprint_bytes,
     kv_cache_destroy, kv_append_quant, kv_attend_decode, kv_attend_decode_static,
-    kv_decode_workspace_bytes, kv_decode_plan, kv_attend_decode_partial, kv_merge_partials,
+    kv_decode_workspace_bytes, kv_decode_launch_kind, kv_decode_plan, kv_attend_decode_partial, kv_merge_partials,
     kv_attend_chunk, kv_chunk_workspace_bytes, kv_chunk_plan, kv_attend_chunk_partial, kv_footprint_bytes,
     kv_layout_footprint_bytes, kv_cache_len, kv_cache_reset, kv_cache_truncate, kv_cache_plane, kv_cache_copy_plane,
     kv_session_bytes, kv_session_save, kv_session_load, kv_last_error, kv_last_status, read_plane,

@@ -34,6 +34,7 @@ _SIGS = {
     "kv_attend_decode_static": (C.c_int, [C.c_void_p, C.c_int, C.c_int, C.c_void_p, C.c_int, C.c_int, C.c_float,
                                           C.c_void_p, C.c_void_p]),
     "kv_decode_workspace_bytes": (C.c_int64, [C.c_void_p, C.c_int, C.c_int, C.c_int]),
+    "kv_decode_launch_kind": (C.c_int, [C.c_void_p, C.c_int, C.c_int, C.c_int, C.c_int, C.c_size_t]),
     "kv_decode_plan": (C.c_int, [C.c_void_p, C.c_int, C.c_int, C.c_int, C.POINTER(C.c_int),
                                  C.POINTER(C.c_int64)]),
     "kv_attend_decode_partial": (C.c_int, [C.c_void_p, C.c_int, C.c_int, C.c_void_p, C.c_int, C.c_int, C.c_float,
@@ -270,6 +271,15 @@ def kv_attend_decode_static(sessions, layer: int, q, sm_scale: float, out, strea
     _check(lib().kv_attend_decode_static(_handles(sessions), len(sessions), layer, _dev_ptr(q, "q"), _dtype_code(q),
                                          q.shape[1], float(sm_scale), _dev_ptr(out, "out"), _stream(stream)))
     return out
+
+
+def kv_decode_launch_kind(sessions, layer: int, n_q_heads: int, q_dtype: int = KV_BF16, ws_bytes=None) -> int:
+    """0: kv_attend_decode runs the split plan of kv_decode_plan; 1: the streamed launch.
+    ws_bytes defaults to kv_decode_workspace_bytes (what kv_attend_decode allocates itself)."""
+    if ws_bytes is None:
+        ws_bytes = kv_decode_workspace_bytes(sessions, layer, n_q_heads)
+    return _check(lib().kv_decode_launch_kind(_handles(sessions), len(sessions), layer, q_dtype, n_q_heads,
+                                              int(ws_bytes)))
 
 
 def kv_decode_plan(sessions, layer: int, n_q_heads: int):

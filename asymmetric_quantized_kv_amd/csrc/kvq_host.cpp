@@ -1132,6 +1132,20 @@ int kv_attend_decode(kv_cache* const* sessions, int n_sessions, int layer, const
                     static_cast<float*>(workspace), static_cast<hipStream_t>(stream), streamed ? &sp : nullptr);
 }
 
+int kv_decode_launch_kind(kv_cache* const* sessions, int n_sessions, int layer, int q_dtype, int n_q_heads,
+                          size_t ws_bytes) {
+  clear_err();
+  DecodePrep p;
+  int rc = decode_prepare(sessions, n_sessions, layer, n_q_heads, true, &p);
+  if (rc) return rc;
+  if (!dtype_ok(q_dtype)) return fail(KV_EINVAL, "q_dtype %d is not one of KV_F32/KV_BF16/KV_F16", q_dtype);
+  int n_splits;
+  int64_t tps;
+  decode_plan(p, &n_splits, &tps);
+  StreamPlan sp;
+  return decode_stream(sessions, n_sessions, p, q_dtype, n_q_heads, n_splits, tps, (int64_t)ws_bytes, &sp) ? 1 : 0;
+}
+
 int kv_attend_decode_static(kv_cache* const* sessions, int n_sessions, int layer, const void* q,
                             int q_dtype, int n_q_heads, float sm_scale, float* out, void* stream) {
   clear_err();

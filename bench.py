@@ -370,8 +370,10 @@ def main():
         "cache_bytes": rag_bytes, "ms": round(t_rag, 4), "GBps": round(rag_bytes / (t_rag * 1e-3) / 1e9, 1),
         "hbm_frac": round(rag_bytes / (t_rag * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "plan": {"n_splits": rag_plan[0], "tokens_per_split": rag_plan[1]},
-        "launch": "streamed: the sessions' 512-token blocks cut into one range per resident workgroup of each "
-                  "KV head (the split plan above is what it replaces; include/kvq.h, kv_attend_decode)",
+        "launch": ("streamed: the sessions' 512-token blocks cut into one range per resident workgroup of each KV "
+                   "head (the split plan above is what it replaces; include/kvq.h, kv_attend_decode)"
+                   if kvq.kv_decode_launch_kind(caches["K8V4"], 0, DEC_HQ, kvq.KV_BF16, ws_rag.numel()) == 1
+                   else "the split plan above"),
     }
     log(f"ragged decode {t_rag:.4f} ms ({extra['ragged_decode']['GBps']} GB/s), plan {rag_plan}")
 

@@ -185,6 +185,12 @@ int kv_attend_decode(kv_cache* const* sessions, int n_sessions, int layer, const
 int kv_attend_decode_static(kv_cache* const* sessions, int n_sessions, int layer, const void* q,
                             int q_dtype, int n_q_heads, float sm_scale, float* out, void* stream);
 
+/* Which launch kv_attend_decode takes for these sessions, queries of q_dtype and a workspace
+ * of ws_bytes: 0 = the split plan of kv_decode_plan, 1 = the streamed launch (see
+ * kv_attend_decode); < 0 on bad arguments (as kv_attend_decode).  Host-only, no device work. */
+int kv_decode_launch_kind(kv_cache* const* sessions, int n_sessions, int layer, int q_dtype,
+                          int n_q_heads, size_t ws_bytes);
+
 /* Workspace bytes kv_attend_decode needs for these sessions; < 0 on bad arguments.  It
  * depends only on shapes (n_sessions, n_q_heads, head_dim, the sessions' max_tokens, the
  * device), so a workspace sized once fits every later call on the same caches. */

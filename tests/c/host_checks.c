@@ -70,6 +70,7 @@ int main(void) {
   EXPECT(kv_attend_decode_static(NULL, 1, 0, NULL, 0, 4, 0.1f, NULL, NULL) == KV_EINVAL);
   EXPECT(kv_attend_chunk(NULL, 0, NULL, 0, 4, 1, 0.1f, NULL, NULL, 0, NULL) == KV_EINVAL);
   EXPECT(kv_decode_plan(NULL, 1, 0, 4, &n, &t) == KV_EINVAL);
+  EXPECT(kv_decode_launch_kind(NULL, 1, 0, KV_BF16, 4, 0) == KV_EINVAL);
   EXPECT(kv_chunk_plan(NULL, 0, 4, 1, &n, &t) == KV_EINVAL);
   EXPECT(kv_attend_decode_partial(NULL, 1, 0, NULL, 0, 4, 0.1f, 1, 512, NULL, 0, NULL) == KV_EINVAL);
   EXPECT(kv_attend_chunk_partial(NULL, 0, NULL, 0, 4, 1, 0.1f, 1, 64, NULL, 0, NULL) == KV_EINVAL);

@@ -9,8 +9,8 @@ splits of uneven sessions (more than one split, some session shorter than the sp
 one launch holds every session (at most 64), no cache is passed twice, the device's resident
 workgroups per KV head number 2 to 128 (4 or 8 KV heads on 256 compute units) and the
 workspace holds one partial per range a session spans (kv_decode_workspace_bytes always
-does).  Each case below meets those conditions; the oracle is the plain fp64 attention over
-its quantized cache.
+does).  Each case below asserts, through kv_decode_launch_kind, that it takes that launch;
+the oracle is the plain fp64 attention over its quantized cache.
 """
 from __future__ import annotations
 
@@ -36,11 +36,10 @@ def _gpu():
     torch.cuda.synchronize()
 
 
-def _uneven(sessions, hq):
-    """The conditions of the streamed launch that depend on the lengths."""
-    n_splits, per = kvq.kv_decode_plan(sessions, 0, hq)
-    lens = [kvq.kv_cache_len(h, 0) for h in sessions]
-    return n_splits > 1 and any(-(-n // per) < n_splits for n in lens)
+def _streamed(sessions, hq, qdt="bf16"):
+    """Whether kv_attend_decode takes the streamed launch here (with the workspace it
+    allocates itself)."""
+    return kvq.kv_decode_launch_kind(sessions, 0, hq, kvq.KV_BF16 if qdt == "bf16" else kvq.KV_F32) == 1
 
 
 def _build(layout, lens, hkv, d, hq, seed, bf16):
@@ -81,7 +80,7 @@ def test_streamed_decode_matches_oracle(layout, d, hkv, g, qdt, lens):
     log(f"streamed {layout} D {d} Hkv {hkv} G {g} q {qdt} lens {lens}")
     sessions, ocs = _build(layout, lens, hkv, d, hq, 1200 + sum(lens) % 97, qdt == "bf16")
     try:
-        assert _uneven(sessions, hq)
+        assert _streamed(sessions, hq, qdt)
         q = I.normal((len(lens), hq, d), 1300 + d + g, 9)
         if qdt == "bf16":
             q = I.bf16_round(q)
@@ -111,7 +110,7 @@ def test_streamed_decode_64_sessions_log_uniform():
     log(f"streamed 64 sessions, {sum(lens)} tokens")
     sessions, ocs = _build("K8V4", lens, hkv, d, hq, 1400, True)
     try:
-        assert _uneven(sessions, hq)
+        assert _streamed(sessions, hq)
         q = I.bf16_round(I.normal((64, hq, d), 1401, 9))
         qd = dev(q, "bf16")
         scale = d ** -0.5
@@ -162,7 +161,7 @@ def test_streamed_decode_tracks_growing_sessions():
                 t = n + step
                 kvq.kv_append_quant(sessions[i], 0, dev(ks[i][t:t + 1], "bf16"), dev(vs[i][t:t + 1], "bf16"))
                 ocs[i].append(0, ks[i][t:t + 1], vs[i][t:t + 1])
-            assert _uneven(sessions, hq)
+            assert _streamed(sessions, hq)
             q = I.bf16_round(I.normal((len(lens0), hq, d), 1600 + step, 9))
             want = O.attend_decode(ocs, 0, q, scale)
             err = max_err(kvq.kv_attend_decode(sessions, 0, dev(q, "bf16"), scale), want)
@@ -193,8 +192,8 @@ def test_streamed_decode_random_batches():
         hq = hkv * g
         sessions, ocs = _build(layout, lens, hkv, d, hq, 1700 + 37 * case, True)
         try:
-            if not _uneven(sessions, hq):
-                log(f"  case {case}: even plan, skipped")
+            if not _streamed(sessions, hq):
+                log(f"  case {case}: split plan, skipped")
                 continue
             q = I.bf16_round(I.normal((n, hq, d), 1800 + case, 9))
             want = O.attend_decode(ocs, 0, q, d ** -0.5)

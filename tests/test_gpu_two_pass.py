@@ -100,8 +100,7 @@ def test_decode_partials_and_merge(case):
         assert n_splits >= 1 and per % 512 == 0 and n_splits * per >= max(lens)
         full = kvq.kv_attend_decode(sessions, 0, qd, scale)
         assert max_err(full, want) <= TOL
-        uneven = len(lens) > 1 and any(-(-n // per) < n_splits for n in lens)
-        if n_splits > 1 and not uneven:
+        if n_splits > 1 and kvq.kv_decode_launch_kind(sessions, 0, hq) == 0:
             two = kvq.kv_merge_partials(kvq.kv_attend_decode_partial(sessions, 0, qd, scale, n_splits, per))
             assert torch.equal(full, two)
     finally:
