@@ -60,7 +60,7 @@ def kernel_source_sha() -> str:
     comment edit does not count as a kernel change."""
     h = hashlib.sha256()
     for f in ("decode.hip", "chunk.hip", "append.hip", "merge.hip", "kvq_internal.h", "wave_ops.h",
-              "buffer_ops.h"):
+              "buffer_ops.h", "merge_row.h"):
         text = (ROOT / "asymmetric_quantized_kv_amd" / "csrc" / f).read_text()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
         text = re.sub(r"//[^\n]*", " ", text)
