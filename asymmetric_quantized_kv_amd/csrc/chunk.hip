@@ -49,6 +49,7 @@ typedef _Float16 half32_t __attribute__((ext_vector_type(32)));
 typedef unsigned int uint6v_t __attribute__((ext_vector_type(6)));
 
 constexpr float kLazyMax = 8.f;   // log2 headroom before the running max is moved
+constexpr float kLazyWeight = 256.f;   // 2^kLazyMax: the largest weight the headroom allows
 
 __device__ __forceinline__ half2_t h2(uint32_t x) { return __builtin_bit_cast(half2_t, x); }
 __device__ __forceinline__ uint32_t u32(half2_t x) { return __builtin_bit_cast(uint32_t, x); }
@@ -533,7 +534,7 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(ChunkArgs a) {
 
   // one 32-key half of a tile: S^T = K Q^T, online softmax, O^T += V^T P^T
   auto half = [&](auto masked, const _Float16* bk, const uint8_t* bkl8, const uint8_t* bks, const _Float16* bv,
-                  int64_t kt0, int st) {
+                  int64_t kt0, int st) __attribute__((always_inline)) {
     float16_t sv;
 #pragma unroll
     for (int v = 0; v < 16; ++v) sv[v] = 0.f;
@@ -589,33 +590,45 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(ChunkArgs a) {
       for (int v = 0; v < 16; ++v)
         if (8 * (v >> 2) + 4 * hl + (v & 3) >= lim) sv[v] = -INFINITY;
     }
-    // online softmax, one query row per lane pair (col, col + 32)
-    float mx = sv[0];
-#pragma unroll
-    for (int v = 1; v < 16; ++v) mx = fmaxf(mx, sv[v]);
-    mx = swap32_max(mx) * qks;
-    const bool move = mx > m + kLazyMax;
-    if (__any(move)) {
-      const float mn = move ? mx : m;
-      const float alpha = __builtin_amdgcn_exp2f(m - (mn == -INFINITY ? 0.f : mn));
-      l *= alpha;
-#pragma unroll
-      for (int t = 0; t < NDT; ++t)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) o[t][v] *= alpha;
-      m = mn;
-    }
-    const float mu = m == -INFINITY ? 0.f : m;
+    // online softmax, one query row per lane pair (col, col + 32).  The weights are formed
+    // against the running max first: each is at most their sum, so a lane whose 16 weights
+    // sum to at most 2^kLazyMax has no score past the max's headroom and needs no tile max.
+    // Only when some lane's sum is larger (or its row has no max yet) is the tile max taken;
+    // if it moves the running max, the accumulators are rescaled and the weights formed again.
     half8_t pb[2];
+    auto weights = [&](float mu) __attribute__((always_inline)) {
+      float s = 0.f;
 #pragma unroll
-    for (int v = 0; v < 16; v += 2) {
-      half2_t pp;
-      pp.x = (_Float16)__builtin_amdgcn_exp2f(fmaf(sv[v], qks, -mu));
-      pp.y = (_Float16)__builtin_amdgcn_exp2f(fmaf(sv[v + 1], qks, -mu));
-      l = __builtin_amdgcn_fdot2(pp, hconst(1.f), l, false);   // sum of the rounded weights
-      pb[v >> 3][v & 7] = pp.x;
-      pb[v >> 3][(v & 7) + 1] = pp.y;
+      for (int v = 0; v < 16; v += 2) {
+        half2_t pp;
+        pp.x = (_Float16)__builtin_amdgcn_exp2f(fmaf(sv[v], qks, -mu));
+        pp.y = (_Float16)__builtin_amdgcn_exp2f(fmaf(sv[v + 1], qks, -mu));
+        s = __builtin_amdgcn_fdot2(pp, hconst(1.f), s, false);   // sum of the rounded weights
+        pb[v >> 3][v & 7] = pp.x;
+        pb[v >> 3][(v & 7) + 1] = pp.y;
+      }
+      return s;
+    };
+    float ls = weights(m == -INFINITY ? 0.f : m);
+    if (__any(!(ls <= kLazyWeight) || m == -INFINITY)) {
+      float mx = sv[0];
+#pragma unroll
+      for (int v = 1; v < 16; ++v) mx = fmaxf(mx, sv[v]);
+      mx = swap32_max(mx) * qks;
+      const bool move = mx > m + kLazyMax;
+      if (__any(move)) {
+        const float mn = move ? mx : m;
+        const float alpha = __builtin_amdgcn_exp2f(m - (mn == -INFINITY ? 0.f : mn));
+        l *= alpha;
+#pragma unroll
+        for (int t = 0; t < NDT; ++t)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) o[t][v] *= alpha;
+        m = mn;
+        ls = weights(m == -INFINITY ? 0.f : m);
+      }
     }
+    l += ls;
 #pragma unroll
     for (int t = 0; t < NDT; ++t) {
 #pragma unroll
@@ -630,7 +643,7 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(ChunkArgs a) {
       }
     }
   };
-  auto consume = [&](auto masked, int t) {
+  auto consume = [&](auto masked, int t) __attribute__((always_inline)) {
     if (wave_active) {
       const int buf = t & 1;
       const _Float16* bk = s_k + buf * KBUF;
