@@ -744,7 +744,10 @@ std::vector<int> longest_first(const std::vector<int64_t>& lens) {
 // streams alone at the end.  A session overlapped by several ranges leaves one partial per
 // range, merged in the launch.  Each part of a session a workgroup takes costs it the
 // session's query preparation and an epilogue besides its blocks, so the cut balances blocks
-// plus kDecodeWgFixedTokens per part: a range over many short sessions holds fewer blocks.
+// plus kStreamPartTokens per part: a range over many short sessions holds fewer blocks.
+// (768 tokens per part measured best for 64 sessions of 512..32,768 tokens, K8V4, Hkv 8,
+// D 128: 178-180 us a call against 181 at 256 and 186-187 at 1,024, same box.)
+constexpr int64_t kStreamPartTokens = 768;
 struct StreamPlan {
   int n_wg = 0;
   int max_seg = 0;                             // partials per row the workspace must hold
@@ -764,7 +767,7 @@ StreamPlan stream_plan(const DecodePrep& p, const std::vector<int>& order, int n
     total += nb[i];
   }
   sp.n_wg = (int)std::max<int64_t>(1, std::min<int64_t>(n_wg, total));
-  const double part = (double)kDecodeWgFixedTokens / kDecodeWaveTokens;   // a part's fixed cost, in blocks
+  const double part = (double)kStreamPartTokens / kDecodeWaveTokens;   // a part's fixed cost, in blocks
   const double target = ((double)total + part * (double)(n + sp.n_wg - 1)) / sp.n_wg;
   sp.wg_block0.assign(sp.n_wg + 1, (int32_t)total);
   sp.wg_block0[0] = 0;

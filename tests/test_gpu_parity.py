@@ -462,6 +462,32 @@ def test_chunk_keys_spanning_five_decades(layout, d, dtype):
         assert err <= TOL
 
 
+@pytest.mark.parametrize("layout,d,dtype", [("K8V4", 128, "bf16"), ("K4V8", 64, "f32"), ("KF8V4", 128, "f16")])
+def test_chunk_running_max_moves_along_the_keys(layout, d, dtype):
+    """Key rows scaled by 1 + 3 t / 64 at position t: the scores grow along the keys, so each
+    32-key half of a row brings a larger maximum than the last. Depending on the row the half's
+    weights then fit the running max's headroom (no tile max), exceed the headroom test without
+    moving the max, or move it (rescale, weights formed again): every branch of the chunk
+    kernel's online softmax runs, on rows that are checked against the oracle."""
+    log(f"chunk growing keys {layout} D{d} {dtype}")
+    hkv, g, n_ctx, n_new = 2, 4, 1400, 100
+    hq, n = hkv * g, n_ctx + n_new
+    k, v, q = I.workload_small(970 + d, n, hkv, d, hq, n_new, n_outliers=0)
+    k = k * (1.0 + 3.0 * np.arange(n, dtype=np.float32) / 64.0)[:, None, None]
+    if dtype == "bf16":
+        k, v, q = I.bf16_round(k), I.bf16_round(v), I.bf16_round(q)
+    oc = O.OracleCache(O.LAYOUT_IDS[layout], 1, hkv, d, n)
+    with gpu_cache(layout, 1, hkv, d, n) as h:
+        kvq.kv_append_quant(h, 0, dev(k, dtype), dev(v, dtype))
+        oc.append(0, host_inputs(k, dtype), host_inputs(v, dtype))
+        scale = d ** -0.5
+        out = kvq.kv_attend_chunk(h, 0, dev(q, dtype), n_new, scale)
+        want = O.attend_chunk(oc, 0, host_inputs(q, dtype), n_new, scale)
+        err = max_err(out, want)
+        log(f"  max err {err:.3e}")
+        assert err <= TOL
+
+
 def _causal_rms_with_fp16_keys(oc, q, n_new, scale, want):
     """RMS distance from `want` of causal attention over the same cache with every key
     rounded to fp16 (what the chunk path would return without the keys' low part)."""
