@@ -101,6 +101,11 @@ __device__ __forceinline__ uint32_t fp8x4(half2_t a, half2_t b, float scale) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
+// Slot of key group g (keys 4 g .. 4 g + 3) in a transposed-value row: within each 16 keys the
+// groups go in the order 0, 2, 1, 3, so that the keys a lane half takes for one P.V product
+// (4 hl + 0..3 and 8 + 4 hl + 0..3 of the 16, the order of the S^T accumulator) are adjacent.
+__device__ __forceinline__ int vt_slot(int g) { return (g & ~3) | ((g & 1) << 1) | ((g >> 1) & 1); }
+
 // fp16 magic numbers: 0x64xx reads as 1024 + xx when xx < 4 bits of exponent room, so
 // a code placed in the low mantissa bits comes back exactly after one packed subtract.
 constexpr uint32_t kMagic = 0x64646464u;
@@ -148,7 +153,9 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(ChunkArgs a) {
   constexpr bool KSPLIT = KLO != 0;
   constexpr int NK = kChunkKeys;   // keys per tile
   constexpr int KSTR = D + 8;      // halves per LDS key row
-  constexpr int VSTR = NK + 4;     // halves per LDS transposed-value row (34 dwords: no bank conflicts)
+  // halves per LDS transposed-value row: 36 dwords, so that the 16-byte reads of 8 lanes down a
+  // column fall in distinct banks
+  constexpr int VSTR = NK + 8;
   constexpr int NDT = D / 32;      // 32-wide output blocks along d
   constexpr int NKS = D / 16;      // k-steps of Q.K^T
   constexpr int KE = D / 4;        // key elements one producer thread dequantizes (4 per key)
@@ -362,7 +369,7 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(ChunkArgs a) {
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          *reinterpret_cast<uint2*>(&bv[(8 * v_dg + e) * VSTR + 4 * v_kg]) = make_uint2(pr[e][0], pr[e][1]);
+          *reinterpret_cast<uint2*>(&bv[(8 * v_dg + e) * VSTR + 4 * vt_slot(v_kg)]) = make_uint2(pr[e][0], pr[e][1]);
       }
     };
     if (n_tiles > 0) {
@@ -633,12 +640,8 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(ChunkArgs a) {
     for (int t = 0; t < NDT; ++t) {
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const _Float16* vp = &bv[(32 * t + col) * VSTR + 32 * st + 16 * kk + 4 * hl];
-        const half4_t lo4 = *reinterpret_cast<const half4_t*>(vp);
-        const half4_t hi4 = *reinterpret_cast<const half4_t*>(vp + 8);
-        half8_t av;
-        av[0] = lo4[0]; av[1] = lo4[1]; av[2] = lo4[2]; av[3] = lo4[3];
-        av[4] = hi4[0]; av[5] = hi4[1]; av[6] = hi4[2]; av[7] = hi4[3];
+        // keys 32 st + 16 kk + 4 hl + (0..3, 8..11), stored side by side (vt_slot): one 16-byte read
+        const half8_t av = *reinterpret_cast<const half8_t*>(&bv[(32 * t + col) * VSTR + 32 * st + 16 * kk + 8 * hl]);
         o[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, pb[kk], o[t], 0, 0, 0);
       }
     }

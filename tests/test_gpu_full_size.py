@@ -91,7 +91,7 @@ def test_turn_100k_plus_500_and_reuse_invariant(layout):
 @pytest.mark.timeout(1200)
 def test_batch_64x32k_decode_sampled_sessions():
     """64 sessions x 32,768 tokens, Hq 32 / Hkv 8 / D 128, K8V4, K4V8 and the fp8-key layout
-    on identical inputs.  Oracle on sessions {0, 21, 63} (planes and outputs); every
+    on identical inputs.  Oracle on sessions {0, 21, 63} (planes bit for bit, and outputs); every
     session's output is finite and inside the hull of that session's values; the attention
     error against unquantized fp64 attention is reported and K4V8's exceeds K8V4's."""
     torch = torch_mod()
@@ -121,8 +121,7 @@ def test_batch_64x32k_decode_sampled_sessions():
                 k, v = kept[s]
                 oc = O.OracleCache(O.LAYOUT_IDS[L], 1, 8, 128, 32768)
                 oc.append(0, k, v)
-                if s == sample[0]:
-                    assert_planes_equal(hs[L][s], oc, 0)
+                assert_planes_equal(hs[L][s], oc, 0)
                 want = O.attend_decode([oc], 0, q[s:s + 1], SM128)[0]
                 ex = max(ex, float(np.max(np.abs(out[s] - want))))
                 exact = np.concatenate([O.attention_exact(q[s, 4 * h:4 * h + 4], k[:, h], v[:, h], SM128)
