@@ -93,6 +93,16 @@ __device__ __forceinline__ float wave_prescale(float lane_amax, float qk_scale, 
   return __uint_as_float((uint32_t)(254 - sb) << 23);
 }
 
+// The block-scaled product of the key low parts (format F: 0 = fp8 E4M3, 2 = fp6 E2M3, both
+// operands) with the key scale taken from byte mm of ka (the instruction's byte select, which
+// must be a constant) and the query scale from qa.
+template <int F>
+__device__ __forceinline__ float16_t scaled_mfma(int mm, const int8v_t& a, const int8v_t& b, const float16_t& c,
+                                                 uint32_t ka, uint32_t qa) {
+  return mm == 0 ? __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, F, F, 0, (int)ka, 0, (int)qa)
+                 : __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, F, F, 1, (int)ka, 0, (int)qa);
+}
+
 // four fp16 values / 2^t as four E4M3 bytes (the conversion divides by its scale operand)
 __device__ __forceinline__ uint32_t fp8x4(half2_t a, half2_t b, float scale) {
   short2_t r = {0, 0};
@@ -533,6 +543,7 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(ChunkArgs a) {
   }
 
   float m = -INFINITY, l = 0.f;
+  float mu = 0.f;   // the running max as the weights' offset (0 while the row has none)
   float16_t o[NDT];
 #pragma unroll
   for (int t = 0; t < NDT; ++t)
@@ -567,8 +578,7 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(ChunkArgs a) {
         const uint4 b1 = *reinterpret_cast<const uint4*>(ql8 + 64 * mm + 32);
         const int8v_t av8 = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
         const int8v_t bv8 = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
-        sv = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av8, bv8, sv, 0, 0, 0, (int)((asc >> (8 * mm)) & 255u), 0,
-                                                              (int)qs8[mm]);
+        sv = scaled_mfma<0>(mm, av8, bv8, sv, asc, qs8[mm]);
       }
     } else if constexpr (KLO == 3) {
       // m-th product at the fp6 rate: lane half hl brings all 32 elements of block 2 m + hl (24
@@ -585,8 +595,7 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(ChunkArgs a) {
         const uint2 b1 = *reinterpret_cast<const uint2*>(ql6 + 64 * mm + 16);
         const int8v_t av6 = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, 0, 0};
         const int8v_t bv6 = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, 0, 0};
-        sv = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av6, bv6, sv, 2, 2, 0, (int)((asc >> (8 * mm)) & 255u), 0,
-                                                              (int)qs8[mm]);
+        sv = scaled_mfma<2>(mm, av6, bv6, sv, asc, qs8[mm]);
       }
     }
     if constexpr (decltype(masked)::value) {
@@ -616,7 +625,7 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(ChunkArgs a) {
       }
       return s;
     };
-    float ls = weights(m == -INFINITY ? 0.f : m);
+    float ls = weights(mu);
     if (__any(!(ls <= kLazyWeight) || m == -INFINITY)) {
       float mx = sv[0];
 #pragma unroll
@@ -632,7 +641,8 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(ChunkArgs a) {
 #pragma unroll
           for (int v = 0; v < 16; ++v) o[t][v] *= alpha;
         m = mn;
-        ls = weights(m == -INFINITY ? 0.f : m);
+        mu = m == -INFINITY ? 0.f : m;
+        ls = weights(mu);
       }
     }
     l += ls;
