@@ -25,11 +25,13 @@
 // (packed fp16 arithmetic on magic-number conversions of the codes), while the raw
 // codes of the next tile are already in flight; each wave computes S^T = K Q^T (lane =
 // query row, 16 keys per 32-key block), keeps an online softmax per row, and accumulates
-// O^T += V^T P^T.  P is used in the key order the S^T accumulator already has and V^T is
-// read in that same order, so no register shuffle sits between the two contractions.
+// O^T += V^T P^T.  P is used in the key order the S^T accumulator already has, and V^T is
+// stored in that same order (vt_slot), so no register shuffle sits between the two
+// contractions and each V^T operand is one 16-byte LDS read.
 // The running max only moves when a row's tile max exceeds it by more than 2^8
 // (probabilities up to 256 stay exact in fp16), which makes the rescale of the
-// accumulators rare.
+// accumulators rare; the tile max itself is only taken when the weights formed against the
+// running max could exceed that headroom.
 #include "kvq_internal.h"
 #include "buffer_ops.h"
 #include "wave_ops.h"
