@@ -676,6 +676,12 @@ int decode_prepare(kv_cache* const* sessions, int n_sessions, int layer, int n_q
 // splits past its end exit at once.  With lengths that differ a lot, many splits let the
 // long sessions spread over the device while short ones take one workgroup each.
 constexpr int64_t kDecodeWgFixedTokens = 256;   // per-workgroup overhead, in streamed tokens
+// The latency of merging the splits inside the launch (each partial written through to memory,
+// the split counter, the last workgroup's coherent reads), in streamed tokens.  Measured on a
+// 22-layer step (4 KV heads x 64, one session): a layer of 512 tokens takes 6.3 us in one split;
+// 1,024 tokens take 7.75 us in one split against 8.6 in two; from 1,536 tokens on the split
+// plan wins (9.1 us at 1,536 in three splits against 10.0 in one).
+constexpr int64_t kDecodeMergeTokens = 768;
 constexpr int kMinSplitGroup = 2;               // query heads a workgroup keeps when a head's group is split
 
 int64_t decode_split_cap(const DecodePrep& p) {
@@ -698,11 +704,13 @@ void decode_plan(const DecodePrep& p, int* n_splits, int64_t* tps) {
     for (int64_t len : p.lens) busy += std::max<int64_t>(1, ceil_div(len, t));
     // rounds of the busy workgroups times (the tokens each one streams + a fixed cost of
     // kDecodeWgFixedTokens for its query preparation and epilogue), a small charge for the
-    // empty workgroups, and the merge's read of n partials per row
+    // empty workgroups, and for a split plan the merge: its latency and its read of n partials
+    // per row
     const int64_t rows = (int64_t)p.lens.size() * p.hkv * p.group;
     const double cost = (double)ceil_div(busy * p.hkv, slots) * (double)(t + kDecodeWgFixedTokens) +
                         0.02 * (double)gran * (double)((n * (int64_t)p.lens.size() - busy) * p.hkv) / (double)slots +
-                        (n > 1 ? (double)rows * n * (p.d + 2) * 4.0 / (double)(208 * slots) : 0.0);
+                        (n > 1 ? (double)kDecodeMergeTokens + (double)rows * n * (p.d + 2) * 4.0 / (double)(208 * slots)
+                               : 0.0);
     if (s == 1 || cost < best * 0.98) {
       best = cost;
       *n_splits = (int)n;
