@@ -488,6 +488,32 @@ def test_chunk_running_max_moves_along_the_keys(layout, d, dtype):
         assert err <= TOL
 
 
+@pytest.mark.parametrize("layout,d,dtype", [("K8V4", 128, "bf16"), ("K8V8", 64, "f32")])
+def test_chunk_score_jump_past_fp32_range(layout, d, dtype):
+    """One key row 2^9 times larger than the rest, past the first tiles: for the rows it
+    attends to, its score exceeds the running max by hundreds of log2 units, so the weights
+    formed against the old max overflow to infinity before the tile max is taken and the max
+    moves.  (Several such keys competing at scores in the hundreds would test the precision of
+    the keys' low part instead: its error grows with the key's magnitude.)"""
+    log(f"chunk score jump {layout} D{d} {dtype}")
+    hkv, g, n_ctx, n_new = 2, 4, 900, 60
+    hq, n = hkv * g, n_ctx + n_new
+    k, v, q = I.workload_small(980 + d, n, hkv, d, hq, n_new, n_outliers=0)
+    k[700] *= np.float32(512.0)
+    if dtype == "bf16":
+        k, v, q = I.bf16_round(k), I.bf16_round(v), I.bf16_round(q)
+    oc = O.OracleCache(O.LAYOUT_IDS[layout], 1, hkv, d, n)
+    with gpu_cache(layout, 1, hkv, d, n) as h:
+        kvq.kv_append_quant(h, 0, dev(k, dtype), dev(v, dtype))
+        oc.append(0, host_inputs(k, dtype), host_inputs(v, dtype))
+        scale = d ** -0.5
+        out = kvq.kv_attend_chunk(h, 0, dev(q, dtype), n_new, scale)
+        want = O.attend_chunk(oc, 0, host_inputs(q, dtype), n_new, scale)
+        err = max_err(out, want)
+        log(f"  max err {err:.3e}")
+        assert np.all(np.isfinite(out.cpu().numpy())) and err <= TOL
+
+
 def _causal_rms_with_fp16_keys(oc, q, n_new, scale, want):
     """RMS distance from `want` of causal attention over the same cache with every key
     rounded to fp16 (what the chunk path would return without the keys' low part)."""
