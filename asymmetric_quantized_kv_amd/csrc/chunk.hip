@@ -18,7 +18,9 @@
 // rounding stays 2^-17 (fp6) or 2^-20 (fp8) below the block's largest key, against fp16's
 // 2^-12 of every key.  fp32 queries are carried as fp16 hi + lo.
 // fp8 (E4M3) keys with power-of-two block scales widen to fp16 exactly in one conversion
-// (v_cvt_scalef32_pk_f16_fp8), so they need no low part: one MFMA per k-step.
+// (v_cvt_scalef32_pk_f16_fp8), so they need no low part: one MFMA per k-step.  With bf16
+// queries they are not widened at all: Q.K^T runs in OCP MX fp8 on the block-scaled MFMA,
+// the cache's codes and block exponents against an exact two-part E4M3 split of the query.
 //
 // A workgroup owns 256 rows of one KV head and one split of the context.
 // Per 64-key tile: the workgroup dequantizes K into LDS as [key][d] and V as [d][key]
@@ -159,8 +161,14 @@ constexpr int key_lo_format() {
   return KB == 16 || KB == kF8 ? 0 : (D == 128 && !QSPLIT ? 3 : 2);
 }
 
-template <int KB, int VB, int D, bool QSPLIT>
+// MX (fp8 keys with bf16 queries): Q.K^T on the block-scaled MFMA in OCP MX fp8.  The keys are
+// the cache's own E4M3 codes and block exponents, copied to LDS as they are; each bf16 query
+// is split into two E4M3 parts with power-of-two scales per 32-element block, hi (its top four
+// significant bits) and lo (the rest, exact for bf16), so the products are those of the exact
+// query.  Two MX products per 64 key elements take the issue time of the four fp16 ones.
+template <int KB, int VB, int D, bool QSPLIT, bool MX = false>
 __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(ChunkArgs a) {
+  static_assert(!MX || (KB == kF8 && !QSPLIT), "MX products: fp8 keys, 16-bit queries");
   constexpr int KLO = key_lo_format<KB, D, QSPLIT>();
   constexpr bool KSPLIT = KLO != 0;
   constexpr int NK = kChunkKeys;   // keys per tile
@@ -180,11 +188,12 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(ChunkArgs a) {
   // scale, ordered [h][m] for block 2 m + h (the scaled MFMA takes the scale of block 2 m + h
   // of its m-th product from lane half h)
   constexpr int NB = D / kBlock, NBH = NB / 2, LSTR = D + 16;
+  constexpr int K8STR = D + 16;    // MX: bytes per LDS key row of E4M3 codes
   static_assert(kChunkThreads == 768 && kChunkRows == 256, "8 consumer + 4 producer waves");
   // two tile buffers: the producers fill one while the consumers read the other
-  __shared__ __attribute__((aligned(16))) _Float16 s_k[2 * KBUF];
+  __shared__ __attribute__((aligned(16))) _Float16 s_k[MX ? NK * K8STR : 2 * KBUF];   // MX: codes, bytes
   __shared__ __attribute__((aligned(16))) uint8_t s_kl8[KLO >= 2 ? 2 * NK * LSTR : 16];
-  __shared__ __attribute__((aligned(4))) uint8_t s_kls[KLO >= 2 ? 2 * NK * NB : 4];
+  __shared__ __attribute__((aligned(4))) uint8_t s_kls[KLO >= 2 || MX ? 2 * NK * NB : 4];
   __shared__ __attribute__((aligned(16))) uint8_t s_q8[KLO >= 2 ? kChunkRows * LSTR : 16];  // fp8 / fp6 queries
   __shared__ __attribute__((aligned(16))) _Float16 s_vt[2 * VBUF];
 
@@ -258,7 +267,17 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(ChunkArgs a) {
     auto produce = [&](int buf) {
       _Float16* bk = s_k + buf * KBUF;
       _Float16* bv = s_vt + buf * VBUF;
-      {
+      if constexpr (MX) {
+        // the codes as they are (KE bytes at byte KE k_part of the key's row) and the block
+        // exponent, ordered [h][m] for block 2 m + h like the low parts' scales
+        uint8_t* b8 = reinterpret_cast<uint8_t*>(s_k) + buf * NK * K8STR + k_key * K8STR + k_part * KE;
+#pragma unroll
+        for (int i = 0; i < KW / 4; ++i)
+          *reinterpret_cast<uint4*>(b8 + 16 * i) = make_uint4(kraw[4 * i], kraw[4 * i + 1], kraw[4 * i + 2], kraw[4 * i + 3]);
+        if constexpr (KW % 4 != 0) static_assert(KW % 4 == 0, "16-byte code runs");
+        const int b = (k_part * KE) / kBlock;
+        if ((k_part * KE) % kBlock == 0) s_kls[buf * NK * NB + k_key * NB + (b & 1) * NBH + (b >> 1)] = (uint8_t)kscale;
+      } else {
         half2_t hi[KE / 2], lo[KE / 2];
         if constexpr (KB == 16) {
 #pragma unroll
@@ -414,10 +433,70 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(ChunkArgs a) {
   // rows are first scaled by a power of two 2^-k that puts their largest |q| in [2^14, 2^15),
   // so fp16 holds them for any magnitude (16-bit queries exactly); 2^k goes into the score
   // scale, one for the wave.
-  half8_t qv[NKS];
+  half8_t qv[MX ? 1 : NKS];
   half8_t ql[QSPLIT ? NKS : 1];
+  // MX: the B operands of the m-th product, E4M3 hi and lo parts of elements 64 m + 16 hl + 0..15
+  // (bytes 0..15) and 64 m + 32 + 16 hl + 0..15 (bytes 16..31), and the exponents of block 2 m + hl
+  int8v_t qhi[MX ? NBH : 1], qlo[MX ? NBH : 1];
+  uint32_t qeh[MX ? NBH : 1], qel[MX ? NBH : 1];
   float qks;   // raw score -> base-2 logit (wave-uniform)
-  {
+  if constexpr (MX) {
+    // block b's 16 elements 32 b + 16 hl + 0..15 of this lane's row (its partner holds the other
+    // 16): two 16-byte loads per block, all issued before the first conversion
+    const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + (tok * a.hq + qh) * (int64_t)D +
+                                                      16 * hl);
+    uint4 raw[2 * NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      raw[2 * b] = valid ? src[4 * b] : make_uint4(0u, 0u, 0u, 0u);
+      raw[2 * b + 1] = valid ? src[4 * b + 1] : make_uint4(0u, 0u, 0u, 0u);
+    }
+    qks = a.qk_scale;   // the products are those of the queries themselves
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      float x[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const uint4 r = raw[2 * b + i / 8];
+        const uint32_t w = (i & 7) < 2 ? r.x : (i & 7) < 4 ? r.y : (i & 7) < 6 ? r.z : r.w;
+        x[i] = __uint_as_float((w >> (16 * (i & 1))) << 16);
+      }
+      float am = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) am = fmaxf(am, fabsf(x[i]));
+      am = swap32_max(am);
+      // hi: x / 2^t in E4M3 with t = floor(log2 amax) - 7 (|x| / 2^t < 256, E4M3 holds up to 448);
+      // lo = x - hi, a multiple of x's bf16 unit below half hi's, at 2^(t - 4): |lo| / 2^(t - 4)
+      // <= 128 and four significant bits hold it (exact but where x is under 2^-13 of the amax)
+      const int t = max((int)((__float_as_uint(am) >> 23) & 255) - 134, -126);
+      const int tl = max(t - 4, -127);
+      const float sh = __uint_as_float((uint32_t)(t + 127) << 23), sl = __uint_as_float((uint32_t)(tl + 127) << 23);
+      uint32_t h4[4], l4[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        short2_t ph = {0, 0}, pl = {0, 0};
+        ph = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(ph, x[4 * j], x[4 * j + 1], sh, false);
+        ph = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(ph, x[4 * j + 2], x[4 * j + 3], sh, true);
+        const uint32_t hw = __builtin_bit_cast(uint32_t, ph);
+        const auto v01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)hw, sh, false);
+        const auto v23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)hw, sh, true);
+        pl = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(pl, x[4 * j] - v01[0], x[4 * j + 1] - v01[1], sl, false);
+        pl = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(pl, x[4 * j + 2] - v23[0], x[4 * j + 3] - v23[1], sl, true);
+        h4[j] = hw;
+        l4[j] = __builtin_bit_cast(uint32_t, pl);
+      }
+      const int m = b >> 1, g = b & 1;   // bytes 16 g .. of the m-th product
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        qhi[m][4 * g + j] = (int)h4[j];
+        qlo[m][4 * g + j] = (int)l4[j];
+      }
+      if (g == hl) {
+        qeh[m] = (uint32_t)(t + 127);
+        qel[m] = (uint32_t)(tl + 127);
+      }
+    }
+  } else {
     // 8 consecutive elements per k-step: one 16-byte load each (two for fp32), all issued
     // before the first conversion
     const int64_t qoff = (tok * a.hq + qh) * (int64_t)D + 8 * hl;
@@ -558,12 +637,28 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(ChunkArgs a) {
     float16_t sv;
 #pragma unroll
     for (int v = 0; v < 16; ++v) sv[v] = 0.f;
+    if constexpr (MX) {
+      // m-th pair of products: lane half hl brings bytes 16 hl .. + 15 of blocks 2 m and 2 m + 1
+      // of its key's codes and the exponent of block 2 m + hl, against the query's hi and lo parts
+      const uint8_t* kr = reinterpret_cast<const uint8_t*>(bk) + (32 * st + col) * K8STR + 16 * hl;
+      const uint8_t* ksp = bks + (32 * st + col) * NB + hl * NBH;
+      const uint32_t asc = NBH == 2 ? (uint32_t)*reinterpret_cast<const uint16_t*>(ksp) : (uint32_t)*ksp;
 #pragma unroll
-    for (int k = 0; k < NKS; ++k) {
-      const int off = (32 * st + col) * KSTR + 16 * k + 8 * hl;
-      const half8_t ak = *reinterpret_cast<const half8_t*>(&bk[off]);
-      sv = __builtin_amdgcn_mfma_f32_32x32x16_f16(ak, qv[k], sv, 0, 0, 0);
-      if constexpr (QSPLIT) sv = __builtin_amdgcn_mfma_f32_32x32x16_f16(ak, ql[k], sv, 0, 0, 0);
+      for (int mm = 0; mm < NBH; ++mm) {
+        const uint4 a0 = *reinterpret_cast<const uint4*>(kr + 64 * mm);
+        const uint4 a1 = *reinterpret_cast<const uint4*>(kr + 64 * mm + 32);
+        const int8v_t av8 = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+        sv = scaled_mfma<0>(mm, av8, qhi[mm], sv, asc, qeh[mm]);
+        sv = scaled_mfma<0>(mm, av8, qlo[mm], sv, asc, qel[mm]);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < NKS; ++k) {
+        const int off = (32 * st + col) * KSTR + 16 * k + 8 * hl;
+        const half8_t ak = *reinterpret_cast<const half8_t*>(&bk[off]);
+        sv = __builtin_amdgcn_mfma_f32_32x32x16_f16(ak, qv[k], sv, 0, 0, 0);
+        if constexpr (QSPLIT) sv = __builtin_amdgcn_mfma_f32_32x32x16_f16(ak, ql[k], sv, 0, 0, 0);
+      }
     }
     if constexpr (KLO == 2) {
       // m-th product: lane half hl brings bytes 16 hl .. + 15 of blocks 2 m and 2 m + 1, and the
@@ -661,9 +756,10 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(ChunkArgs a) {
   auto consume = [&](auto masked, int t) __attribute__((always_inline)) {
     if (wave_active) {
       const int buf = t & 1;
-      const _Float16* bk = s_k + buf * KBUF;
+      const _Float16* bk = MX ? reinterpret_cast<const _Float16*>(reinterpret_cast<const uint8_t*>(s_k) + buf * NK * K8STR)
+                              : s_k + buf * KBUF;
       const uint8_t* bkl8 = s_kl8 + (KLO >= 2 ? buf * NK * LSTR : 0);
-      const uint8_t* bks = s_kls + (KLO >= 2 ? buf * NK * NB : 0);
+      const uint8_t* bks = s_kls + (KLO >= 2 || MX ? buf * NK * NB : 0);
       const _Float16* bv = s_vt + buf * VBUF;
       const int64_t kt0 = k_lo + (int64_t)t * NK;
       half(masked, bk, bkl8, bks, bv, kt0, 0);
@@ -708,9 +804,9 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(ChunkArgs a) {
   }
 }
 
-template <int KB, int VB, int D, bool QSPLIT>
+template <int KB, int VB, int D, bool QSPLIT, bool MX = false>
 const void* kernel_ptr() {
-  return reinterpret_cast<const void*>(&chunk_kernel<KB, VB, D, QSPLIT>);
+  return reinterpret_cast<const void*>(&chunk_kernel<KB, VB, D, QSPLIT, MX>);
 }
 
 template <int KB, int VB, int D>
@@ -720,6 +816,8 @@ hipError_t launch_t(const ChunkArgs& a, hipStream_t s) {
   dim3 grid((unsigned)mt, a.hkv, a.n_splits);
   if (a.q_dtype == 0)
     hipLaunchKernelGGL((chunk_kernel<KB, VB, D, true>), grid, dim3(kChunkThreads), 0, s, a);
+  else if (KB == kF8 && a.q_dtype == 1)
+    hipLaunchKernelGGL((chunk_kernel<KB, VB, D, false, KB == kF8>), grid, dim3(kChunkThreads), 0, s, a);
   else
     hipLaunchKernelGGL((chunk_kernel<KB, VB, D, false>), grid, dim3(kChunkThreads), 0, s, a);
   return hipGetLastError();
@@ -750,6 +848,8 @@ hipError_t launch_chunk(const ChunkArgs& a, int kbits, int vbits, int d, hipStre
   return hipErrorInvalidValue;
 }
 
+// (The MX instantiation that fp8 keys take with bf16 queries holds, like this one, one
+// workgroup per compute unit.)
 const void* chunk_kernel_for(int kbits, int vbits, int d, bool q_fp32) {
   if (kbits == 16) return ptr_d<16, 16>(d, q_fp32);
   if (kbits == kF8) return ptr_d<kF8, 4>(d, q_fp32);

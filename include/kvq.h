@@ -26,8 +26,10 @@
  *     e = clamp(floor(log2(amax)) - 8, -127, 127) (-127 for an all-zero block), and per
  *     element the E4M3 code (bias 7, largest 448, no infinities) of x * 2^-e rounded to
  *     nearest, ties to even, saturated at +-448; a result of zero is stored as +0.
- *     x_hat = E4M3 value * 2^(s - 127).  The attention kernels widen these keys to fp16
- *     (exactly while |x| < 65536: the fp16 control layout's range);
+ *     x_hat = E4M3 value * 2^(s - 127).  Decode, and the chunk path with fp16 or fp32
+ *     queries, widen these keys to fp16 (exactly while |x| < 65536: the fp16 control
+ *     layout's range); the chunk path with bf16 queries multiplies them as they are, on
+ *     the MX-fp8 matrix instructions;
  *   - planes per (layer, KV head), token-major: KC [cap][code bytes], KS [cap][scale
  *     bytes] (2*D/32 for fp16 scales, D/32 for exponent bytes), VC, VS; cap = max_tokens
  *     rounded up to 256 tokens (the KVSplit page's remark on 256-byte alignment, section
@@ -53,7 +55,11 @@
  *     the rest that much resolution.  Decode with fp8 or fp16 keys and the chunk path
  *     scale the query by a power of two that puts its largest element (per head in
  *     decode, per 32 query rows in the chunk path) in [2^14, 2^15) and carry it in fp16:
- *     16-bit queries exactly, fp32 queries as an fp16 high and low part.
+ *     16-bit queries exactly, fp32 queries as an fp16 high and low part.  The chunk path
+ *     with fp8 keys and bf16 queries splits each query element into two E4M3 parts with a
+ *     power-of-two scale per 32-element block (exact but for elements below 2^-13 of their
+ *     block's largest); its block-scaled products were measured less accurate than the
+ *     fp16 ones (worst tested output errors 0.9-1.8e-3 against 0.6-1.0e-3).
  *   - the chunk path carries dequantized keys and values in fp16 (keys as an fp16 high
  *     part plus a scaled 6- or 8-bit low part): their magnitudes must stay below 65504,
  *     or the outputs are not finite.  Decode takes 8- and 4-bit keys exactly (integer dot
