@@ -627,9 +627,10 @@ def test_kf8v4_footprint():
 
 
 def test_fp8_queries_would_miss_the_attention_tolerance():
-    """Why the fp8-key layout's chunk path keeps fp16 MFMA: rounding the *queries* to MX
-    fp8 as well (what an fp8 x fp8 MFMA needs) moves attention outputs far past the 5e-3
-    tolerance on the turn's input recipe, while the fp8 keys alone are the cache's content."""
+    """Why the fp8-key chunk path does not round each query to one MX fp8 value for its
+    fp8 x fp8 products: that moves attention outputs far past the 5e-3 tolerance on the
+    turn's input recipe, while the fp8 keys alone are the cache's content.  The kernel
+    therefore splits each bf16 query into two E4M3 parts (next test)."""
     k, v, q = I.workload_small(5, 4000, 1, 128, 8, 64, bf16=True, n_outliers=4)
     oc = O.OracleCache(5, 1, 1, 128, 4000)
     oc.append(0, k, v)
@@ -639,3 +640,30 @@ def test_fp8_queries_would_miss_the_attention_tolerance():
     q8 = O.mx_dequant_rows(qc, qs).reshape(q.shape).astype(np.float32)
     err = float(np.abs(O.attend_chunk(oc, 0, q8, 64, sm) - want).max())
     assert err > 10 * 5e-3, err
+
+
+def test_bf16_two_part_e4m3_split():
+    """The fp8-key chunk path's query split (OCP MX, two E4M3 parts per element): with
+    t = floor(log2 amax) - 7 for the 32-element block, hi = E4M3(x / 2^t) and
+    lo = E4M3((x - hi 2^t) / 2^(t-4)) give hi 2^t + lo 2^(t-4) = x exactly for every bf16 x
+    of magnitude at least 2^(floor(log2 amax) - 13), and within 2^(t-14) below that.  Checked
+    over every bf16 value of the binades from 2^-20 to 2^1 (the block's amax in [1, 2)) and
+    for block maxima 2^-90 .. 2^90, with the E4M3 rounding of the oracle."""
+    vals = O.e4m3_values()
+    for big in (-90, -3, 0, 7, 90):
+        # every bf16 bit pattern of [2^(big-20), 2^(big+1)) and its negation
+        lo_bits = (127 + big - 20) << 7
+        hi_bits = (127 + big + 1) << 7
+        pat = np.arange(lo_bits, hi_bits, dtype=np.uint32) << 16
+        x = pat.view(np.float32).astype(np.float64)
+        x = np.concatenate([x, -x])
+        amax_exp = big   # every block holds an element of [2^big, 2^(big+1))
+        t = amax_exp - 7
+        hi = vals[O.e4m3_encode(x * 2.0 ** -t)] * 2.0 ** t
+        assert np.all(np.abs(x) * 2.0 ** -t < 448)
+        lo = vals[O.e4m3_encode((x - hi) * 2.0 ** -(t - 4))] * 2.0 ** (t - 4)
+        assert np.all(np.abs(x - hi) * 2.0 ** -(t - 4) <= 128)
+        err = np.abs(hi + lo - x)
+        big_enough = np.abs(x) >= 2.0 ** (amax_exp - 13)
+        assert np.all(err[big_enough] == 0)
+        assert np.all(err <= 2.0 ** (t - 14))
