@@ -467,9 +467,11 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(ChunkArgs a) {
       am = swap32_max(am);
       // hi: x / 2^t in E4M3 with t = floor(log2 amax) - 7 (|x| / 2^t < 256, E4M3 holds up to 448);
       // lo = x - hi, a multiple of x's bf16 unit below half hi's, at 2^(t - 4): |lo| / 2^(t - 4)
-      // <= 128 and four significant bits hold it (exact but where x is under 2^-13 of the amax)
+      // <= 128 and four significant bits hold it (exact but where x is under 2^-13 of the amax).
+      // Both exponents stay at or above -126, so each conversion scale is a normal float (a
+      // zero block, or one under 2^-115, would otherwise give the remainder a scale of 0)
       const int t = max((int)((__float_as_uint(am) >> 23) & 255) - 134, -126);
-      const int tl = max(t - 4, -127);
+      const int tl = max(t - 4, -126);
       const float sh = __uint_as_float((uint32_t)(t + 127) << 23), sl = __uint_as_float((uint32_t)(tl + 127) << 23);
       uint32_t h4[4], l4[4];
 #pragma unroll

@@ -415,6 +415,40 @@ def test_queries_beyond_fp16_range(layout, dtype):
         assert err_c <= TOL and err_d <= TOL
 
 
+@pytest.mark.parametrize("layout", ["KF8V4", "K8V4", "FP16"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_queries_with_zero_and_tiny_blocks(layout, dtype):
+    """Query 32-element blocks that are all zero or sit near the bottom of the format's range
+    (a zero query row too): every per-block query scale of the chunk path must stay a usable
+    power of two, and decode's per-head scale too."""
+    log(f"zero and tiny query blocks {layout} {dtype}")
+    d, hkv, g, n_ctx, n_new = 128, 2, 4, 300, 70
+    n = n_ctx + n_new
+    k, v, _ = I.workload_small(4600, n, hkv, d, hkv * g, 1, bf16=(dtype == "bf16"))
+    if dtype == "bf16":
+        k = I.bf16_round(k)
+    q = I.normal((n_new, hkv * g, d), 47, 9)
+    tiny = 2.0 ** -120 if dtype == "bf16" else 2.0 ** -14   # bf16: below 2^-115; fp16: its smallest normal
+    q[:, 0, 32:64] = 0.0                       # one zero block per row
+    q[:, 1, 64:96] *= np.float32(tiny)         # a block at the bottom of the range
+    q[:, 2, :] = 0.0                           # a zero query head
+    q[:, 3, 96:] *= np.float32(tiny)           # a tiny block beside ordinary ones
+    q[::7, 4, :] *= np.float32(tiny)           # every seventh row of a head tiny throughout
+    q = q.astype(np.float32)
+    if dtype == "bf16":
+        q = I.bf16_round(q)
+    oc = O.OracleCache(O.LAYOUT_IDS[layout], 1, hkv, d, n)
+    oc.append(0, host_inputs(k, dtype), host_inputs(v, dtype))
+    with gpu_cache(layout, 1, hkv, d, n) as h:
+        kvq.kv_append_quant(h, 0, dev(k, dtype), dev(v, dtype))
+        out_c = kvq.kv_attend_chunk(h, 0, dev(q, dtype), n_new, d ** -0.5)
+        out_d = kvq.kv_attend_decode([h], 0, dev(q[-1:], dtype), d ** -0.5)
+        err_c = max_err(out_c, O.attend_chunk(oc, 0, host_inputs(q, dtype), n_new, d ** -0.5))
+        err_d = max_err(out_d, O.attend_decode([oc], 0, host_inputs(q[-1:], dtype), d ** -0.5))
+        log(f"  chunk max err {err_c:.3e}, decode max err {err_d:.3e}")
+        assert err_c <= TOL and err_d <= TOL
+
+
 @pytest.mark.parametrize("layout", ["K8V4", "K4V8", "FP16", "KF8V4"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_chunk_query_outlier_channels(layout, dtype):
