@@ -311,6 +311,12 @@ CHUNK_CASES = [
     ("KF8V4", 128, 8, "bf16", 3000, 200),
     ("KF8V4", 64, 2, "f32", 0, 700),
     ("KF8V4", 128, 5, "f16", 1500, 64),
+    # bf16 queries on fp8 keys take the MX fp8 products, at both head_dims and every group size
+    ("KF8V4", 64, 8, "bf16", 1200, 150),
+    ("KF8V4", 64, 16, "bf16", 0, 333),
+    ("KF8V4", 64, 1, "bf16", 2500, 9),
+    ("KF8V4", 128, 16, "bf16", 257, 45),
+    ("KF8V4", 128, 1, "bf16", 90, 70),
 ]
 
 
@@ -417,12 +423,13 @@ def test_queries_beyond_fp16_range(layout, dtype):
 
 @pytest.mark.parametrize("layout", ["KF8V4", "K8V4", "FP16"])
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
-def test_queries_with_zero_and_tiny_blocks(layout, dtype):
+@pytest.mark.parametrize("d", [128, 64])
+def test_queries_with_zero_and_tiny_blocks(layout, dtype, d):
     """Query 32-element blocks that are all zero or sit near the bottom of the format's range
     (a zero query row too): every per-block query scale of the chunk path must stay a usable
     power of two, and decode's per-head scale too."""
-    log(f"zero and tiny query blocks {layout} {dtype}")
-    d, hkv, g, n_ctx, n_new = 128, 2, 4, 300, 70
+    log(f"zero and tiny query blocks {layout} D{d} {dtype}")
+    hkv, g, n_ctx, n_new = 2, 4, 300, 70
     n = n_ctx + n_new
     k, v, _ = I.workload_small(4600, n, hkv, d, hkv * g, 1, bf16=(dtype == "bf16"))
     if dtype == "bf16":
@@ -430,9 +437,9 @@ def test_queries_with_zero_and_tiny_blocks(layout, dtype):
     q = I.normal((n_new, hkv * g, d), 47, 9)
     tiny = 2.0 ** -120 if dtype == "bf16" else 2.0 ** -14   # bf16: below 2^-115; fp16: its smallest normal
     q[:, 0, 32:64] = 0.0                       # one zero block per row
-    q[:, 1, 64:96] *= np.float32(tiny)         # a block at the bottom of the range
+    q[:, 1, d // 2:d // 2 + 32] *= np.float32(tiny)   # a block at the bottom of the range
     q[:, 2, :] = 0.0                           # a zero query head
-    q[:, 3, 96:] *= np.float32(tiny)           # a tiny block beside ordinary ones
+    q[:, 3, d - 32:] *= np.float32(tiny)       # a tiny block beside ordinary ones
     q[::7, 4, :] *= np.float32(tiny)           # every seventh row of a head tiny throughout
     q = q.astype(np.float32)
     if dtype == "bf16":
@@ -496,7 +503,8 @@ def test_chunk_keys_spanning_five_decades(layout, d, dtype):
         assert err <= TOL
 
 
-@pytest.mark.parametrize("layout,d,dtype", [("K8V4", 128, "bf16"), ("K4V8", 64, "f32"), ("KF8V4", 128, "f16")])
+@pytest.mark.parametrize("layout,d,dtype", [("K8V4", 128, "bf16"), ("K4V8", 64, "f32"), ("KF8V4", 128, "f16"),
+                                            ("KF8V4", 64, "f16"), ("KF8V4", 128, "bf16"), ("KF8V4", 64, "bf16")])
 def test_chunk_running_max_moves_along_the_keys(layout, d, dtype):
     """Key rows scaled by 1 + 3 t / 64 at position t: the scores grow along the keys, so each
     32-key half of a row brings a larger maximum than the last. Depending on the row the half's
