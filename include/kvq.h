@@ -62,7 +62,8 @@
  *     fp16 ones: on the same inputs, 1.1 to 2.7 times the widened path's output error
  *     (worst tested 3.9e-3 against 1.5e-3, a softmax made peaked by keys growing 70-fold
  *     along the context; 0.7-1.8e-3 against 0.4-1.0e-3 on the other cases): the
- *     instruction keeps each product only down to 2^-14 of the largest one it sums.
+ *     instruction keeps each product only down to 2^-14 of the largest one in its
+ *     32-element block.
  *   - the chunk path carries dequantized keys and values in fp16 (keys as an fp16 high
  *     part plus a scaled 6- or 8-bit low part): their magnitudes must stay below 65504,
  *     or the outputs are not finite.  Decode takes 8- and 4-bit keys exactly (integer dot
